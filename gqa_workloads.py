@@ -1,0 +1,134 @@
+"""Seeded synthetic inputs and the workload table for the GQA core.
+
+This module only draws random numbers and casts them; it holds none of the
+attention arithmetic.  Both the oracle-side tests and the GPU-side tests and
+benchmark take their inputs from here, so the two sides see identical bytes.
+
+Recipe (one fixed rule for every workload):
+
+* a CPU ``torch.Generator`` seeded with the workload's seed;
+* draws in float32 with ``torch.randn`` in the order q, k, v (decode: the
+  per-sequence lengths first, with ``torch.randint`` over [lo, hi] inclusive,
+  then q, k_cache, v_cache);
+* a standard deviation other than 1 is applied in float32 before the cast;
+* the cast to bfloat16 is torch's round-to-nearest-even.
+
+Shapes follow the pages' workloads: the worked example of "Implementing GQA
+from scratch" (§5: B=32, L=1024, 8 heads, d_model=512, 4 key/value heads), the
+Llama-2-7B style 32/8 head split with d=128 ("What is Grouped-Query
+Attention", §2.3 and §3.4), the A100 prefill length 4096 and the Qwen2-72B
+64/8 head split ("Attention in Qwen, DeepSeek and LLaMA3", §2.2 and §2.3), at
+32K context.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    path: str  # "prefill" or "decode"
+    dtype: str  # "f32" or "bf16"
+    B: int
+    h_q: int
+    h_kv: int
+    d: int
+    L: int = 1  # prefill sequence length
+    S: int = 0  # decode cache capacity
+    causal: bool = False
+    std: float = 1.0
+    seqlen_range: tuple = (0, 0)  # decode: inclusive [lo, hi]
+    seed: int = 0
+    description: str = field(default="", compare=False)
+
+    @property
+    def G(self) -> int:
+        return self.h_q // self.h_kv
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+
+WORKLOADS = {
+    "tiny_prefill_f32": Workload(
+        "tiny_prefill_f32", "prefill", "f32", B=1, L=128, h_q=8, h_kv=2, d=64, causal=True,
+        std=1.0, seed=1,
+        description="tiny fp32 causal prefill, B=1 L=128 h_q=8 h_kv=2 d=64"),
+    "worked_example_prefill_bf16": Workload(
+        "worked_example_prefill_bf16", "prefill", "bf16", B=32, L=1024, h_q=8, h_kv=4, d=64,
+        causal=False, std=1.0, seed=2,
+        description="bf16 non-causal prefill, B=32 L=1024 h_q=8 h_kv=4 d=64"),
+    "llama2_7b_prefill_bf16": Workload(
+        "llama2_7b_prefill_bf16", "prefill", "bf16", B=1, L=4096, h_q=32, h_kv=8, d=128,
+        causal=True, std=1.0 / math.sqrt(2.0), seed=3,
+        description="bf16 causal prefill, B=1 L=4096 h_q=32 h_kv=8 d=128"),
+    "batched_decode_bf16": Workload(
+        "batched_decode_bf16", "decode", "bf16", B=64, h_q=32, h_kv=8, d=128, S=8192,
+        std=1.0, seqlen_range=(1024, 8192), seed=4,
+        description="bf16 decode, B=64 h_q=32 h_kv=8 d=128 S=8192 lengths U{1024..8192}"),
+    "long_context_prefill_bf16": Workload(
+        "long_context_prefill_bf16", "prefill", "bf16", B=1, L=32768, h_q=64, h_kv=8, d=128,
+        causal=True, std=1.0 / math.sqrt(2.0), seed=5,
+        description="bf16 causal prefill, B=1 L=32768 h_q=64 h_kv=8 d=128"),
+}
+
+# Order in which the five workloads are listed everywhere.
+WORKLOAD_ORDER = ["tiny_prefill_f32", "worked_example_prefill_bf16", "llama2_7b_prefill_bf16",
+                  "batched_decode_bf16", "long_context_prefill_bf16"]
+
+
+def _draw(gen, shape, std, dtype):
+    x = torch.randn(*shape, generator=gen, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(torch.tensor(std, dtype=torch.float32))
+    return x.to(dtype)
+
+
+def prefill_inputs(B, L, h_q, h_kv, d, seed, std=1.0, dtype=torch.bfloat16):
+    """Seeded CPU tensors q [B,L,h_q,d], k, v [B,L,h_kv,d] of the given dtype."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    q = _draw(gen, (B, L, h_q, d), std, dtype)
+    k = _draw(gen, (B, L, h_kv, d), std, dtype)
+    v = _draw(gen, (B, L, h_kv, d), std, dtype)
+    return q, k, v
+
+
+def decode_inputs(B, h_q, h_kv, S, d, seed, seqlen_range, std=1.0, dtype=torch.bfloat16):
+    """Seeded CPU tensors: seqlens [B] int32, q [B,1,h_q,d], k_cache, v_cache [B,h_kv,S,d]."""
+    lo, hi = seqlen_range
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    seqlens = torch.randint(lo, hi + 1, (B,), generator=gen, dtype=torch.int64).to(torch.int32)
+    q = _draw(gen, (B, 1, h_q, d), std, dtype)
+    k_cache = _draw(gen, (B, h_kv, S, d), std, dtype)
+    v_cache = _draw(gen, (B, h_kv, S, d), std, dtype)
+    return seqlens, q, k_cache, v_cache
+
+
+def workload_inputs(w: Workload):
+    """Inputs of a named workload, as CPU tensors (see prefill_inputs/decode_inputs)."""
+    if w.path == "prefill":
+        return prefill_inputs(w.B, w.L, w.h_q, w.h_kv, w.d, w.seed, w.std, w.torch_dtype())
+    return decode_inputs(w.B, w.h_q, w.h_kv, w.S, w.d, w.seed, w.seqlen_range, w.std,
+                         w.torch_dtype())
+
+
+def sample_rows(n, B, L, h_q, seed, include=()):
+    """Seeded (b, i, h) triples for sampled checks, sorted by (b, h, i).
+
+    ``include`` adds fixed triples (for example the first and last position).
+    """
+    gen = torch.Generator(device="cpu").manual_seed(int(seed) + 1000003)
+    b = torch.randint(0, B, (n,), generator=gen)
+    i = torch.randint(0, L, (n,), generator=gen)
+    h = torch.randint(0, h_q, (n,), generator=gen)
+    rows = {(int(x), int(y), int(z)) for x, y, z in zip(b, i, h)}
+    rows.update(tuple(int(t) for t in r) for r in include)
+    return sorted(rows, key=lambda r: (r[0], r[2], r[1]))

@@ -1,0 +1,142 @@
+"""Plain fp64 CPU oracle for the grouped-query attention core.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import this package.  The product
+(the HIP library and its Python binding) never imports it, and this package
+imports nothing from the product: the two share no code.
+
+Two independent implementations live here:
+
+* ``gqa_oracle.c`` -- the fp64 C oracle (OpenMP over independent rows), loaded
+  with ctypes.  It explicitly repeats every key/value head once per query head
+  of its group, then evaluates softmax(q k^T * scale) v row by row
+  ("Modern LLM architecture (1): GQA and RMSNorm", §2.1 formula and §2.3
+  repeat_interleave module).
+* ``brute.py`` -- a pure-Python (``math`` only) brute force for tiny inputs.
+
+All functions take and return float64 numpy arrays in the layouts of the
+library's entry points: prefill q, o [B, L, h_q, d] and k, v [B, L, h_kv, d];
+decode q, o [B, h_q, d] (the one new position per sequence), caches
+[B, h_kv, S, d] and seqlens [B].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gqa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libgqa_oracle.so")
+
+# No -ffast-math and no FP contraction: the C code's operation order is the
+# order that is evaluated.
+_CFLAGS = ["-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-Wextra"]
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with the host gcc into ``oracle/libgqa_oracle.so``."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.gqa_oracle_prefill.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_double, P]
+    lib.gqa_oracle_prefill.restype = I
+    lib.gqa_oracle_prefill_rows.argtypes = [P, P, ctypes.c_int64, P, P, I, I, I, I, I, I,
+                                           ctypes.c_double, P, P]
+    lib.gqa_oracle_prefill_rows.restype = I
+    lib.gqa_oracle_decode.argtypes = [P, P, P, P, P, I, I, I, I, I]
+    lib.gqa_oracle_decode.restype = I
+    lib.gqa_oracle_num_threads.argtypes = []
+    lib.gqa_oracle_num_threads.restype = I
+    _lib = lib
+    return lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    """Threads the oracle's parallel loops use (OpenMP's maximum)."""
+    return int(_load().gqa_oracle_num_threads())
+
+
+def prefill(q, k, v, causal: bool, scale: float, return_probs: bool = False):
+    """Full prefill.  q [B,L,h_q,d], k/v [B,L,h_kv,d] -> o [B,L,h_q,d] (float64).
+
+    With ``return_probs`` also returns the softmax matrices [B, h_q, L, L]
+    (zero where a key is masked).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, L, h_q, d = q.shape
+    h_kv = k.shape[2]
+    if k.shape != (B, L, h_kv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, L, h_kv, d] matching q")
+    o = np.empty_like(q)
+    probs = np.empty((B, h_q, L, L)) if return_probs else None
+    rc = _load().gqa_oracle_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, L, h_q, h_kv, d,
+                                    int(bool(causal)), float(scale),
+                                    _ptr(probs) if probs is not None else None)
+    if rc != 0:
+        raise ValueError("oracle prefill rejected its arguments (rc=%d)" % rc)
+    return (o, probs) if return_probs else o
+
+
+def prefill_rows(q_rows, rows_bih, k, v, h_q: int, causal: bool, scale: float):
+    """Prefill output of selected rows only.
+
+    q_rows [n, d] holds the query vectors of the rows (b, i, h) listed in
+    rows_bih [n, 3]; k/v are the full [B, L, h_kv, d] tensors.  Returns [n, d].
+    """
+    q_rows = _f64(q_rows)
+    rows = np.ascontiguousarray(np.asarray(rows_bih, dtype=np.int64).reshape(-1, 3))
+    k, v = _f64(k), _f64(v)
+    B, L, h_kv, d = k.shape
+    n = rows.shape[0]
+    if q_rows.shape != (n, d):
+        raise ValueError("q_rows must be [n, d]")
+    out = np.empty((n, d))
+    rc = _load().gqa_oracle_prefill_rows(_ptr(q_rows), _ptr(rows), n, _ptr(k), _ptr(v), B, L,
+                                         h_q, h_kv, d, int(bool(causal)), float(scale),
+                                         _ptr(out), None)
+    if rc != 0:
+        raise ValueError("oracle prefill_rows rejected its arguments (rc=%d)" % rc)
+    return out
+
+
+def decode(q, k_cache, v_cache, seqlens):
+    """Decode.  q [B,h_q,d], caches [B,h_kv,S,d], seqlens [B] -> o [B,h_q,d]."""
+    q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
+    sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+    B, h_q, d = q.shape
+    _, h_kv, S, _ = kc.shape
+    if kc.shape != (B, h_kv, S, d) or vc.shape != kc.shape or sl.shape != (B,):
+        raise ValueError("decode shapes do not match")
+    o = np.empty_like(q)
+    rc = _load().gqa_oracle_decode(_ptr(q), _ptr(kc), _ptr(vc), _ptr(sl), _ptr(o), B, h_q,
+                                   h_kv, S, d)
+    if rc != 0:
+        raise ValueError("oracle decode rejected its arguments (rc=%d)" % rc)
+    return o

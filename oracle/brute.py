@@ -1,0 +1,74 @@
+"""Pure-Python brute force for tiny grouped-query attention cases.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  Uses nothing but the
+``math`` module and nested lists, so that it shares no code path with the C
+oracle or with numpy/torch.  It follows the same definition, written out
+independently:
+
+* group size G = h_q / h_kv, query head h uses key/value head h // G
+  ("Modern LLM architecture (1): GQA and RMSNorm", §2.3;
+  "Attention in Qwen, DeepSeek and LLaMA3", §2.2);
+* weights w_j = exp(s_j) / sum_t exp(s_t) with s_j = scale * <q, k_j> over the
+  visible keys ("Modern LLM architecture (1)", §2.1);
+* output = sum_j w_j v_j.
+
+Inputs are nested lists (or anything indexable the same way); outputs are
+nested lists of floats.
+"""
+import math
+
+
+def _softmax_average(q, keys, values, scale):
+    """sum_j softmax_j(scale * <q, k_j>) * v_j over the given keys; [] keys -> zeros."""
+    d_v = len(values[0]) if values else len(q)
+    if not keys:
+        return [0.0] * d_v, []
+    scores = [scale * math.fsum(qc * kc for qc, kc in zip(q, key)) for key in keys]
+    top = max(scores)
+    expd = [math.exp(s - top) for s in scores]
+    total = math.fsum(expd)
+    weights = [e / total for e in expd]
+    out = [math.fsum(w * val[c] for w, val in zip(weights, values)) for c in range(d_v)]
+    return out, weights
+
+
+def prefill(q, k, v, causal, scale):
+    """q [B][L][h_q][d], k/v [B][L][h_kv][d] -> (o [B][L][h_q][d], probs [B][h_q][L][L])."""
+    B, L, h_q = len(q), len(q[0]), len(q[0][0])
+    h_kv = len(k[0][0])
+    if h_q % h_kv:
+        raise ValueError("h_q must be a multiple of h_kv")
+    G = h_q // h_kv
+    o = [[[None] * h_q for _ in range(L)] for _ in range(B)]
+    probs = [[[[0.0] * L for _ in range(L)] for _ in range(h_q)] for _ in range(B)]
+    for b in range(B):
+        for h in range(h_q):
+            g = h // G
+            for i in range(L):
+                last = i + 1 if causal else L
+                keys = [k[b][j][g] for j in range(last)]
+                vals = [v[b][j][g] for j in range(last)]
+                out, w = _softmax_average(q[b][i][h], keys, vals, scale)
+                o[b][i][h] = out
+                for j, wj in enumerate(w):
+                    probs[b][h][i][j] = wj
+    return o, probs
+
+
+def decode(q, k_cache, v_cache, seqlens):
+    """q [B][h_q][d], caches [B][h_kv][S][d], seqlens [B] -> o [B][h_q][d]."""
+    B, h_q, d = len(q), len(q[0]), len(q[0][0])
+    h_kv = len(k_cache[0])
+    G = h_q // h_kv
+    scale = 1.0 / math.sqrt(d)
+    o = []
+    for b in range(B):
+        n = int(seqlens[b])
+        row = []
+        for h in range(h_q):
+            g = h // G
+            out, _ = _softmax_average(q[b][h], [k_cache[b][g][j] for j in range(n)],
+                                      [v_cache[b][g][j] for j in range(n)], scale)
+            row.append(out)
+        o.append(row)
+    return o

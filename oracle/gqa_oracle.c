@@ -1,0 +1,277 @@
+/*
+ * gqa_oracle.c -- plain fp64 CPU reference for the grouped-query attention core.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the oracle that the HIP kernels are
+ * checked against.  Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg may load it.  It shares no code, header, table or helper with
+ * the GPU library, and it is deliberately slow: no tiling, no online softmax,
+ * no fusion, no reordering of the arithmetic beyond what the definition states.
+ *
+ * What it computes (all in double precision):
+ *
+ *   Scaled dot-product attention, softmax(Q K^T * scale) V, per query head
+ *   ("Modern LLM architecture (1): GQA and RMSNorm", §2.1, the attention
+ *   formula), with the grouped-query head map of the same page, §2.3: the
+ *   h_kv key/value heads are repeated group_size = h_q / h_kv times along the
+ *   head axis with repeat_interleave, so query head h reads key/value head
+ *   floor(h / group_size).  The integer-division form of that map is also
+ *   stated in "Attention in Qwen, DeepSeek and LLaMA3", §2.2 (cache reuse
+ *   structure) and §2.3 (the q_idx // 4 cache index).
+ *
+ *   The repeat is materialised explicitly (one copied slab per query head),
+ *   exactly as the repeat_interleave in the page's module does, so that no
+ *   stride trick of the GPU path can hide in here.
+ *
+ *   Causal masking keeps key j for query i iff j <= i (square alignment; the
+ *   masked_fill(mask == 0, -inf) convention of the same page, §2.1-§2.3).
+ *
+ *   Decode: one new query token per sequence attends over the cache rows
+ *   [0, seqlens[b]) of a head-major cache [B, h_kv, S, d]
+ *   ("What is Grouped-Query Attention", §2.2 step 2 for the cache layout and
+ *   §3.2 for appending the new token before attending).  The scale is
+ *   1/sqrt(d).  A sequence with seqlens[b] == 0 has no visible key; its output
+ *   is defined as zero.
+ *
+ * Every entry point returns 0 on success and a negative number for a bad
+ * argument (it never aborts).  Arrays are dense, row-major, caller-owned.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_ERR_ARG (-1)
+#define ORACLE_ERR_NOMEM (-2)
+
+/* Number of threads the parallel loops below will use. */
+int gqa_oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Query head h reads key/value head floor(h / group_size). */
+static int kv_head_of(int h, int h_q, int h_kv) {
+    int group_size = h_q / h_kv;
+    return h / group_size;
+}
+
+/*
+ * Explicit repeat: copy the n_keys rows of key/value head kvh of sequence b out
+ * of a strided source into a dense [n_keys][d] slab.  The source element
+ * (b, j, kvh, c) sits at b*sb + j*sj + kvh*sh + c.
+ */
+static void repeat_kv_slab(const double *src, long sb, long sj, long sh, int b,
+                           int kvh, int n_keys, int d, double *dst) {
+    for (int j = 0; j < n_keys; ++j) {
+        const double *row = src + (long)b * sb + (long)j * sj + (long)kvh * sh;
+        memcpy(dst + (long)j * d, row, sizeof(double) * (size_t)d);
+    }
+}
+
+/*
+ * One query row against n_vis keys of its (already repeated) head:
+ *   s_j   = scale * sum_c q[c] * krep[j][c]          (c ascending)
+ *   m     = max_j s_j
+ *   e_j   = exp(s_j - m),  Z = sum_j e_j
+ *   out   = sum_j (e_j / Z) * vrep[j]
+ * The max subtraction does not change the result in real arithmetic; it keeps
+ * exp() finite.  n_vis == 0 gives a zero row.  `scores` is scratch of n_vis
+ * doubles; `probs`, when not NULL, receives e_j / Z.
+ */
+static void attend_one_row(const double *q, const double *krep, const double *vrep,
+                           int n_vis, int d, double scale, double *scores,
+                           double *out, double *probs) {
+    for (int c = 0; c < d; ++c) out[c] = 0.0;
+    if (n_vis <= 0) return;
+
+    double m = -INFINITY;
+    for (int j = 0; j < n_vis; ++j) {
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c) dot += q[c] * krep[(long)j * d + c];
+        scores[j] = scale * dot;
+        if (scores[j] > m) m = scores[j];
+    }
+    double z = 0.0;
+    for (int j = 0; j < n_vis; ++j) {
+        scores[j] = exp(scores[j] - m);
+        z += scores[j];
+    }
+    for (int j = 0; j < n_vis; ++j) {
+        double p = scores[j] / z;
+        if (probs) probs[j] = p;
+        for (int c = 0; c < d; ++c) out[c] += p * vrep[(long)j * d + c];
+    }
+}
+
+static int check_heads(int h_q, int h_kv) {
+    if (h_q <= 0 || h_kv <= 0) return ORACLE_ERR_ARG;
+    if (h_q % h_kv != 0) return ORACLE_ERR_ARG; /* group size must be whole */
+    return 0;
+}
+
+/*
+ * Prefill for a list of query rows.
+ *   q_rows  [n_rows][d]   the query vectors of the listed rows
+ *   row_bih [n_rows][3]   (b, i, h) of each listed row
+ *   k, v    [B][L][h_kv][d]
+ *   out     [n_rows][d]
+ *   probs   NULL, or [n_rows][L]: the softmax row (zeros beyond the visible keys)
+ * Rows are processed in groups that share (b, h) so the repeated slab of their
+ * head is built once per group; rows must be sorted by (b, h) for that to help,
+ * but any order is correct.
+ */
+int gqa_oracle_prefill_rows(const double *q_rows, const int64_t *row_bih, int64_t n_rows,
+                            const double *k, const double *v, int B, int L, int h_q,
+                            int h_kv, int d, int causal, double scale, double *out,
+                            double *probs) {
+    if (B <= 0 || L <= 0 || d <= 0 || n_rows < 0) return ORACLE_ERR_ARG;
+    if (check_heads(h_q, h_kv)) return ORACLE_ERR_ARG;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t b = row_bih[3 * r], i = row_bih[3 * r + 1], h = row_bih[3 * r + 2];
+        if (b < 0 || b >= B || i < 0 || i >= L || h < 0 || h >= h_q) return ORACLE_ERR_ARG;
+    }
+    const long sh = d, sj = (long)h_kv * d, sb = (long)L * sj;
+
+    /* Split the row list into runs of equal (b, h). */
+    int64_t *run_start = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_rows + 1));
+    if (!run_start) return ORACLE_ERR_NOMEM;
+    int64_t n_runs = 0;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        if (r == 0 || row_bih[3 * r] != row_bih[3 * (r - 1)] ||
+            row_bih[3 * r + 2] != row_bih[3 * (r - 1) + 2])
+            run_start[n_runs++] = r;
+    }
+    run_start[n_runs] = n_rows;
+
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *krep = (double *)malloc(sizeof(double) * (size_t)L * d);
+        double *vrep = (double *)malloc(sizeof(double) * (size_t)L * d);
+        double *scores = (double *)malloc(sizeof(double) * (size_t)L);
+        if (!krep || !vrep || !scores) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t run = 0; run < n_runs; ++run) {
+                int64_t r0 = run_start[run], r1 = run_start[run + 1];
+                int b = (int)row_bih[3 * r0], h = (int)row_bih[3 * r0 + 2];
+                int kvh = kv_head_of(h, h_q, h_kv);
+                /* explicit repeat of this head's keys and values */
+                repeat_kv_slab(k, sb, sj, sh, b, kvh, L, d, krep);
+                repeat_kv_slab(v, sb, sj, sh, b, kvh, L, d, vrep);
+                for (int64_t r = r0; r < r1; ++r) {
+                    int i = (int)row_bih[3 * r + 1];
+                    int n_vis = causal ? i + 1 : L;
+                    double *prow = NULL;
+                    if (probs) {
+                        prow = probs + r * (int64_t)L;
+                        for (int j = 0; j < L; ++j) prow[j] = 0.0;
+                    }
+                    attend_one_row(q_rows + r * (int64_t)d, krep, vrep, n_vis, d, scale,
+                                   scores, out + r * (int64_t)d, prow);
+                }
+            }
+        }
+        free(krep);
+        free(vrep);
+        free(scores);
+    }
+    free(run_start);
+    return failed ? ORACLE_ERR_NOMEM : 0;
+}
+
+/*
+ * Full prefill:  q, o [B][L][h_q][d];  k, v [B][L][h_kv][d].
+ * probs: NULL, or [B][h_q][L][L] softmax matrices (zeros where masked).
+ */
+int gqa_oracle_prefill(const double *q, const double *k, const double *v, double *o, int B,
+                       int L, int h_q, int h_kv, int d, int causal, double scale,
+                       double *probs) {
+    if (B <= 0 || L <= 0 || d <= 0) return ORACLE_ERR_ARG;
+    if (check_heads(h_q, h_kv)) return ORACLE_ERR_ARG;
+    int64_t n = (int64_t)B * h_q * L;
+    int64_t *bih = (int64_t *)malloc(sizeof(int64_t) * 3 * (size_t)n);
+    double *qr = (double *)malloc(sizeof(double) * (size_t)(n * d));
+    double *orow = (double *)malloc(sizeof(double) * (size_t)(n * d));
+    if (!bih || !qr || !orow) {
+        free(bih);
+        free(qr);
+        free(orow);
+        return ORACLE_ERR_NOMEM;
+    }
+    /* list rows ordered by (b, h, i); gather their query vectors */
+    int64_t r = 0;
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < h_q; ++h)
+            for (int i = 0; i < L; ++i, ++r) {
+                bih[3 * r] = b;
+                bih[3 * r + 1] = i;
+                bih[3 * r + 2] = h;
+                memcpy(qr + r * d, q + (((int64_t)b * L + i) * h_q + h) * d,
+                       sizeof(double) * (size_t)d);
+            }
+    int rc = gqa_oracle_prefill_rows(qr, bih, n, k, v, B, L, h_q, h_kv, d, causal, scale,
+                                     orow, probs);
+    if (rc == 0) {
+        r = 0;
+        for (int b = 0; b < B; ++b)
+            for (int h = 0; h < h_q; ++h)
+                for (int i = 0; i < L; ++i, ++r)
+                    memcpy(o + (((int64_t)b * L + i) * h_q + h) * d, orow + r * d,
+                           sizeof(double) * (size_t)d);
+    }
+    free(bih);
+    free(qr);
+    free(orow);
+    return rc;
+}
+
+/*
+ * Decode: q, o [B][h_q][d] (the single new position of each sequence);
+ * k_cache, v_cache [B][h_kv][S][d]; seqlens [B] with 0 <= seqlens[b] <= S.
+ * scale = 1/sqrt(d).
+ */
+int gqa_oracle_decode(const double *q, const double *k_cache, const double *v_cache,
+                      const int32_t *seqlens, double *o, int B, int h_q, int h_kv, int S,
+                      int d) {
+    if (B <= 0 || S <= 0 || d <= 0) return ORACLE_ERR_ARG;
+    if (check_heads(h_q, h_kv)) return ORACLE_ERR_ARG;
+    for (int b = 0; b < B; ++b)
+        if (seqlens[b] < 0 || seqlens[b] > S) return ORACLE_ERR_ARG;
+    const double scale = 1.0 / sqrt((double)d);
+    const long sj = d, sh = (long)S * d, sb = (long)h_kv * sh;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *krep = (double *)malloc(sizeof(double) * (size_t)S * d);
+        double *vrep = (double *)malloc(sizeof(double) * (size_t)S * d);
+        double *scores = (double *)malloc(sizeof(double) * (size_t)S);
+        if (!krep || !vrep || !scores) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bh = 0; bh < (int64_t)B * h_q; ++bh) {
+                int b = (int)(bh / h_q), h = (int)(bh % h_q);
+                int kvh = kv_head_of(h, h_q, h_kv);
+                int n = seqlens[b];
+                repeat_kv_slab(k_cache, sb, sj, sh, b, kvh, n, d, krep);
+                repeat_kv_slab(v_cache, sb, sj, sh, b, kvh, n, d, vrep);
+                attend_one_row(q + bh * d, krep, vrep, n, d, scale, scores, o + bh * d,
+                               NULL);
+            }
+        }
+        free(krep);
+        free(vrep);
+        free(scores);
+    }
+    return failed ? ORACLE_ERR_NOMEM : 0;
+}

@@ -1,0 +1,313 @@
+"""Pins that tie the fp64 oracle to what the pages and the mathematics fix.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+something other than itself: a hand-derived closed form stored under
+``tests/golden/`` (with its citation), a library routine that the method
+reduces to in a special case (torch's fp64 scaled_dot_product_attention for
+MHA, MQA and its enable_gqa form), an invariant of softmax attention, or the
+independent pure-Python brute force.
+
+``test_oracle_pins.py`` runs every pin under pytest.  ``test_oracle_mutants.py``
+runs this file as a script against deliberately broken copies of the C oracle
+(``python tests/oracle_pins.py <path/to/lib.so>``) and expects a failure for
+each, which shows the pins catch plausible mistakes.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+import sys
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+from oracle import brute  # noqa: E402
+
+GOLDEN = os.path.join(HERE, "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand(shape, seed, std=1.0):
+    g = np.random.default_rng(seed)
+    return g.standard_normal(shape) * std
+
+
+def _close(a, b, tol, what):
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max-abs error {err:.3e} > {tol:.1e}"
+
+
+def _sdpa(q, k, v, causal, scale, enable_gqa=False):
+    """torch fp64 SDPA on [B, L, H, d] tensors (test-only library routine)."""
+    tq = torch.from_numpy(np.ascontiguousarray(q)).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(np.ascontiguousarray(k)).permute(0, 2, 1, 3)
+    tv = torch.from_numpy(np.ascontiguousarray(v)).permute(0, 2, 1, 3)
+    o = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale,
+                                       enable_gqa=enable_gqa)
+    return o.permute(0, 2, 1, 3).contiguous().numpy()
+
+
+# ---------------------------------------------------------------- golden pins
+
+def pin_hand_2x2():
+    g = _golden("hand_2x2.json")
+    q, k, v = (np.array(g[n]) for n in ("q", "k", "v"))
+    tol = g["tolerance"]
+    o, p = oracle.prefill(q, k, v, causal=False, scale=g["scale"], return_probs=True)
+    _close(o, g["expected_noncausal"], tol, "hand 2x2 non-causal")
+    _close(p, g["expected_probs_noncausal"], tol, "hand 2x2 probabilities")
+    o = oracle.prefill(q, k, v, causal=True, scale=g["scale"])
+    _close(o, g["expected_causal"], tol, "hand 2x2 causal")
+    assert np.array_equal(o[0, 0, 0], v[0, 0, 0]), "causal row 0 must equal V[0] exactly"
+    for causal, key in ((False, "expected_noncausal"), (True, "expected_causal")):
+        ob, _ = brute.prefill(g["q"], g["k"], g["v"], causal, g["scale"])
+        _close(ob, g[key], tol, f"brute force hand 2x2 causal={causal}")
+
+
+def _head_map_tensors(g):
+    L = len(g["k_per_kv_head"][0])
+    h_q = len(g["q_per_head"])
+    q = np.array([[g["q_per_head"] for _ in range(L)]])  # [1, L, h_q, d]
+    k = np.array([np.array(g["k_per_kv_head"]).transpose(1, 0, 2)])  # [1, L, h_kv, d]
+    v = np.array([np.array(g["v_per_kv_head"]).transpose(1, 0, 2)])
+    return q, k, v, L, h_q
+
+
+def pin_head_map():
+    g = _golden("head_map_4q2kv.json")
+    q, k, v, L, h_q = _head_map_tensors(g)
+    tol = g["tolerance"]
+    o = oracle.prefill(q, k, v, causal=False, scale=g["scale"])
+    for i in range(L):
+        _close(o[0, i], g["expected_noncausal_per_head"], tol, f"head map non-causal row {i}")
+    o = oracle.prefill(q, k, v, causal=True, scale=g["scale"])
+    exp = np.array(g["expected_causal_per_head_per_row"]).transpose(1, 0, 2)  # [L, h_q, d]
+    _close(o[0], exp, tol, "head map causal")
+    ob, _ = brute.prefill(q.tolist(), k.tolist(), v.tolist(), True, g["scale"])
+    _close(np.array(ob)[0], exp, tol, "brute force head map causal")
+
+
+def pin_decode_golden():
+    g = _golden("decode_cache_3seq.json")
+    B = len(g["seqlens"])
+    kc = np.array([[g["k_rows"]] for _ in range(B)])  # [B, 1, S, d]
+    vc = np.array([[g["v_rows"]] for _ in range(B)])
+    q = np.array(g["q"])
+    o = oracle.decode(q, kc, vc, g["seqlens"])
+    _close(o, g["expected"], g["tolerance"], "decode golden")
+    ob = brute.decode(g["q"], kc.tolist(), vc.tolist(), g["seqlens"])
+    _close(ob, g["expected"], g["tolerance"], "brute force decode golden")
+
+
+# ------------------------------------------------------- library reductions
+
+def pin_mha_reduction():
+    """h_kv == h_q: per-head softmax attention == torch fp64 SDPA."""
+    B, L, H, d = 2, 9, 3, 8
+    q, k, v = _rand((B, L, H, d), 1), _rand((B, L, H, d), 2), _rand((B, L, H, d), 3)
+    for causal in (False, True):
+        o = oracle.prefill(q, k, v, causal=causal, scale=0.3)
+        _close(o, _sdpa(q, k, v, causal, 0.3), 1e-12, f"MHA vs SDPA causal={causal}")
+
+
+def pin_mqa_reduction():
+    """h_kv == 1: equals attention against one key/value head broadcast with expand."""
+    B, L, H, d = 2, 7, 4, 6
+    q, k, v = _rand((B, L, H, d), 4), _rand((B, L, 1, d), 5), _rand((B, L, 1, d), 6)
+    kx, vx = np.broadcast_to(k, (B, L, H, d)), np.broadcast_to(v, (B, L, H, d))
+    for causal in (False, True):
+        o = oracle.prefill(q, k, v, causal=causal, scale=1 / math.sqrt(d))
+        _close(o, _sdpa(q, kx, vx, causal, 1 / math.sqrt(d)), 1e-12,
+               f"MQA vs expanded SDPA causal={causal}")
+
+
+def pin_gqa_library():
+    """General group sizes against torch's own grouped form (enable_gqa) and the brute force."""
+    for (B, L, h_q, h_kv, d, seed) in ((2, 11, 6, 2, 5, 7), (1, 13, 8, 4, 4, 8),
+                                       (2, 5, 6, 3, 3, 9)):
+        q = _rand((B, L, h_q, d), seed)
+        k = _rand((B, L, h_kv, d), seed + 1)
+        v = _rand((B, L, h_kv, d), seed + 2)
+        for causal in (False, True):
+            o = oracle.prefill(q, k, v, causal=causal, scale=0.4)
+            ref = _sdpa(q, k, v, causal, 0.4, enable_gqa=True)
+            _close(o, ref, 1e-12, f"GQA {h_q}/{h_kv} vs SDPA enable_gqa causal={causal}")
+    q, k, v = _rand((1, 4, 4, 3), 20), _rand((1, 4, 2, 3), 21), _rand((1, 4, 2, 3), 22)
+    ob, _ = brute.prefill(q.tolist(), k.tolist(), v.tolist(), True, 0.7)
+    _close(oracle.prefill(q, k, v, causal=True, scale=0.7), ob, 1e-12, "C oracle vs brute force")
+
+
+# ------------------------------------------------------------------ properties
+
+def pin_rows_sum_to_one():
+    q, k, v = _rand((2, 10, 4, 6), 30), _rand((2, 10, 2, 6), 31), _rand((2, 10, 2, 6), 32)
+    for causal in (False, True):
+        _, p = oracle.prefill(q, k, v, causal=causal, scale=0.5, return_probs=True)
+        _close(p.sum(-1), np.ones(p.shape[:-1]), 1e-14, f"softmax rows sum to 1 causal={causal}")
+        assert (p >= 0).all()
+        if causal:
+            L = p.shape[-1]
+            assert np.all(p[..., np.triu_indices(L, 1)[0], np.triu_indices(L, 1)[1]] == 0.0), \
+                "masked probabilities must be exactly zero"
+
+
+def pin_k_zero_mean():
+    """K == 0: every visible key has weight 1/n, output = mean of the visible V rows."""
+    B, L, h_q, h_kv, d = 2, 8, 4, 2, 5
+    q, v = _rand((B, L, h_q, d), 40), _rand((B, L, h_kv, d), 41)
+    k = np.zeros((B, L, h_kv, d))
+    G = h_q // h_kv
+    o = oracle.prefill(q, k, v, causal=False, scale=0.9)
+    for h in range(h_q):
+        _close(o[:, :, h], np.broadcast_to(v[:, :, h // G].mean(1, keepdims=True), (B, L, d)),
+               1e-12, "K=0 non-causal mean")
+    o = oracle.prefill(q, k, v, causal=True, scale=0.9)
+    for h in range(h_q):
+        cum = np.cumsum(v[:, :, h // G], axis=1) / np.arange(1, L + 1)[None, :, None]
+        _close(o[:, :, h], cum, 1e-12, "K=0 causal running mean")
+    S = 12
+    kc, vc = np.zeros((B, h_kv, S, d)), _rand((B, h_kv, S, d), 42)
+    lens = [5, 12]
+    od = oracle.decode(q[:, 0], kc, vc, lens)
+    for b in range(B):
+        for h in range(h_q):
+            _close(od[b, h], vc[b, h // G, :lens[b]].mean(0), 1e-12, "K=0 decode mean")
+
+
+def pin_causal_row0():
+    B, L, h_q, h_kv, d = 3, 6, 8, 2, 7
+    q, k, v = _rand((B, L, h_q, d), 50), _rand((B, L, h_kv, d), 51), _rand((B, L, h_kv, d), 52)
+    o = oracle.prefill(q, k, v, causal=True, scale=0.125)
+    for h in range(h_q):
+        assert np.array_equal(o[:, 0, h], v[:, 0, h // (h_q // h_kv)]), "causal row 0 != V[0]"
+
+
+def pin_identical_heads():
+    B, L, h_q, h_kv, d = 2, 9, 8, 2, 4
+    G = h_q // h_kv
+    qg = _rand((B, L, h_kv, 1, d), 60)
+    q = np.repeat(qg, G, axis=3).reshape(B, L, h_q, d)
+    k, v = _rand((B, L, h_kv, d), 61), _rand((B, L, h_kv, d), 62)
+    for causal in (False, True):
+        o = oracle.prefill(q, k, v, causal=causal, scale=0.3)
+        for h in range(h_q):
+            assert np.array_equal(o[:, :, h], o[:, :, (h // G) * G]), "heads of a group differ"
+        # heads of different groups differ (the key/value heads differ)
+        assert not np.allclose(o[:, :, 0], o[:, :, G])
+
+
+def pin_invariances():
+    B, L, h_q, h_kv, d = 2, 10, 6, 3, 5
+    q, k, v = _rand((B, L, h_q, d), 70), _rand((B, L, h_kv, d), 71), _rand((B, L, h_kv, d), 72)
+    for causal in (False, True):
+        base = oracle.prefill(q, k, v, causal=causal, scale=0.4)
+        u = _rand((d,), 73)
+        _close(oracle.prefill(q, k + u, v, causal=causal, scale=0.4), base, 1e-11,
+               f"key shift invariance causal={causal}")
+        _close(oracle.prefill(3.0 * q, k, v, causal=causal, scale=0.4 / 3.0), base, 1e-11,
+               f"q scaling invariance causal={causal}")
+        c = np.full_like(v, 2.5)
+        _close(oracle.prefill(q, k, c, causal=causal, scale=0.4), np.full_like(q, 2.5), 1e-12,
+               "constant V rows")
+    perm = np.random.default_rng(74).permutation(L)
+    base = oracle.prefill(q, k, v, causal=False, scale=0.4)
+    _close(oracle.prefill(q, k[:, perm], v[:, perm], causal=False, scale=0.4), base, 1e-12,
+           "key/value permutation invariance")
+    S = 9
+    kc, vc = _rand((B, h_kv, S, d), 75), _rand((B, h_kv, S, d), 76)
+    lens = [9, 6]
+    od = oracle.decode(q[:, 0], kc, vc, lens)
+    kp, vp = kc.copy(), vc.copy()
+    for b in range(B):
+        p = np.random.default_rng(77 + b).permutation(lens[b])
+        kp[b, :, :lens[b]] = kc[b][:, p]
+        vp[b, :, :lens[b]] = vc[b][:, p]
+    _close(oracle.decode(q[:, 0], kp, vp, lens), od, 1e-12, "decode permutation invariance")
+
+
+def pin_cross_path():
+    """decode of the last position == row L-1 of causal prefill over the same keys."""
+    B, L, h_q, h_kv, d = 2, 12, 8, 2, 6
+    q, k, v = _rand((B, L, h_q, d), 80), _rand((B, L, h_kv, d), 81), _rand((B, L, h_kv, d), 82)
+    o = oracle.prefill(q, k, v, causal=True, scale=1 / math.sqrt(d))
+    kc = np.ascontiguousarray(k.transpose(0, 2, 1, 3))
+    vc = np.ascontiguousarray(v.transpose(0, 2, 1, 3))
+    od = oracle.decode(q[:, L - 1], kc, vc, [L] * B)
+    _close(od, o[:, L - 1], 1e-12, "decode vs last causal prefill row")
+    od = oracle.decode(q[:, 4], kc, vc, [5] * B)
+    _close(od, o[:, 4], 1e-12, "decode with seqlen 5 vs causal prefill row 4")
+
+
+def pin_rows_match_full():
+    B, L, h_q, h_kv, d = 2, 7, 4, 2, 3
+    q, k, v = _rand((B, L, h_q, d), 90), _rand((B, L, h_kv, d), 91), _rand((B, L, h_kv, d), 92)
+    full = oracle.prefill(q, k, v, causal=True, scale=0.6)
+    rows = [(1, 6, 3), (1, 0, 3), (0, 2, 1), (0, 5, 1), (1, 3, 0)]
+    qr = np.array([q[b, i, h] for b, i, h in rows])
+    out = oracle.prefill_rows(qr, rows, k, v, h_q, causal=True, scale=0.6)
+    _close(out, np.array([full[b, i, h] for b, i, h in rows]), 0.0, "rows entry vs full entry")
+
+
+def pin_decode_tail_ignored():
+    B, h_q, h_kv, S, d = 3, 4, 2, 8, 4
+    q = _rand((B, h_q, d), 100)
+    kc, vc = _rand((B, h_kv, S, d), 101), _rand((B, h_kv, S, d), 102)
+    lens = [3, 8, 0]
+    base = oracle.decode(q, kc, vc, lens)
+    kp, vp = kc.copy(), vc.copy()
+    for b in range(B):
+        kp[b, :, lens[b]:] = np.nan
+        vp[b, :, lens[b]:] = np.nan
+    o = oracle.decode(q, kp, vp, lens)
+    assert np.array_equal(o, base), "rows beyond seqlens leaked into the output"
+    assert np.array_equal(o[2], np.zeros((h_q, d))), "seqlen 0 must give zeros"
+
+
+def pin_argument_errors():
+    q, k = np.zeros((1, 2, 3, 4)), np.zeros((1, 2, 2, 4))
+    try:
+        oracle.prefill(q, k, k, causal=False, scale=1.0)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("h_q % h_kv != 0 must be rejected")
+
+
+ALL_PINS = [pin_hand_2x2, pin_head_map, pin_decode_golden, pin_mha_reduction,
+            pin_mqa_reduction, pin_gqa_library, pin_rows_sum_to_one, pin_k_zero_mean,
+            pin_causal_row0, pin_identical_heads, pin_invariances, pin_cross_path,
+            pin_rows_match_full, pin_decode_tail_ignored, pin_argument_errors]
+
+
+def main(argv):
+    """Run every pin against the oracle library at argv[1]; exit 1 if any fails."""
+    if len(argv) > 1:
+        oracle._LIB_PATH = argv[1]
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except AssertionError as e:
+            failed.append(f"{pin.__name__}: {e}")
+    for f in failed:
+        print("FAIL", f)
+    print("pins failed: %d of %d" % (len(failed), len(ALL_PINS)))
+    return 1 if failed else 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv))

@@ -1,0 +1,58 @@
+"""Plant plausible mistakes in a copy of the C oracle and check the pins catch each.
+
+Every mutant is a one-line textual edit of oracle/gqa_oracle.c, compiled with
+gcc into a temporary directory and run through ``tests/oracle_pins.py`` in a
+child process (a mutant may crash; that counts as caught).  The unmodified
+source is run the same way as a control and must pass.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(ROOT, "oracle", "gqa_oracle.c")
+
+MUTANTS = {
+    "modulo_head_map": ("return h / group_size;", "return h % h_kv;"),
+    "scale_dropped": ("scores[j] = scale * dot;", "scores[j] = dot;"),
+    "causal_off_by_one": ("int n_vis = causal ? i + 1 : L;", "int n_vis = causal ? i : L;"),
+    "softmax_sign": ("scores[j] = exp(scores[j] - m);", "scores[j] = exp(m - scores[j]);"),
+    "no_normalisation": ("double p = scores[j] / z;", "double p = scores[j];"),
+    "k_v_swapped": ("repeat_kv_slab(k, sb, sj, sh, b, kvh, L, d, krep);",
+                    "repeat_kv_slab(v, sb, sj, sh, b, kvh, L, d, krep);"),
+    "transposed_key_index": ("dot += q[c] * krep[(long)j * d + c];",
+                             "dot += q[c] * krep[(long)c * n_vis + j];"),
+    "decode_reads_whole_cache": ("int n = seqlens[b];", "int n = S;"),
+    "decode_scale_wrong": ("const double scale = 1.0 / sqrt((double)d);",
+                           "const double scale = 1.0 / (double)d;"),
+    "first_head_of_group_only": ("int kvh = kv_head_of(h, h_q, h_kv);\n                int n = seqlens[b];",
+                                 "int kvh = 0;\n                int n = seqlens[b];"),
+}
+
+
+def _build_and_run(tmp_path, source, name):
+    src = tmp_path / f"{name}.c"
+    lib = tmp_path / f"lib{name}.so"
+    src.write_text(source)
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                    "-ffp-contract=off", str(src), "-o", str(lib), "-lm"], check=True)
+    env = dict(os.environ, OMP_NUM_THREADS="2")
+    return subprocess.run([sys.executable, os.path.join(HERE, "oracle_pins.py"), str(lib)],
+                          capture_output=True, text=True, env=env, timeout=300)
+
+
+def test_unmutated_oracle_passes_all_pins(tmp_path):
+    r = _build_and_run(tmp_path, open(SRC).read(), "control")
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    text = open(SRC).read()
+    old, new = MUTANTS[name]
+    assert text.count(old) == 1, f"mutation site for {name} not found exactly once"
+    r = _build_and_run(tmp_path, text.replace(old, new), name)
+    assert r.returncode != 0, f"mutant {name} survived every pin:\n{r.stdout}"
