@@ -1,0 +1,153 @@
+"""MI355X (gfx950) grouped-query attention core: Python binding of ``libgqa_hip.so``.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/gqa.h``.  PyTorch supplies device memory
+and the current stream.  There is no fallback: if the library is missing or
+the device is not a gfx950 GPU, the calls raise.
+
+    prefill(q, k, v, causal=..., scale=None, out=None)
+        q [B, L, h_q, d], k/v [B, L, h_kv, d] (bf16 or fp32, contiguous, on the
+        GPU) -> o [B, L, h_q, d].  Query head h reads key/value head
+        h // (h_q // h_kv).
+    decode(q, k_cache, v_cache, seqlens, out=None, workspace=None, chunk=0)
+        q [B, 1, h_q, d] bf16, caches [B, h_kv, S, d] bf16, seqlens [B] int32
+        -> o [B, 1, h_q, d].
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libgqa_hip.so")
+
+GQA_F32 = 0
+GQA_BF16 = 1
+
+_lib = None
+
+
+class GQAError(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {status_string(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libgqa_hip.so`` (building it first only if it does not exist)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+        _build.build()
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.gqa_prefill.argtypes = [P, P, P, P, I, I, I, I, I, I, I, F, P]
+    L.gqa_prefill.restype = I
+    L.gqa_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, ctypes.c_size_t, P]
+    L.gqa_decode.restype = I
+    L.gqa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.gqa_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.gqa_decode_default_chunk.argtypes = [I]
+    L.gqa_decode_default_chunk.restype = I
+    L.gqa_status_string.argtypes = [I]
+    L.gqa_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().gqa_status_string(int(status)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GQA_BF16
+    if t.dtype == torch.float32:
+        return GQA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(t: torch.Tensor, name: str, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def prefill(q, k, v, *, causal: bool, scale: float | None = None, out=None):
+    _check(q, "q", 4)
+    _check(k, "k", 4)
+    _check(v, "v", 4)
+    B, L, h_q, d = q.shape
+    h_kv = k.shape[2]
+    if tuple(k.shape) != (B, L, h_kv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, L, h_kv, d] with q's B, L and d")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", 4)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().gqa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, L, h_q,
+                           h_kv, d, _dtype_code(q), int(bool(causal)), float(scale), _stream(q))
+    if st != 0:
+        raise GQAError(st, "gqa_prefill")
+    return out
+
+
+def decode_workspace_bytes(B: int, h_q: int, S: int, d: int, chunk: int = 0) -> int:
+    return int(lib().gqa_decode_workspace_bytes(B, h_q, S, d, chunk))
+
+
+def decode_default_chunk(S: int) -> int:
+    return int(lib().gqa_decode_default_chunk(S))
+
+
+def decode(q, k_cache, v_cache, seqlens, *, out=None, workspace=None, chunk: int = 0):
+    _check(q, "q", 4)
+    _check(k_cache, "k_cache", 4)
+    _check(v_cache, "v_cache", 4)
+    _check(seqlens, "seqlens", 1)
+    B, one, h_q, d = q.shape
+    if one != 1:
+        raise ValueError("q must be [B, 1, h_q, d]")
+    _, h_kv, S, _ = k_cache.shape
+    if tuple(k_cache.shape) != (B, h_kv, S, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, h_kv, S, d] with q's B and d")
+    if seqlens.dtype != torch.int32 or seqlens.shape[0] != B:
+        raise ValueError("seqlens must be int32 [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", 4)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    need = decode_workspace_bytes(B, h_q, S, d, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                          seqlens.data_ptr(), out.data_ptr(), B, h_q, h_kv, S, d, _dtype_code(q),
+                          int(chunk), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          _stream(q))
+    if st != 0:
+        raise GQAError(st, "gqa_decode")
+    return out

@@ -1,0 +1,164 @@
+// gqa_api.hip -- the C ABI declared in include/gqa.h: argument validation, work
+// map selection and kernel launch.  Nothing here allocates device memory.
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "gqa.h"
+#include "gqa_kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up_256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+gqa_status check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GQA_ERR_DEVICE;
+    if (dev < kMaxDevices) {
+        int known = g_device_ok[dev].load(std::memory_order_relaxed);
+        if (known == 1) return GQA_OK;
+        if (known == 2) return GQA_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GQA_ERR_DEVICE;
+    bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices) g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? GQA_OK : GQA_ERR_DEVICE;
+}
+
+// Largest power of two that divides G, capped at 8: the number of query heads
+// of one group that share a prefill work-group.
+int heads_per_workgroup(int G) {
+    int gw = 1;
+    while (gw < 8 && G % (2 * gw) == 0) gw *= 2;
+    return gw;
+}
+
+int decode_chunk(int chunk, int S) { return chunk == 0 ? gqa_decode_default_chunk(S) : chunk; }
+
+bool chunk_valid(int chunk) { return chunk == 0 || (chunk >= 64 && chunk <= 8192 && chunk % 64 == 0); }
+
+}  // namespace
+
+extern "C" {
+
+const char *gqa_status_string(gqa_status s) {
+    switch (s) {
+        case GQA_OK: return "ok";
+        case GQA_ERR_NULL_POINTER: return "a required pointer is NULL";
+        case GQA_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";
+        case GQA_ERR_SIZE: return "a size, scale or chunk argument is out of range";
+        case GQA_ERR_HEADS: return "h_q is not a multiple of h_kv";
+        case GQA_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
+        case GQA_ERR_DTYPE: return "dtype not supported by this entry point";
+        case GQA_ERR_WORKSPACE: return "decode workspace is NULL or too small";
+        case GQA_ERR_LAUNCH: return "the HIP runtime reported a launch error";
+        case GQA_ERR_DEVICE: return "the current device is not a gfx950 GPU";
+        default: return "unknown status";
+    }
+}
+
+gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *o, int B, int L,
+                       int h_q, int h_kv, int d, gqa_dtype dt, int causal, float scale,
+                       void *hip_stream) {
+    if (!q || !k || !v || !o) return GQA_ERR_NULL_POINTER;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GQA_ERR_ALIGNMENT;
+    if (B <= 0 || L <= 0 || h_q <= 0 || h_kv <= 0) return GQA_ERR_SIZE;
+    if (h_q % h_kv != 0) return GQA_ERR_HEADS;
+    if (d != 64 && d != 128) return GQA_ERR_HEAD_DIM;
+    if (dt != GQA_F32 && dt != GQA_BF16) return GQA_ERR_DTYPE;
+    if (!(scale > 0.f) || !isfinite(scale)) return GQA_ERR_SIZE;
+    const int64_t rows_q = (int64_t)B * L * h_q, rows_kv = (int64_t)B * L * h_kv;
+    if (rows_q > (int64_t)1 << 31 || rows_kv > (int64_t)1 << 31) return GQA_ERR_SIZE;
+
+    gqa::PrefillArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.B = B;
+    a.L = L;
+    a.h_q = h_q;
+    a.h_kv = h_kv;
+    a.G = h_q / h_kv;
+    a.GW = heads_per_workgroup(a.G);
+    a.nsub = a.G / a.GW;
+    a.BM = 32 * (8 / a.GW);
+    a.n_units = B * h_kv * a.nsub;
+    a.n_qtiles = (L + a.BM - 1) / a.BM;
+    a.c = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
+    if ((int64_t)a.n_units * a.n_qtiles > 0x7fffffff) return GQA_ERR_SIZE;
+
+    gqa_status st = check_device();
+    if (st != GQA_OK) return st;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    int rc = dt == GQA_BF16 ? gqa::launch_prefill_bf16(a, d, causal != 0, stream)
+                            : gqa::launch_prefill_f32(a, d, causal != 0, stream);
+    return rc == 0 ? GQA_OK : GQA_ERR_LAUNCH;
+}
+
+int gqa_decode_default_chunk(int S) {
+    (void)S;
+    return 512;
+}
+
+size_t gqa_decode_workspace_bytes(int B, int h_q, int S, int d, int chunk) {
+    if (B <= 0 || h_q <= 0 || S <= 0 || (d != 64 && d != 128) || !chunk_valid(chunk)) return 0;
+    const int ch = decode_chunk(chunk, S);
+    const size_t nc = (size_t)((S + ch - 1) / ch);
+    const size_t rows = (size_t)B * h_q * nc;
+    return round_up_256(rows * d * sizeof(float)) + round_up_256(rows * sizeof(float));
+}
+
+gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *seqlens, void *o, int B, int h_q, int h_kv, int S, int d,
+                      gqa_dtype dt, int chunk, void *workspace, size_t workspace_bytes,
+                      void *hip_stream) {
+    if (!q || !k_cache || !v_cache || !seqlens || !o) return GQA_ERR_NULL_POINTER;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+        (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
+        return GQA_ERR_ALIGNMENT;
+    if (B <= 0 || h_q <= 0 || h_kv <= 0 || S <= 0) return GQA_ERR_SIZE;
+    if (h_q % h_kv != 0) return GQA_ERR_HEADS;
+    if (d != 64 && d != 128) return GQA_ERR_HEAD_DIM;
+    if (dt != GQA_BF16) return GQA_ERR_DTYPE;
+    if (!chunk_valid(chunk)) return GQA_ERR_SIZE;
+    if (B > 65535) return GQA_ERR_SIZE;  // grid z
+    const int ch = decode_chunk(chunk, S);
+    const size_t need = gqa_decode_workspace_bytes(B, h_q, S, d, chunk);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+
+    gqa::DecodeArgs a;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.seqlens = seqlens;
+    a.o = o;
+    a.B = B;
+    a.h_q = h_q;
+    a.h_kv = h_kv;
+    a.G = h_q / h_kv;
+    a.S = S;
+    a.CH = ch;
+    a.NC = (S + ch - 1) / ch;
+    a.n_qsub = (a.G + 15) / 16;
+    if ((int64_t)h_kv * a.n_qsub > 65535) return GQA_ERR_SIZE;  // grid y
+    const size_t rows = (size_t)B * h_q * a.NC;
+    a.opart = static_cast<float *>(workspace);
+    a.lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                      round_up_256(rows * d * sizeof(float)));
+    a.c = (float)(1.4426950408889634 / sqrt((double)d));
+
+    gqa_status st = check_device();
+    if (st != GQA_OK) return st;
+    int rc = gqa::launch_decode_bf16(a, d, static_cast<hipStream_t>(hip_stream));
+    return rc == 0 ? GQA_OK : GQA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// gqa_device.h -- gfx950 device helpers shared by the GQA kernels.
+//
+// Lane layouts of the two bf16 MFMA shapes used here (wave64):
+//
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds A[m = l%32][k = 8*(l/32) + i], i = 0..7
+//     B: lane l holds B[k = 8*(l/32) + i][n = l%32]
+//     D: lane l, element r holds D[m = 8*(r/4) + 4*(l/32) + r%4][n = l%32]
+//
+//   v_mfma_f32_16x16x32_bf16  D[16x16] += A[16x32] * B[32x16]
+//     A: lane l holds A[m = l%16][k = 8*(l/16) + i]
+//     B: lane l holds B[k = 8*(l/16) + i][n = l%16]
+//     D: lane l, element r holds D[m = 4*(l/16) + r][n = l%16]
+//
+//   ds_read_b64_tr_b16: in each group of 16 lanes, lanes 4e..4e+3 each point at
+//   4 consecutive b16 values; together they form row e (16 values) of a 4x16
+//   block, and lane j of the group receives column j of that block.
+//
+// These were checked on the hardware with exact small-integer products.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+#define GQA_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing 64-bit LDS read (4 b16 values), see the layout note above.
+__device__ __forceinline__ short4v lds_read_tr16(const __bf16 *lds_ptr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((GQA_LDS short4v *)(lds_ptr));
+}
+
+__device__ __forceinline__ bf16x8 join_tr(short4v lo, short4v hi) {
+    typedef short short8v __attribute__((ext_vector_type(8)));
+    short8v s = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, s);
+}
+
+// Value held by lane l ^ 32 (the other half of the wave).
+__device__ __forceinline__ float other_half(float x) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(threadIdx.x % 64 < 32 ? p[1] : p[0]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Work-group ids are handed to the 8 XCDs round-robin (id % 8).  Renumber them
+// so that XCD x receives one contiguous range of logical ids: consecutive
+// logical ids (tiles that share a key/value head) then run on one XCD and
+// share its L2.
+__device__ __forceinline__ int xcd_contiguous_id(int id, int total) {
+    const int nx = 8;
+    int per = total / nx, rem = total % nx;
+    int x = id % nx, slot = id / nx;
+    return x * per + (x < rem ? x : rem) + slot;
+}
+
+__device__ __forceinline__ u32x4 load16(const void *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ void store16_lds(void *p, u32x4 v) {
+    *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+}  // namespace gqa

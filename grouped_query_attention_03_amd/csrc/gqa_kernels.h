@@ -1,0 +1,38 @@
+// gqa_kernels.h -- internal launch interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gqa {
+
+// Prefill work map: a work-group covers GW query heads of one group (a
+// "subgroup"; nsub = G / GW of them per key/value head) times BM positions.
+struct PrefillArgs {
+    const void *q, *k, *v;
+    void *o;
+    int B, L, h_q, h_kv, G;
+    int GW, nsub, BM;
+    int n_units;   // B * h_kv * nsub
+    int n_qtiles;  // ceil(L / BM)
+    float c;       // scale * log2(e)
+};
+
+struct DecodeArgs {
+    const void *q, *k_cache, *v_cache;
+    const int32_t *seqlens;
+    void *o;
+    float *opart;  // [B, h_q, NC, d] partial outputs (normalised per chunk)
+    float *lse;    // [B, h_q, NC] log2-sum-exp of each chunk, in scaled log2 units
+    int B, h_q, h_kv, G, S;
+    int CH, NC;    // keys per chunk, chunks per sequence (ceil(S / CH))
+    int n_qsub;    // query-head subgroups of at most 16 heads per key/value head
+    float c;       // log2(e) / sqrt(d)
+};
+
+int launch_prefill_bf16(const PrefillArgs &a, int d, bool causal, hipStream_t stream);
+int launch_prefill_f32(const PrefillArgs &a, int d, bool causal, hipStream_t stream);
+int launch_decode_bf16(const DecodeArgs &a, int d, hipStream_t stream);
+
+}  // namespace gqa

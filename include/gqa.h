@@ -1,0 +1,111 @@
+/*
+ * gqa.h -- C ABI of the MI355X (gfx950) grouped-query attention core.
+ *
+ * The library computes O = softmax(Q K^T * scale) V per query head, where the
+ * h_q query heads are split into h_kv groups of G = h_q / h_kv consecutive
+ * heads and every head of a group reads the group's single key/value head:
+ * query head h uses key/value head floor(h / G).  The key/value heads are never
+ * copied per query head.
+ *   - attention formula: "Modern LLM architecture (1): GQA and RMSNorm", §2.1;
+ *   - grouping and the floor(h / G) head map: the same page, §2.3, and
+ *     "Attention in Qwen, DeepSeek and LLaMA3", §2.2 and §2.3;
+ *   - h_q must be a whole multiple of h_kv: "What is Grouped-Query Attention",
+ *     §2.2.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers (hipMalloc'd or equivalent), dense and
+ *     row-major in the layouts given below, 16-byte aligned.  The caller owns
+ *     every buffer, including the decode workspace; the library allocates and
+ *     frees nothing and keeps no state between calls, so concurrent calls on
+ *     different streams are safe as long as their output/workspace buffers do
+ *     not overlap.
+ *   - `hip_stream` is a hipStream_t (NULL = the default stream).  Work is
+ *     enqueued asynchronously; the caller synchronises.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     non-zero status means nothing was launched.  GQA_ERR_LAUNCH reports a
+ *     failure returned by the HIP runtime at launch time.  No entry point
+ *     throws or aborts.
+ *   - Accumulation and softmax statistics are fp32; outputs have the input
+ *     dtype (bf16 outputs are rounded to nearest even).
+ */
+#ifndef GQA_H
+#define GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
+
+typedef int gqa_status;
+enum {
+    GQA_OK = 0,
+    GQA_ERR_NULL_POINTER = 1,  /* a required pointer is NULL */
+    GQA_ERR_ALIGNMENT = 2,     /* a pointer is not 16-byte aligned */
+    GQA_ERR_SIZE = 3,          /* a size is <= 0, too large, or a chunk size is invalid */
+    GQA_ERR_HEADS = 4,         /* h_q is not a multiple of h_kv */
+    GQA_ERR_HEAD_DIM = 5,      /* d is not 64 or 128 */
+    GQA_ERR_DTYPE = 6,         /* dtype not supported by this entry point */
+    GQA_ERR_WORKSPACE = 7,     /* workspace NULL or smaller than required */
+    GQA_ERR_LAUNCH = 8,        /* the HIP runtime reported an error at launch */
+    GQA_ERR_DEVICE = 9         /* the current device is not a gfx950 GPU */
+};
+
+/*
+ * Prefill: every position attends to the keys of its own sequence.
+ *   q, o : [B, L, h_q, d]   (dtype dt)
+ *   k, v : [B, L, h_kv, d]  (dtype dt)
+ *   causal != 0: position i attends to keys 0..i (square alignment); else to all L.
+ *   scale: multiplies Q K^T before the softmax; pass 1/sqrt(d) for the usual form.
+ *   dt: GQA_BF16 (bf16 MFMA path) or GQA_F32 (fp32 path).
+ * The causal mask follows the masked_fill(mask == 0, -inf) form of
+ * "Modern LLM architecture (1): GQA and RMSNorm", §2.1-§2.3.
+ * Limits: B * h_q * L and B * h_kv * L must each fit in 2^31 elements of d.
+ */
+gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *o, int B, int L,
+                       int h_q, int h_kv, int d, gqa_dtype dt, int causal, float scale,
+                       void *hip_stream);
+
+/*
+ * Decode: one new query position per sequence attends to rows [0, seqlens[b])
+ * of a head-major key/value cache ("What is Grouped-Query Attention", §2.2 step
+ * 2 for the [batch, g, seq_len, d_head] cache and §3.2 for appending the new
+ * token's key/value before attending, which the caller has already done).
+ *   q, o               : [B, 1, h_q, d]  bf16
+ *   k_cache, v_cache   : [B, h_kv, S, d] bf16
+ *   seqlens            : [B] int32 on the device, each in [0, S]; not checked on
+ *                        the device.  seqlens[b] == 0 yields a zero output row.
+ *                        Cache rows at or beyond seqlens[b] are never read.
+ *   scale is fixed to 1/sqrt(d).
+ *   chunk: keys per split of the sequence; 0 picks the library default,
+ *          otherwise a multiple of 64 in [64, 8192].  The result does not
+ *          depend on it beyond floating-point rounding.
+ *   workspace: device buffer of at least gqa_decode_workspace_bytes(...) bytes
+ *          holding per-split partial outputs and log-sum-exp values; its
+ *          contents on entry are ignored.
+ * Two kernels run on `hip_stream`: a split pass over (sequence, key/value
+ * head, chunk) and a log-sum-exp merge pass over (sequence, query head).
+ */
+gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *seqlens, void *o, int B, int h_q, int h_kv, int S, int d,
+                      gqa_dtype dt, int chunk, void *workspace, size_t workspace_bytes,
+                      void *hip_stream);
+
+/* Bytes of decode workspace needed for these sizes and chunk (0 = default);
+ * returns 0 when the sizes or the chunk are invalid. */
+size_t gqa_decode_workspace_bytes(int B, int h_q, int S, int d, int chunk);
+
+/* The chunk size gqa_decode uses when passed chunk == 0. */
+int gqa_decode_default_chunk(int S);
+
+/* Static, NUL-terminated description of a status code. */
+const char *gqa_status_string(gqa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H */

@@ -1,0 +1,123 @@
+"""Host-side checks of the C ABI: symbols, argument validation, workspace sizing.
+
+These run without a GPU.  Validation happens before any HIP call, so fake
+(non-NULL, aligned or misaligned) addresses are enough: nothing is launched
+and nothing is dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import grouped_query_attention_03_amd as gqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa.h")
+
+OK, NULLP, ALIGN, SIZE, HEADS, HEADDIM, DTYPE, WORKSPACE, LAUNCH, DEVICE = range(10)
+A = 0x10000   # a fake 16-byte-aligned address
+MIS = 0x10008  # a fake misaligned address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("gqa_prefill", "gqa_decode", "gqa_decode_workspace_bytes",
+              "gqa_decode_default_chunk", "gqa_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(gqa.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"symbols declared in gqa.h but not exported: {missing}"
+
+
+def test_status_strings_are_distinct():
+    s = [gqa.status_string(i) for i in range(10)]
+    assert len(set(s)) == 10
+    assert gqa.status_string(99) == "unknown status"
+
+
+def prefill_status(q=A, k=A, v=A, o=A, B=1, L=16, h_q=8, h_kv=2, d=64, dt=1, causal=1,
+                   scale=0.125):
+    return gqa.lib().gqa_prefill(q, k, v, o, B, L, h_q, h_kv, d, dt, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULLP), (dict(o=None), NULLP),
+    (dict(k=MIS), ALIGN), (dict(o=MIS), ALIGN),
+    (dict(B=0), SIZE), (dict(L=-3), SIZE), (dict(h_q=0), SIZE), (dict(h_kv=0), SIZE),
+    (dict(h_q=8, h_kv=3), HEADS), (dict(h_q=6, h_kv=4), HEADS),
+    (dict(d=96), HEADDIM), (dict(d=256), HEADDIM), (dict(d=32), HEADDIM),
+    (dict(dt=2), DTYPE),
+    (dict(scale=0.0), SIZE), (dict(scale=-1.0), SIZE), (dict(scale=float("inf")), SIZE),
+    (dict(scale=float("nan")), SIZE),
+    (dict(B=1 << 16, L=1 << 14, h_q=16, h_kv=16), SIZE),
+])
+def test_prefill_rejects_bad_arguments(kw, status):
+    assert prefill_status(**kw) == status
+
+
+def test_prefill_without_a_gpu_reports_the_device():
+    # every argument is valid; with no gfx950 device present the call must fail
+    # loudly (no CPU fallback)
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert prefill_status() == DEVICE
+
+
+def decode_status(q=A, kc=A, vc=A, sl=A, o=A, B=4, h_q=32, h_kv=8, S=1024, d=128, dt=1,
+                  chunk=0, ws=A, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = gqa.decode_workspace_bytes(B, h_q, S, d, chunk) if d in (64, 128) else 1 << 30
+    return gqa.lib().gqa_decode(q, kc, vc, sl, o, B, h_q, h_kv, S, d, dt, chunk, ws, ws_bytes,
+                                None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sl=None), NULLP), (dict(kc=None), NULLP),
+    (dict(vc=MIS), ALIGN), (dict(sl=A + 2), ALIGN),
+    (dict(S=0), SIZE), (dict(B=0), SIZE),
+    (dict(h_q=32, h_kv=5), HEADS), (dict(d=80), HEADDIM), (dict(dt=0), DTYPE),
+    (dict(chunk=100), SIZE), (dict(chunk=32), SIZE), (dict(chunk=16384), SIZE),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE), (dict(ws=A + 8), WORKSPACE),
+])
+def test_decode_rejects_bad_arguments(kw, status):
+    assert decode_status(**kw) == status
+
+
+def test_decode_without_a_gpu_reports_the_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert decode_status(sl=A + 4) == DEVICE  # int32 alignment is enough for seqlens
+
+
+@pytest.mark.parametrize("B,h_q,S,d,chunk", [(64, 32, 8192, 128, 0), (3, 8, 1000, 64, 64),
+                                             (1, 1, 1, 128, 8192), (2, 64, 5000, 128, 512)])
+def test_workspace_bytes(B, h_q, S, d, chunk):
+    ch = gqa.decode_default_chunk(S) if chunk == 0 else chunk
+    nc = -(-S // ch)
+    rows = B * h_q * nc
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert gqa.decode_workspace_bytes(B, h_q, S, d, chunk) == up(rows * d * 4) + up(rows * 4)
+
+
+def test_workspace_bytes_invalid():
+    assert gqa.decode_workspace_bytes(0, 32, 8192, 128, 0) == 0
+    assert gqa.decode_workspace_bytes(1, 32, 8192, 96, 0) == 0
+    assert gqa.decode_workspace_bytes(1, 32, 8192, 128, 65) == 0
+
+
+def test_default_chunk_is_valid():
+    for S in (1, 100, 8192, 65536):
+        ch = gqa.decode_default_chunk(S)
+        assert ch % 64 == 0 and 64 <= ch <= 8192

@@ -1,0 +1,269 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
+
+Both sides see the same seeded inputs from ``gqa_workloads``; the oracle gets
+the exact values the GPU received (bf16 upcast exactly to float64).
+
+Tolerances (whole compared tensor): fp32 max-abs <= 1e-4; bf16 max-abs <= 2e-2
+and relative L2 <= 1e-2.  Small shapes are compared in full (several tiles,
+ragged tails, every group size class); the five named workloads run at their
+full sizes in the launch configuration the benchmark times and are compared on
+seeded samples of rows (decode: on sampled sequences, all heads).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_workloads as wl
+import grouped_query_attention_03_amd as gqa
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-4
+BF16_MAXABS = 2e-2
+BF16_RELL2 = 1e-2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def check(out, ref, dtype, what):
+    o = np.asarray(out, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    assert o.shape == r.shape, f"{what}: shape {o.shape} vs {r.shape}"
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    err = np.abs(o - r)
+    maxabs = float(err.max()) if err.size else 0.0
+    rel = float(np.linalg.norm(o - r) / max(np.linalg.norm(r), 1e-300))
+    say(f"  {what}: max-abs {maxabs:.3e} rel-L2 {rel:.3e}")
+    if dtype == "f32":
+        assert maxabs <= F32_TOL, f"{what}: max-abs {maxabs:.3e} > {F32_TOL}"
+    else:
+        assert maxabs <= BF16_MAXABS, f"{what}: max-abs {maxabs:.3e} > {BF16_MAXABS}"
+        assert rel <= BF16_RELL2, f"{what}: rel-L2 {rel:.3e} > {BF16_RELL2}"
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def run_prefill(q, k, v, causal, scale, dev):
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.full_like(qd, float("nan"))  # every element must be overwritten
+    gqa.prefill(qd, kd, vd, causal=causal, scale=scale, out=out)
+    torch.cuda.synchronize()
+    return out
+
+
+# ------------------------------------------------------------------ prefill, full
+
+PREFILL_SMALL = [
+    # B, L, h_q, h_kv, d, dtype, causal
+    (1, 128, 8, 2, 64, "f32", True),       # the tiny fp32 workload's shape
+    (2, 77, 4, 4, 128, "f32", True),
+    (1, 300, 6, 2, 64, "f32", False),
+    (1, 1, 8, 1, 128, "f32", True),
+    (2, 300, 8, 2, 128, "bf16", True),     # G = 4, ragged tail
+    (1, 257, 8, 4, 64, "bf16", False),     # G = 2
+    (1, 1000, 16, 2, 128, "bf16", True),   # G = 8
+    (1, 129, 16, 1, 64, "bf16", True),     # G = 16 (MQA), two work-groups per group
+    (2, 17, 4, 4, 128, "bf16", False),     # MHA
+    (1, 1, 8, 2, 128, "bf16", True),       # L = 1
+    (1, 200, 6, 2, 128, "bf16", True),     # G = 3
+    (1, 150, 12, 2, 64, "bf16", False),    # G = 6
+    (3, 64, 8, 8, 64, "bf16", True),       # exactly one tile
+    (1, 513, 32, 8, 128, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_SMALL, ids=lambda c: "B{}_L{}_hq{}_hkv{}_d{}_{}_{}".format(
+    *c[:6], "causal" if c[6] else "full"))
+def test_prefill_matches_oracle(case, dev):
+    B, L, h_q, h_kv, d, dtype, causal = case
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    std = 1.0 if dtype == "f32" else 1 / math.sqrt(2)
+    seed = 1000 + 7 * L + h_q
+    q, k, v = wl.prefill_inputs(B, L, h_q, h_kv, d, seed, std, tdt)
+    scale = 1 / math.sqrt(d)
+    say(f"prefill {case} seed {seed}")
+    out = run_prefill(q, k, v, causal, scale, dev)
+    ref = oracle.prefill(f64(q), f64(k), f64(v), causal=causal, scale=scale)
+    check(f64(out), ref, dtype, f"prefill {case}")
+
+
+def test_prefill_non_default_scale(dev):
+    q, k, v = wl.prefill_inputs(1, 190, 8, 2, 128, 77, 1.0, torch.bfloat16)
+    say("prefill scale 0.05 B1 L190 8/2 d128")
+    out = run_prefill(q, k, v, True, 0.05, dev)
+    check(f64(out), oracle.prefill(f64(q), f64(k), f64(v), causal=True, scale=0.05), "bf16",
+          "prefill scale 0.05")
+
+
+def test_prefill_causal_row0_is_v0_exactly(dev):
+    B, L, h_q, h_kv, d = 2, 100, 8, 2, 128
+    q, k, v = wl.prefill_inputs(B, L, h_q, h_kv, d, 31, 1.0, torch.bfloat16)
+    say("prefill causal row 0")
+    out = run_prefill(q, k, v, True, 1 / math.sqrt(d), dev).cpu()
+    for h in range(h_q):
+        assert torch.equal(out[:, 0, h], v[:, 0, h // (h_q // h_kv)])
+
+
+def test_prefill_is_deterministic(dev):
+    q, k, v = wl.prefill_inputs(1, 700, 16, 4, 128, 32, 1.0, torch.bfloat16)
+    say("prefill determinism")
+    o1 = run_prefill(q, k, v, True, 0.088, dev)
+    o2 = run_prefill(q, k, v, True, 0.088, dev)
+    assert torch.equal(o1, o2)
+
+
+def test_prefill_head_map_discriminates(dev):
+    """Key/value head 0 has all-zero keys, so heads 0..G-1 must return running means of V0."""
+    B, L, h_q, h_kv, d = 1, 96, 8, 2, 64
+    q, k, v = wl.prefill_inputs(B, L, h_q, h_kv, d, 33, 1.0, torch.bfloat16)
+    k[:, :, 0] = 0
+    say("prefill head-map discriminator")
+    out = f64(run_prefill(q, k, v, True, 0.125, dev))
+    v0 = f64(v)[:, :, 0]
+    running_mean = np.cumsum(v0, axis=1) / np.arange(1, L + 1)[None, :, None]
+    for h in range(h_q // h_kv):
+        check(out[:, :, h], running_mean, "bf16", f"head {h} reads kv head 0")
+    check(out, oracle.prefill(f64(q), f64(k), f64(v), causal=True, scale=0.125), "bf16",
+          "head-map case vs oracle")
+
+
+# ---------------------------------------------------------- named workloads, full size
+
+def _sampled_prefill(name, n_rows, dev):
+    w = wl.WORKLOADS[name]
+    q, k, v = wl.workload_inputs(w)
+    say(f"prefill workload {name} ({w.description}) seed {w.seed}")
+    out = run_prefill(q, k, v, w.causal, w.scale, dev)
+    rows = wl.sample_rows(n_rows, w.B, w.L, w.h_q, w.seed,
+                          include=[(0, 0, 0), (w.B - 1, w.L - 1, w.h_q - 1), (0, w.L - 1, 0)])
+    idx = torch.tensor(rows)
+    q_rows = q[idx[:, 0], idx[:, 1], idx[:, 2]]
+    o_rows = out.cpu()[idx[:, 0], idx[:, 1], idx[:, 2]]
+    ref = oracle.prefill_rows(f64(q_rows), rows, f64(k), f64(v), w.h_q, causal=w.causal,
+                              scale=w.scale)
+    check(f64(o_rows), ref, w.dtype, f"{name}: {len(rows)} sampled rows")
+    assert not torch.isnan(out).any(), f"{name}: output not fully written"
+
+
+def test_workload_tiny_prefill_f32_full(dev):
+    w = wl.WORKLOADS["tiny_prefill_f32"]
+    q, k, v = wl.workload_inputs(w)
+    say(f"prefill workload {w.name}")
+    out = run_prefill(q, k, v, w.causal, w.scale, dev)
+    check(f64(out), oracle.prefill(f64(q), f64(k), f64(v), causal=w.causal, scale=w.scale),
+          "f32", w.name)
+
+
+def test_workload_worked_example_prefill(dev):
+    _sampled_prefill("worked_example_prefill_bf16", 512, dev)
+
+
+def test_workload_llama2_prefill(dev):
+    _sampled_prefill("llama2_7b_prefill_bf16", 384, dev)
+
+
+def test_workload_long_context_prefill(dev):
+    _sampled_prefill("long_context_prefill_bf16", 96, dev)
+
+
+# ------------------------------------------------------------------------- decode
+
+def run_decode(seqlens, q, kc, vc, dev, chunk=0, out_fill=float("nan")):
+    qd, kd, vd, sd = q.to(dev), kc.to(dev), vc.to(dev), seqlens.to(dev)
+    out = torch.full_like(qd, out_fill)
+    gqa.decode(qd, kd, vd, sd, out=out, chunk=chunk)
+    torch.cuda.synchronize()
+    return out
+
+
+def decode_ref(seqlens, q, kc, vc, bsel=None):
+    if bsel is None:
+        bsel = list(range(q.shape[0]))
+    bi = torch.tensor(bsel)
+    return oracle.decode(f64(q[bi, 0]), f64(kc[bi]), f64(vc[bi]), seqlens[bi].numpy())
+
+
+def test_workload_batched_decode(dev):
+    w = wl.WORKLOADS["batched_decode_bf16"]
+    seqlens, q, kc, vc = wl.workload_inputs(w)
+    say(f"decode workload {w.name} ({w.description}) total keys {int(seqlens.sum())}")
+    out = run_decode(seqlens, q, kc, vc, dev).cpu()
+    assert not torch.isnan(out).any()
+    order = torch.argsort(seqlens).tolist()
+    picks = torch.randperm(w.B, generator=torch.Generator().manual_seed(w.seed))[:6].tolist()
+    bsel = sorted({order[0], order[-1], *picks})  # shortest, longest and 6 seeded sequences
+    ref = decode_ref(seqlens, q, kc, vc, bsel)
+    check(f64(out[torch.tensor(bsel), 0]), ref, "bf16", f"{w.name}: sequences {bsel}")
+
+
+DECODE_SMALL = [
+    # B, h_q, h_kv, S, d, seqlens
+    (6, 32, 8, 1100, 128, [0, 1, 511, 512, 513, 1100]),
+    (3, 8, 8, 700, 64, [700, 64, 65]),        # G = 1
+    (2, 32, 1, 300, 128, [300, 17]),          # G = 32: two query-head subgroups
+    (2, 16, 2, 1000, 64, [999, 1000]),        # G = 8
+    (4, 12, 4, 96, 128, [96, 95, 33, 32]),    # G = 3
+]
+
+
+@pytest.mark.parametrize("case", DECODE_SMALL, ids=lambda c: "B{}_hq{}_hkv{}_S{}_d{}".format(*c[:5]))
+def test_decode_matches_oracle(case, dev):
+    B, h_q, h_kv, S, d, lens = case
+    seed = 2000 + S + h_q
+    _, q, kc, vc = wl.decode_inputs(B, h_q, h_kv, S, d, seed, (1, S))
+    seqlens = torch.tensor(lens, dtype=torch.int32)
+    # poison every cache row beyond its sequence length: it must never be read
+    for b, n in enumerate(lens):
+        kc[b, :, n:] = float("nan")
+        vc[b, :, n:] = float("nan")
+    say(f"decode {case} seed {seed}")
+    out = run_decode(seqlens, q, kc, vc, dev).cpu()
+    check(f64(out[:, 0]), decode_ref(seqlens, q, kc, vc), "bf16", f"decode {case}")
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert torch.equal(out[b], torch.zeros_like(out[b]))
+
+
+def test_decode_split_size_does_not_change_the_result(dev):
+    B, h_q, h_kv, S, d = 4, 32, 8, 3000, 128
+    seqlens, q, kc, vc = wl.decode_inputs(B, h_q, h_kv, S, d, 41, (1, S))
+    ref = decode_ref(seqlens, q, kc, vc)
+    outs = {}
+    for ch in (64, 128, 512, 1024, 8192):
+        say(f"decode split identity chunk {ch}")
+        outs[ch] = run_decode(seqlens, q, kc, vc, dev, chunk=ch).cpu()
+        check(f64(outs[ch][:, 0]), ref, "bf16", f"chunk {ch} vs oracle")
+    for ch in outs:
+        check(f64(outs[ch]), f64(outs[8192]), "bf16", f"chunk {ch} vs chunk 8192")
+
+
+def test_decode_is_deterministic(dev):
+    seqlens, q, kc, vc = wl.decode_inputs(8, 32, 8, 2048, 128, 42, (1, 2048))
+    say("decode determinism")
+    assert torch.equal(run_decode(seqlens, q, kc, vc, dev), run_decode(seqlens, q, kc, vc, dev))
+
+
+def test_decode_equals_last_row_of_causal_prefill(dev):
+    B, L, h_q, h_kv, d = 2, 777, 32, 8, 128
+    q, k, v = wl.prefill_inputs(B, L, h_q, h_kv, d, 43, 1.0, torch.bfloat16)
+    say("decode vs causal prefill last row")
+    po = run_prefill(q, k, v, True, 1 / math.sqrt(d), dev).cpu()
+    kc = k.transpose(1, 2).contiguous()
+    vc = v.transpose(1, 2).contiguous()
+    seqlens = torch.full((B,), L, dtype=torch.int32)
+    do = run_decode(seqlens, q[:, L - 1:L].contiguous(), kc, vc, dev).cpu()
+    check(f64(do), f64(po[:, L - 1:L]), "bf16", "decode vs prefill row L-1")
