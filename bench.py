@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of the grouped-query attention core on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--decode-workload NAME|none] [--no-cpu-baseline]
+
+Prints ONE JSON line on stdout.  A step is one call of the prefill entry point
+on the selected workload (default: the pages' worked example, B=32, L=1024,
+8 query heads over 4 key/value heads, d=64, bf16, non-causal).  K steps are
+timed back to back between two device synchronisations; ``value`` is the
+algorithmic TFLOP/s of that timed region (4 * B * h_q * d * visible (query,
+key) pairs per step; causal counts L(L+1)/2 pairs per head).
+
+The decode entry point is timed next on its own workload (64 sequences, 32
+query heads over 8 key/value heads, d=128, S=8192, lengths U{1024..8192}).  A
+512 MiB buffer is rewritten before every decode call, outside the timed events,
+so the 256 MiB last-level cache cannot serve the KV cache; its throughput is
+KV-cache bytes actually needed (sum of lengths * h_kv * d * 2 tensors * 2 B)
+per second of kernel time, reported under ``decode``.
+
+``roofline`` divides the algorithmic work of one launch by the launch's
+average duration measured with HIP events on the launch stream; ``traffic``
+comes from the rocprofv3 HBM counter summary under ``profiles/`` when that
+summary was taken on the current kernel source, else null.  ``cpu_baseline``
+times the fp64 CPU oracle on a bounded sample of the same workload.
+
+With ``--copy-calibration`` it instead runs a plain 1 GiB device copy (for
+scaling the HBM byte counters) and prints nothing else.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GQA prefill TFLOP/s (% MFMA peak); decode KV-cache GB/s (% HBM peak)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+FLUSH_BYTES = 512 << 20
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+CSRC = os.path.join(ROOT, "grouped_query_attention_03_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_flops(w) -> float:
+    pairs = w.L * (w.L + 1) // 2 if w.causal else w.L * w.L
+    return 4.0 * w.B * w.h_q * w.d * pairs
+
+
+def decode_kv_bytes(w, seqlens) -> float:
+    return float(int(seqlens.sum())) * w.h_kv * w.d * 2 * 2
+
+
+def source_digest(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "prefill": ["prefill_bf16.hip", "prefill_f32.hip", "gqa_device.h", "gqa_kernels.h"],
+    "decode": ["decode_bf16.hip", "gqa_device.h", "gqa_kernels.h"],
+}
+
+
+def recorded_traffic(kind: str, workload: str, launches_per_step: int = 1):
+    """HBM bytes per launch from the committed counter summary, if it matches the source.
+
+    The summary has one table row per (kernel kind, workload) with the source
+    digest it was taken on and scaled FETCH/WRITE bytes per launch.
+    """
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    digest = source_digest(KERNEL_SOURCES[kind])
+    for line in open(TRAFFIC_SUMMARY):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) < 5 or cells[0] != kind or cells[1] != workload:
+            continue
+        if cells[2] != digest:
+            return None
+        try:
+            return float(cells[3]) + float(cells[4])
+        except ValueError:
+            return None
+    return None
+
+
+def time_launches(fn, steps, before=None):
+    """Run fn() `steps` times; returns (wall seconds, per-launch event ms list)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if before is not None:
+            before()
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
+def bench_prefill(w, steps, warmup):
+    import torch
+    import gqa_workloads as wl
+    import grouped_query_attention_03_amd as gqa
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in wl.workload_inputs(w))
+    out = torch.empty_like(q)
+
+    def step():
+        gqa.prefill(q, k, v, causal=w.causal, scale=w.scale, out=out)
+
+    for _ in range(warmup):
+        step()
+    wall, ev = time_launches(step, steps)
+    flops = prefill_flops(w)
+    avg_ms = sum(ev) / len(ev)
+    return {
+        "value": flops * steps / wall / 1e12,
+        "ms_per_step": wall * 1e3 / steps,
+        "kernel_ms_avg": avg_ms,
+        "kernel_ms_min": min(ev),
+        "flops_per_launch": flops,
+    }
+
+
+def bench_decode(w, steps, warmup):
+    import torch
+    import gqa_workloads as wl
+    import grouped_query_attention_03_amd as gqa
+    dev = torch.device("cuda:0")
+    seqlens, q, kc, vc = wl.workload_inputs(w)
+    kv_bytes = decode_kv_bytes(w, seqlens)
+    seqlens, q, kc, vc = seqlens.to(dev), q.to(dev), kc.to(dev), vc.to(dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(gqa.decode_workspace_bytes(w.B, w.h_q, w.S, w.d), dtype=torch.uint8,
+                     device=dev)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
+    def step():
+        gqa.decode(q, kc, vc, seqlens, out=out, workspace=ws)
+
+    def evict():
+        flush.fill_(1)
+
+    for _ in range(warmup):
+        evict()
+        step()
+    wall, ev = time_launches(step, steps, before=evict)
+    avg_ms = sum(ev) / len(ev)
+    achieved = kv_bytes / (avg_ms * 1e-3) / 1e9
+    traffic = recorded_traffic("decode", w.name)
+    return {
+        "workload": w.name,
+        "description": w.description,
+        "value": achieved,
+        "unit": "GB/s",
+        "kernel_ms_avg": avg_ms,
+        "kernel_ms_min": min(ev),
+        "kv_bytes_per_call": kv_bytes,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernels": "decode split + log-sum-exp merge (one call, timed together)"},
+    }
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The fp64 oracle timed on about budget_s seconds of the workload's own rows.
+
+    Whole batch elements are run (all heads, all positions); when the whole
+    workload takes less than the budget it is run repeatedly and the mean rate
+    is reported.
+    """
+    import gqa_workloads as wl
+    import oracle
+    q, k, v = wl.workload_inputs(w)
+    qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
+
+    def run(nb):
+        t0 = time.perf_counter()
+        oracle.prefill(qd[:nb], kd[:nb], vd[:nb], causal=w.causal, scale=w.scale)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    nb = int(max(1, min(w.B, round(budget_s / max(t1, 1e-3)))))
+    reps, total = 0, 0.0
+    while total < budget_s or reps == 0:
+        total += run(nb) if (nb > 1 or reps > 0) else t1
+        reps += 1
+    per_b = prefill_flops(w) / w.B
+    return {"value": per_b * nb * reps / total / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle", "seconds": total,
+            "sample": f"{nb} of {w.B} batch elements of {w.name} (all {w.h_q} heads x {w.L} "
+                      f"positions each), run {reps} time(s), fp64"}
+
+
+def copy_calibration():
+    import torch
+    dev = torch.device("cuda:0")
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {n} bytes 3 times")
+
+
+def main(argv=None):
+    import gqa_workloads as wl
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="worked_example_prefill_bf16",
+                    choices=[n for n in wl.WORKLOAD_ORDER if wl.WORKLOADS[n].path == "prefill"])
+    ap.add_argument("--decode-workload", default="batched_decode_bf16",
+                    choices=["none"] + [n for n in wl.WORKLOAD_ORDER
+                                        if wl.WORKLOADS[n].path == "decode"])
+    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the GQA core is built and timed on a single "
+              "MI355X; run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    w = wl.WORKLOADS[args.workload]
+    log(f"prefill {w.name}: {w.description}; steps {args.steps} warmup {args.warmup}")
+    pf = bench_prefill(w, args.steps, args.warmup)
+    peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+    achieved = pf["flops_per_launch"] / (pf["kernel_ms_avg"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": pf["value"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pf["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded i.i.d. normal draws cast to the compute dtype (no dataset)",
+        "config": {"workload": w.name, "path": "prefill", "B": w.B, "L": w.L, "h_q": w.h_q,
+                   "h_kv": w.h_kv, "d": w.d, "causal": w.causal, "scale": w.scale,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": achieved,
+                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": recorded_traffic("prefill", w.name),
+                     "kernel_ms_avg": pf["kernel_ms_avg"], "kernel_ms_min": pf["kernel_ms_min"]},
+    }
+    log(f"prefill: {pf['value']:.1f} TFLOP/s wall, kernel avg {pf['kernel_ms_avg']:.4f} ms "
+        f"({achieved:.1f} TFLOP/s, {100 * achieved / peak:.1f}% of peak)")
+    if args.decode_workload != "none":
+        dw = wl.WORKLOADS[args.decode_workload]
+        log(f"decode {dw.name}: {dw.description}; steps {args.decode_steps}")
+        line["decode"] = bench_decode(dw, args.decode_steps, args.warmup)
+        log(f"decode: {line['decode']['value']:.1f} GB/s, kernel avg "
+            f"{line['decode']['kernel_ms_avg']:.4f} ms")
+    if not args.no_cpu_baseline:
+        log("cpu baseline: fp64 oracle on a bounded sample")
+        line["cpu_baseline"] = cpu_baseline(w)
+        log(f"cpu baseline: {line['cpu_baseline']}")
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
