@@ -13,8 +13,10 @@ key) pairs per step; causal counts L(L+1)/2 pairs per head).
 
 The decode entry point is timed next on its own workload (64 sequences, 32
 query heads over 8 key/value heads, d=128, S=8192, lengths U{1024..8192}).  A
-512 MiB buffer is rewritten before every decode call, outside the timed events,
-so the 256 MiB last-level cache cannot serve the KV cache; its throughput is
+512 MiB buffer is read before every decode call, outside the timed events, so
+the 256 MiB last-level cache holds none of the KV cache (a read, not a write:
+evicting with writes would leave dirty lines whose write-back lands inside the
+timed kernel); its throughput is
 KV-cache bytes actually needed (sum of lengths * h_kv * d * 2 tensors * 2 B)
 per second of kernel time, reported under ``decode``.
 
@@ -152,15 +154,17 @@ def bench_decode(w, steps, warmup):
     kv_bytes = decode_kv_bytes(w, seqlens)
     seqlens, q, kc, vc = seqlens.to(dev), q.to(dev), kc.to(dev), vc.to(dev)
     out = torch.empty_like(q)
-    ws = torch.empty(gqa.decode_workspace_bytes(w.B, w.h_q, w.S, w.d), dtype=torch.uint8,
+    ws = torch.empty(gqa.decode_workspace_bytes(w.B, w.h_q, w.h_kv, w.d), dtype=torch.uint8,
                      device=dev)
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
 
     def step():
         gqa.decode(q, kc, vc, seqlens, out=out, workspace=ws)
 
+    flush.fill_(1)
+
     def evict():
-        flush.fill_(1)
+        flush.sum(dtype=torch.int64)  # a read-only pass over 512 MiB
 
     for _ in range(warmup):
         evict()

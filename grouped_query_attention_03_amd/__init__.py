@@ -9,7 +9,7 @@ the device is not a gfx950 GPU, the calls raise.
         q [B, L, h_q, d], k/v [B, L, h_kv, d] (bf16 or fp32, contiguous, on the
         GPU) -> o [B, L, h_q, d].  Query head h reads key/value head
         h // (h_q // h_kv).
-    decode(q, k_cache, v_cache, seqlens, out=None, workspace=None, chunk=0)
+    decode(q, k_cache, v_cache, seqlens, out=None, workspace=None, num_splits=0)
         q [B, 1, h_q, d] bf16, caches [B, h_kv, S, d] bf16, seqlens [B] int32
         -> o [B, 1, h_q, d].
 """
@@ -54,8 +54,8 @@ def lib() -> ctypes.CDLL:
     L.gqa_decode.restype = I
     L.gqa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     L.gqa_decode_workspace_bytes.restype = ctypes.c_size_t
-    L.gqa_decode_default_chunk.argtypes = [I]
-    L.gqa_decode_default_chunk.restype = I
+    L.gqa_decode_default_splits.argtypes = []
+    L.gqa_decode_default_splits.restype = I
     L.gqa_status_string.argtypes = [I]
     L.gqa_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -114,15 +114,15 @@ def prefill(q, k, v, *, causal: bool, scale: float | None = None, out=None):
     return out
 
 
-def decode_workspace_bytes(B: int, h_q: int, S: int, d: int, chunk: int = 0) -> int:
-    return int(lib().gqa_decode_workspace_bytes(B, h_q, S, d, chunk))
+def decode_workspace_bytes(B: int, h_q: int, h_kv: int, d: int, num_splits: int = 0) -> int:
+    return int(lib().gqa_decode_workspace_bytes(B, h_q, h_kv, d, num_splits))
 
 
-def decode_default_chunk(S: int) -> int:
-    return int(lib().gqa_decode_default_chunk(S))
+def decode_default_splits() -> int:
+    return int(lib().gqa_decode_default_splits())
 
 
-def decode(q, k_cache, v_cache, seqlens, *, out=None, workspace=None, chunk: int = 0):
+def decode(q, k_cache, v_cache, seqlens, *, out=None, workspace=None, num_splits: int = 0):
     _check(q, "q", 4)
     _check(k_cache, "k_cache", 4)
     _check(v_cache, "v_cache", 4)
@@ -141,12 +141,12 @@ def decode(q, k_cache, v_cache, seqlens, *, out=None, workspace=None, chunk: int
         _check(out, "out", 4)
         if out.shape != q.shape or out.dtype != q.dtype:
             raise ValueError("out must match q in shape and dtype")
-    need = decode_workspace_bytes(B, h_q, S, d, chunk)
+    need = decode_workspace_bytes(B, h_q, h_kv, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     st = lib().gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                           seqlens.data_ptr(), out.data_ptr(), B, h_q, h_kv, S, d, _dtype_code(q),
-                          int(chunk), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          int(num_splits), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_decode")

@@ -3,21 +3,27 @@
 // One new query position per sequence attends to cache rows [0, seqlens[b]) of
 // k_cache/v_cache [B, h_kv, S, d] ("What is Grouped-Query Attention", §2.2 step 2
 // for the cache layout, §3.2 for attending over the appended cache).  The pass
-// is bound by reading the cache, so the design goal is to read every valid
-// cache byte exactly once per key/value head, never once per query head:
+// is bound by reading the cache, so every valid cache byte is read exactly once
+// per key/value head, never once per query head, and the reads are kept
+// streaming without bubbles:
 //
-// decode_split: one work-group per (sequence, key/value head, chunk of CH keys).
-//   The G query heads of the group are stacked as the N dimension of a
-//   v_mfma_f32_16x16x32_bf16 (S^T = K Q^T, keys on M), so one read of a cache
-//   row serves every query head of the group.  K rows go straight from HBM into
-//   MFMA A-operand registers with 16-byte loads; V rows go through a
-//   wave-private LDS buffer and come back transposed (ds_read_b64_tr_b16) as the
-//   A operand of O^T = V^T P^T.  The 4 waves take interleaved 32-key blocks of
-//   the chunk and prefetch the next block while computing the current one.
-//   Each chunk leaves, per query head, its normalised partial output and its
-//   log-sum-exp (base 2, in units of scale*log2(e)) in the workspace.
-// decode_merge: one wave per (sequence, query head) combines the chunks with
-//   weights 2^(lse_c - max lse), i.e. the exact log-sum-exp merge.
+// decode_split: a persistent, evenly balanced stream per wave.  The valid
+//   32-key blocks of all (sequence, key/value head) segments form one list of
+//   T blocks; wave w of NW takes the contiguous slice [w*T/NW, (w+1)*T/NW),
+//   which may span several segments.  The G query heads of the segment's group
+//   are stacked as the N dimension of v_mfma_f32_16x16x32_bf16 (S^T = K Q^T,
+//   keys on M), so one read of a cache row serves every query head of the
+//   group.  K rows go straight from HBM into MFMA A-operand registers with
+//   16-byte loads; V rows go through the wave's LDS buffer and come back
+//   transposed (ds_read_b64_tr_b16) as the A operand of O^T = V^T P^T.  The
+//   next block's loads are always in flight, also across segment boundaries.
+//   For every segment it touches, a wave writes the segment's partial output
+//   (normalised) and its log-sum-exp (base 2, in units of scale*log2(e)) to
+//   slot w + segment of the workspace: the (wave, segment) pairs form a
+//   monotone staircase, so those slots are distinct.
+// decode_merge: one wave per (sequence, query head) finds the waves whose
+//   slices cover its segment and combines their partials with weights
+//   2^(lse - max lse): the exact log-sum-exp merge.
 // Rows at or beyond seqlens[b] are never loaded.
 #include "gqa_device.h"
 #include "gqa_kernels.h"
@@ -32,194 +38,260 @@ constexpr float DC_TAU = 8.0f;     // lazy-rescale threshold, log2 units
 
 template <int D>
 struct DcLayout {
-    static constexpr int VS = D + 16;                  // V row stride in LDS, elements
-    static constexpr int V_ELEMS = DC_BK * VS;         // one wave's V block
     static constexpr int KSTEPS = D / 32;              // 16x16x32 k-steps over d
-    static constexpr int KLOADS = 2 * KSTEPS;          // 16-byte K loads per lane per block
-    static constexpr int VLOADS = DC_BK * D / 8 / 64;  // 16-byte V loads per lane per block
-    static constexpr int OS = D + 1;                   // combine buffer row stride, floats
-    static constexpr int V_BYTES = DC_WAVES * V_ELEMS * 2;
-    static constexpr int C_BYTES = DC_WAVES * (16 * OS + 32) * 4;
-    static constexpr int BYTES = V_BYTES > C_BYTES ? V_BYTES : C_BYTES;
+    static constexpr int ROW_BYTES = 2 * D;            // one cache row
+    static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+    static constexpr int ROWS_PER_DMA = 64 / CPR;      // rows one 64-lane 16-byte load covers
+    static constexpr int KV_DMA = DC_BK / ROWS_PER_DMA;  // loads per K (and per V) block
+    static constexpr int TILE = DC_BK * ROW_BYTES;     // one K or V block in LDS
+    static constexpr int ROWS_PER_SWEEP = 256 / ROW_BYTES;  // rows per pass over the 64 banks
 };
 
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// Tiles sit in LDS unpadded (each direct load writes 64 consecutive 16-byte
+// chunks); chunk c of row r is stored at chunk position c ^ swz(r).
+//   kswz: 16 lanes reading one 16-byte chunk of 16 consecutive rows (the
+//         MFMA A/B operand reads of K and Q) hit 16 distinct 4-bank groups.
+//   vswz: the 8 rows x 32 bytes of one half-wave transposing read of V hit
+//         64 distinct banks.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+    using Lay = DcLayout<D>;
+    return (r / Lay::ROWS_PER_SWEEP) % Lay::CPR;
+}
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+    using Lay = DcLayout<D>;
+    return 2 * ((r / Lay::ROWS_PER_SWEEP) % (Lay::CPR / 2));
 }
 
-template <int D>
-__device__ __forceinline__ void dc_load_block(const __bf16 *__restrict__ kb,
-                                              const __bf16 *__restrict__ vb, int key0, int kend,
-                                              u32x4 (&kr)[DcLayout<D>::KLOADS],
-                                              u32x4 (&vr)[DcLayout<D>::VLOADS]) {
+// Direct loads of `n_dma` x 1 KiB into `dst`: load i, lane l fetches row
+// i * ROWS_PER_DMA + l / CPR (clamped to last_row), logical chunk
+// (l % CPR) ^ swz(row), and the hardware stores it at byte 1024 i + 16 l.
+template <int D, bool VSW>
+__device__ __forceinline__ void dc_dma_rows(const __bf16 *__restrict__ src, size_t row_stride,
+                                            int row0, int last_row, int n_dma, GQA_LDS char *dst) {
     using Lay = DcLayout<D>;
     const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int key = key0 + 16 * mb + (lane & 15);
-        const bool ok = key < kend;
-#pragma unroll
-        for (int ks = 0; ks < Lay::KSTEPS; ++ks)
-            kr[mb * Lay::KSTEPS + ks] =
-                ok ? load16(kb + (size_t)key * D + 32 * ks + 8 * (lane >> 4)) : u32x4{0u, 0u, 0u, 0u};
-    }
-    constexpr int CPR = D / 8;
-#pragma unroll
-    for (int i = 0; i < Lay::VLOADS; ++i) {
-        const int cidx = lane + 64 * i;
-        const int row = cidx / CPR, col = cidx % CPR;
-        const int key = key0 + row;
-        vr[i] = key < kend ? load16(vb + (size_t)key * D + 8 * col) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < n_dma; ++i) {
+        const int row = i * Lay::ROWS_PER_DMA + lane / Lay::CPR;
+        const int chunk = (lane % Lay::CPR) ^ (VSW ? vswz<D>(row) : kswz<D>(row));
+        const int srow = min(row0 + row, last_row);
+        dma16_to_lds(src + (size_t)srow * row_stride + 8 * chunk, dst + i * 1024);
     }
 }
 
+// 16-byte read of logical chunk c of row r from a kswz-swizzled tile.
 template <int D>
-__global__ __launch_bounds__(DC_THREADS) void decode_split_kernel(DecodeArgs a) {
+__device__ __forceinline__ bf16x8 dc_read_row_chunk(const GQA_LDS char *tile, int r, int c) {
+    using Lay = DcLayout<D>;
+    return *reinterpret_cast<const GQA_LDS bf16x8 *>(tile + r * Lay::ROW_BYTES +
+                                                     16 * (c ^ kswz<D>(r)));
+}
+
+// One 32-key block: S^T = K Q^T, online-softmax update, O^T += V^T P^T, with
+// Q, K and V read from this slot's LDS tiles.
+template <int D, int QROWS>
+__device__ __forceinline__ void dc_block(const GQA_LDS char *qt, const GQA_LDS char *kt,
+                                         const GQA_LDS char *vt, int key0, int kend, bool qvalid,
+                                         float c, float &m_run, float &l_run,
+                                         f32x4 (&acc)[D / 16]) {
+    using Lay = DcLayout<D>;
+    constexpr int DB = D / 16;
+    const int lane = threadIdx.x & 63, g = lane >> 4, jl = lane & 15;
+    f32x4 s[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int ks = 0; ks < Lay::KSTEPS; ++ks) {
+        // A = K rows (key jl of the m-block), B = Q^T (query column jl); d-chunk 4 ks + g.
+        // Columns beyond the tile's QROWS heads read its last row and are zeroed.
+        bf16x8 qf = dc_read_row_chunk<D>(qt, jl < QROWS ? jl : QROWS - 1, 4 * ks + g);
+        qf = qvalid ? qf : bf16x8{};
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+            s[mb] = mfma16x16x32(dc_read_row_chunk<D>(kt, 16 * mb + jl, 4 * ks + g), qf, s[mb]);
+    }
+    if (key0 + DC_BK > kend) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (key0 + 16 * mb + 4 * g + r >= kend) s[mb][r] = -INFINITY;
+    }
+    // block max over the 32 keys of this query column (4 lanes share a column)
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, other_half(mx));
+    const float mnew = mx * c;
+    if (__any(mnew > m_run + DC_TAU)) {
+        const float m2 = fmaxf(m_run, mnew);
+        const float alpha = (m2 == -INFINITY) ? 1.f : fast_exp2(m_run - m2);
+        m_run = m2;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    }
+    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+    bf16x8 pb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float p = fast_exp2(fmaf(s[i >> 2][i & 3], c, -mu));
+        l_run += p;
+        pb[i] = (__bf16)p;
+    }
+    // V^T operand: transposing reads of rows 4g + jl/4 (and 16 rows further down)
+    const int r0 = 4 * g + (jl >> 2);
+    const int sw = vswz<D>(r0);  // also the swizzle of row r0 + 16
+    const GQA_LDS char *rp = vt + r0 * Lay::ROW_BYTES + 8 * (jl & 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const int chunk = (2 * db + ((jl & 3) >> 1)) ^ sw;
+        const GQA_LDS char *p0 = rp + 16 * chunk;
+        short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GQA_LDS short4v *)p0);
+        short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GQA_LDS short4v *)(p0 + 16 * Lay::ROW_BYTES));
+        acc[db] = mfma16x16x32(join_tr(lo, hi), pb, acc[db]);
+    }
+}
+
+// Segment bookkeeping shared by the split and merge passes.  Segments are
+// ordered (sequence b, key/value head, query-head subgroup); segment
+// (b, kv, qs) has nblk(b) = ceil(seqlens[b] / 32) blocks.
+__device__ __forceinline__ int dc_nblk(const int32_t *seqlens, int b) {
+    return (load_const(seqlens, b) + DC_BK - 1) / DC_BK;
+}
+
+__device__ __forceinline__ long long dc_slice_start(int w, long long T, int NW) {
+    return (long long)w * T / NW;
+}
+
+// QD = 1 KiB loads per block for the query tile (ceil(query heads x 2d / 1024)).
+template <int D, int QD>
+__global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs a) {
     using Lay = DcLayout<D>;
     constexpr int DB = D / 16;  // 16-wide blocks of the head dimension
-    __shared__ __attribute__((aligned(16))) char smem[Lay::BYTES];
+    constexpr int OPS = QD + 2 * Lay::KV_DMA;  // memory instructions issued per block
+    // two slots per wave, each with its own Q, K and V tiles (separate arrays,
+    // so loads into one slot are visibly independent of reads from the other)
+    __shared__ __attribute__((aligned(1024))) char qA_s[DC_WAVES][QD * 1024];
+    __shared__ __attribute__((aligned(1024))) char kA_s[DC_WAVES][Lay::TILE];
+    __shared__ __attribute__((aligned(1024))) char vA_s[DC_WAVES][Lay::TILE];
+    __shared__ __attribute__((aligned(1024))) char qB_s[DC_WAVES][QD * 1024];
+    __shared__ __attribute__((aligned(1024))) char kB_s[DC_WAVES][Lay::TILE];
+    __shared__ __attribute__((aligned(1024))) char vB_s[DC_WAVES][Lay::TILE];
 
-    const int chunk = blockIdx.x;
-    const int kvh = blockIdx.y / a.n_qsub, qs = blockIdx.y % a.n_qsub;
-    const int b = blockIdx.z;
-    const int seqlen = a.seqlens[b];
-    const int c0 = chunk * a.CH;
-    if (c0 >= seqlen) return;  // whole work-group exits together
-    const int kend = min(seqlen, c0 + a.CH);
-    const int nblocks = (kend - c0 + DC_BK - 1) / DC_BK;
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    const int w = blockIdx.x * DC_WAVES + wave;
+    if (w >= a.NW) return;
+    const int g = lane >> 4, qcol = lane & 15;
+    const int segs_per_b = a.h_kv * a.n_qsub;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, jl = lane & 15;
-    const int heads_here = min(16, a.G - 16 * qs);
-    const int qcol = lane & 15;  // query head (within the subgroup) of this lane's column
-    const int head_base = kvh * a.G + 16 * qs;
+    // total blocks and this wave's slice
+    long long T = 0;
+    for (int b = 0; b < a.B; ++b) T += (long long)dc_nblk(a.seqlens, b) * segs_per_b;
+    const long long pos = dc_slice_start(w, T, a.NW);
+    const long long end = dc_slice_start(w + 1, T, a.NW);
+    if (pos >= end) return;
 
-    // Q^T operand: lane holds 8 head-dim values of query column qcol.
-    bf16x8 qf[Lay::KSTEPS];
-    if (qcol < heads_here) {
-        const __bf16 *qp = static_cast<const __bf16 *>(a.q) +
-                           ((size_t)b * a.h_q + head_base + qcol) * D + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < Lay::KSTEPS; ++ks)
-            qf[ks] = __builtin_bit_cast(bf16x8, load16(qp + 32 * ks));
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < Lay::KSTEPS; ++ks) qf[ks] = bf16x8{};
+    struct Cur {
+        int b, seg, blk;
+    };
+    Cur cur{0, 0, 0};
+    {
+        long long cum = 0;
+        for (int b = 0; b < a.B; ++b) {
+            const long long nb = dc_nblk(a.seqlens, b);
+            if (pos < cum + nb * segs_per_b) {
+                cur = Cur{b, (int)((pos - cum) / nb), (int)((pos - cum) % nb)};
+                break;
+            }
+            cum += nb * segs_per_b;
+        }
     }
+    const float c = a.c;
 
-    const size_t slab = ((size_t)b * a.h_kv + kvh) * (size_t)a.S * D;
-    const __bf16 *kb = static_cast<const __bf16 *>(a.k_cache) + slab;
-    const __bf16 *vb = static_cast<const __bf16 *>(a.v_cache) + slab;
-    __bf16 *vw = reinterpret_cast<__bf16 *>(smem) + wave * Lay::V_ELEMS;
+    auto advance = [&](Cur &u) {
+        if (++u.blk == dc_nblk(a.seqlens, u.b)) {
+            u.blk = 0;
+            if (++u.seg == segs_per_b) {
+                u.seg = 0;
+                do {
+                    ++u.b;
+                } while (u.b < a.B && dc_nblk(a.seqlens, u.b) == 0);
+            }
+        }
+    };
+    auto heads_in = [&](const Cur &u) { return min(16, a.G - 16 * (u.seg % a.n_qsub)); };
+    // every issue is OPS direct loads: Q rows (query heads of the subgroup,
+    // clamped to its last head), K rows, V rows (clamped to the last valid key)
+    auto issue = [&](const Cur &u, GQA_LDS char *qt, GQA_LDS char *kt, GQA_LDS char *vt) {
+        const int kvh = u.seg / a.n_qsub, qs = u.seg % a.n_qsub;
+        const size_t slab = ((size_t)u.b * a.h_kv + kvh) * (size_t)a.S * D;
+        const int kend = load_const(a.seqlens, u.b);
+        const int head0 = kvh * a.G + 16 * qs;
+        dc_dma_rows<D, false>(static_cast<const __bf16 *>(a.q) + ((size_t)u.b * a.h_q + head0) * D, D, 0,
+                              heads_in(u) - 1, QD, qt);
+        dc_dma_rows<D, false>(static_cast<const __bf16 *>(a.k_cache) + slab, D, DC_BK * u.blk, kend - 1,
+                              Lay::KV_DMA, kt);
+        dc_dma_rows<D, true>(static_cast<const __bf16 *>(a.v_cache) + slab, D, DC_BK * u.blk, kend - 1,
+                             Lay::KV_DMA, vt);
+    };
 
+    long long left = end - pos;  // blocks left to compute
+    long long issued = 0;        // blocks whose loads have been issued
+    Cur nxt = cur;
+    bool seg_open = false;
     f32x4 acc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x4{};
     float m_run = -INFINITY, l_run = 0.f;
-    const float c = a.c;
 
-    u32x4 kr[Lay::KLOADS], vr[Lay::VLOADS];
-    int blk = wave;
-    if (blk < nblocks) dc_load_block<D>(kb, vb, c0 + DC_BK * blk, kend, kr, vr);
+    auto close_segment = [&](const Cur &u) {
+        float l_tot = l_run + __shfl_xor(l_run, 16);
+        l_tot += other_half(l_tot);
+        const size_t slot = (size_t)w + (size_t)u.b * segs_per_b + u.seg;
+        if (qcol < heads_in(u)) {
+            const float inv = 1.f / l_tot;
+            float *op = a.opart + (slot * 16 + qcol) * D + 4 * g;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                *reinterpret_cast<float4 *>(op + 16 * db) =
+                    make_float4(acc[db][0] * inv, acc[db][1] * inv, acc[db][2] * inv, acc[db][3] * inv);
+            if (g == 0) a.lse[slot * 16 + qcol] = m_run + __log2f(l_tot);
+        }
+        seg_open = false;
+    };
+    auto step = [&](const GQA_LDS char *qt, const GQA_LDS char *kt, const GQA_LDS char *vt) {
+        if (!seg_open) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[db] = f32x4{};
+            m_run = -INFINITY;
+            l_run = 0.f;
+            seg_open = true;
+        }
+        // this slot's loads are complete once at most the OPS loads of the other
+        // slot (issued after them) are still in flight; stores issued in between
+        // only make the wait stricter
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(OPS) : "memory");
+        dc_block<D, QD * Lay::ROWS_PER_DMA>(qt, kt, vt, DC_BK * cur.blk, load_const(a.seqlens, cur.b),
+                    qcol < heads_in(cur), c, m_run, l_run, acc);
+        --left;
+        if (cur.blk + 1 == dc_nblk(a.seqlens, cur.b) || left == 0) close_segment(cur);
+        advance(cur);
+    };
+    // the load cursor stops at the slice's last block; later issues repeat it
+    auto next_issue = [&](GQA_LDS char *qt, GQA_LDS char *kt, GQA_LDS char *vt) {
+        if (issued > 0 && issued < end - pos) advance(nxt);
+        ++issued;
+        issue(nxt, qt, kt, vt);
+    };
 
-    for (; blk < nblocks; blk += DC_WAVES) {
-        const int key0 = c0 + DC_BK * blk;
-        // stage this block's V rows in the wave's LDS buffer
-        constexpr int CPR = D / 8;
-#pragma unroll
-        for (int i = 0; i < Lay::VLOADS; ++i) {
-            const int cidx = lane + 64 * i;
-            store16_lds(vw + (cidx / CPR) * Lay::VS + 8 * (cidx % CPR), vr[i]);
-        }
-        u32x4 kcur[Lay::KLOADS];
-#pragma unroll
-        for (int i = 0; i < Lay::KLOADS; ++i) kcur[i] = kr[i];
-        // prefetch the wave's next block
-        if (blk + DC_WAVES < nblocks) dc_load_block<D>(kb, vb, key0 + DC_BK * DC_WAVES, kend, kr, vr);
-
-        // S^T = K Q^T: two 16-key m-blocks
-        f32x4 s[2] = {f32x4{}, f32x4{}};
-#pragma unroll
-        for (int ks = 0; ks < Lay::KSTEPS; ++ks)
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-                s[mb] = mfma16x16x32(__builtin_bit_cast(bf16x8, kcur[mb * Lay::KSTEPS + ks]), qf[ks], s[mb]);
-        if (key0 + DC_BK > kend) {
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (key0 + 16 * mb + 4 * g + r >= kend) s[mb][r] = -INFINITY;
-        }
-        // block max over the 32 keys of this query column (4 lanes share a column)
-        float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, other_half(mx));
-        const float mnew = mx * c;
-        if (__any(mnew > m_run + DC_TAU)) {
-            const float m2 = fmaxf(m_run, mnew);
-            const float alpha = (m2 == -INFINITY) ? 1.f : fast_exp2(m_run - m2);
-            m_run = m2;
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-        }
-        const float mu = (m_run == -INFINITY) ? 0.f : m_run;
-        bf16x8 pb;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float p = fast_exp2(fmaf(s[i >> 2][i & 3], c, -mu));
-            l_run += p;
-            pb[i] = (__bf16)p;
-        }
-        wave_sync();  // the V block written above is visible to the whole wave
-        const __bf16 *vp = vw + (4 * g + (jl >> 2)) * Lay::VS + 4 * (jl & 3);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            short4v lo = lds_read_tr16(vp + 16 * db);
-            short4v hi = lds_read_tr16(vp + 16 * Lay::VS + 16 * db);
-            acc[db] = mfma16x16x32(join_tr(lo, hi), pb, acc[db]);
-        }
-        wave_sync();  // reads of this block finish before the next block is staged
-    }
-
-    // ---- combine the 4 waves of the work-group
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += other_half(l_tot);
-    __syncthreads();  // V buffers are reused below
-    float *cO = reinterpret_cast<float *>(smem);                // [wave][16][OS]
-    float *cm = cO + DC_WAVES * 16 * Lay::OS;                   // [wave][16]
-    float *cl = cm + DC_WAVES * 16;                             // [wave][16]
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) cO[(wave * 16 + qcol) * Lay::OS + 16 * db + 4 * g + r] = acc[db][r];
-    if (g == 0) {
-        cm[wave * 16 + qcol] = m_run;
-        cl[wave * 16 + qcol] = l_tot;
-    }
-    __syncthreads();
-    float *opart = a.opart;
-    float *lse = a.lse;
-    for (int idx = tid; idx < heads_here * D; idx += DC_THREADS) {
-        const int q = idx / D, dd = idx % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < DC_WAVES; ++w) M = fmaxf(M, cm[w * 16 + q]);
-        float wsum = 0.f, o = 0.f;
-#pragma unroll
-        for (int w = 0; w < DC_WAVES; ++w) {
-            const float mw = cm[w * 16 + q];
-            const float f = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-            wsum += f * cl[w * 16 + q];
-            o += f * cO[(w * 16 + q) * Lay::OS + dd];
-        }
-        const size_t row = ((size_t)b * a.h_q + head_base + q) * a.NC + chunk;
-        opart[row * D + dd] = o / wsum;
-        if (dd == 0) lse[row] = M + __log2f(wsum);
+    GQA_LDS char *qA = (GQA_LDS char *)qA_s[wave], *kA = (GQA_LDS char *)kA_s[wave], *vA = (GQA_LDS char *)vA_s[wave];
+    GQA_LDS char *qB = (GQA_LDS char *)qB_s[wave], *kB = (GQA_LDS char *)kB_s[wave], *vB = (GQA_LDS char *)vB_s[wave];
+    next_issue(qA, kA, vA);
+    while (left > 0) {
+        next_issue(qB, kB, vB);
+        step(qA, kA, vA);
+        next_issue(qA, kA, vA);
+        if (left > 0) step(qB, kB, vB);
     }
 }
 
@@ -229,28 +301,49 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     const int lane = threadIdx.x & 63;
     const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (wid >= a.B * a.h_q) return;
-    const int b = wid / a.h_q;
-    const int seqlen = a.seqlens[b];
-    const int n = (seqlen + a.CH - 1) / a.CH;
+    const int b = wid / a.h_q, h = wid % a.h_q;
+    const int kvh = h / a.G, hg = h % a.G, qs = hg / 16, qcol = hg % 16;
+    const int segs_per_b = a.h_kv * a.n_qsub;
     __bf16 *op = static_cast<__bf16 *>(a.o) + (size_t)wid * D + PER * lane;
-    if (n <= 0) {
+    const int nb = dc_nblk(a.seqlens, b);
+    if (nb == 0) {
 #pragma unroll
         for (int e = 0; e < PER; ++e) op[e] = (__bf16)0.f;
         return;
     }
-    const float *lp = a.lse + (size_t)wid * a.NC;
-    const float *pp = a.opart + (size_t)wid * a.NC * D + PER * lane;
+    long long T = 0, P = 0;
+    for (int bb = 0; bb < a.B; ++bb) {
+        const long long n = (long long)dc_nblk(a.seqlens, bb) * segs_per_b;
+        if (bb < b) P += n;
+        T += n;
+    }
+    const int seg_in_b = kvh * a.n_qsub + qs;
+    P += (long long)seg_in_b * nb;  // first block of this segment
+    const long long seg_global = (long long)b * segs_per_b + seg_in_b;
+    // waves whose slices intersect [P, P + nb)
+    int w0 = (int)min((long long)a.NW - 1, P * a.NW / T);
+    while (w0 > 0 && dc_slice_start(w0, T, a.NW) > P) --w0;
+    while (dc_slice_start(w0 + 1, T, a.NW) <= P) ++w0;
+    // lane j handles wave w0 + j (and + 64, ...)
     float M = -INFINITY;
-    for (int cidx = 0; cidx < n; ++cidx) M = fmaxf(M, lp[cidx]);
+    for (int w = w0 + lane; w < a.NW && dc_slice_start(w, T, a.NW) < P + nb; w += 64) {
+        if (dc_slice_start(w + 1, T, a.NW) > dc_slice_start(w, T, a.NW))
+            M = fmaxf(M, a.lse[((size_t)w + seg_global) * 16 + qcol]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
     float wsum = 0.f;
-    for (int cidx = 0; cidx < n; ++cidx) {
-        const float w = fast_exp2(lp[cidx] - M);
-        wsum += w;
+    for (int w = w0; w < a.NW && dc_slice_start(w, T, a.NW) < P + nb; ++w) {
+        if (dc_slice_start(w + 1, T, a.NW) <= dc_slice_start(w, T, a.NW)) continue;  // empty slice
+        const size_t slot = (size_t)w + seg_global;
+        const float f = fast_exp2(a.lse[slot * 16 + qcol] - M);
+        wsum += f;
+        const float *pp = a.opart + (slot * 16 + qcol) * D + PER * lane;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, pp[(size_t)cidx * D + e], acc[e]);
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(f, pp[e], acc[e]);
     }
     const float inv = 1.f / wsum;
 #pragma unroll
@@ -259,14 +352,24 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 
 }  // namespace
 
+template <int D, int QD>
+void launch_split(const DecodeArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_split_kernel<D, QD>), dim3((a.NW + DC_WAVES - 1) / DC_WAVES),
+                       dim3(DC_THREADS), 0, stream, a);
+}
+
 int launch_decode_bf16(const DecodeArgs &a, int d, hipStream_t stream) {
-    dim3 grid1(a.NC, a.h_kv * a.n_qsub, a.B), block(DC_THREADS);
-    dim3 grid2((a.B * a.h_q + 3) / 4);
+    const int qh = a.G < 16 ? a.G : 16;  // query heads per subgroup
+    const int qkib = (qh * 2 * d + 1023) / 1024;
+    dim3 grid2((a.B * a.h_q + 3) / 4), block(DC_THREADS);
     if (d == 128) {
-        hipLaunchKernelGGL(decode_split_kernel<128>, grid1, block, 0, stream, a);
+        if (qkib <= 1) launch_split<128, 1>(a, stream);
+        else if (qkib <= 2) launch_split<128, 2>(a, stream);
+        else launch_split<128, 4>(a, stream);
         hipLaunchKernelGGL(decode_merge_kernel<128>, grid2, block, 0, stream, a);
     } else {
-        hipLaunchKernelGGL(decode_split_kernel<64>, grid1, block, 0, stream, a);
+        if (qkib <= 1) launch_split<64, 1>(a, stream);
+        else launch_split<64, 2>(a, stream);
         hipLaunchKernelGGL(decode_merge_kernel<64>, grid2, block, 0, stream, a);
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;

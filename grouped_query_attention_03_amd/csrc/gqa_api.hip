@@ -40,9 +40,10 @@ int heads_per_workgroup(int G) {
     return gw;
 }
 
-int decode_chunk(int chunk, int S) { return chunk == 0 ? gqa_decode_default_chunk(S) : chunk; }
+constexpr int kDefaultSplits = 1024;  // 256 CUs x 4 resident waves of the split pass
+constexpr int kMaxSplits = 1 << 20;
 
-bool chunk_valid(int chunk) { return chunk == 0 || (chunk >= 64 && chunk <= 8192 && chunk % 64 == 0); }
+bool splits_valid(int n) { return n >= 0 && n <= kMaxSplits; }
 
 }  // namespace
 
@@ -53,7 +54,7 @@ const char *gqa_status_string(gqa_status s) {
         case GQA_OK: return "ok";
         case GQA_ERR_NULL_POINTER: return "a required pointer is NULL";
         case GQA_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";
-        case GQA_ERR_SIZE: return "a size, scale or chunk argument is out of range";
+        case GQA_ERR_SIZE: return "a size, scale or split-count argument is out of range";
         case GQA_ERR_HEADS: return "h_q is not a multiple of h_kv";
         case GQA_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
         case GQA_ERR_DTYPE: return "dtype not supported by this entry point";
@@ -103,22 +104,21 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *o, int
     return rc == 0 ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
-int gqa_decode_default_chunk(int S) {
-    (void)S;
-    return 512;
-}
+int gqa_decode_default_splits(void) { return kDefaultSplits; }
 
-size_t gqa_decode_workspace_bytes(int B, int h_q, int S, int d, int chunk) {
-    if (B <= 0 || h_q <= 0 || S <= 0 || (d != 64 && d != 128) || !chunk_valid(chunk)) return 0;
-    const int ch = decode_chunk(chunk, S);
-    const size_t nc = (size_t)((S + ch - 1) / ch);
-    const size_t rows = (size_t)B * h_q * nc;
-    return round_up_256(rows * d * sizeof(float)) + round_up_256(rows * sizeof(float));
+size_t gqa_decode_workspace_bytes(int B, int h_q, int h_kv, int d, int num_splits) {
+    if (B <= 0 || h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0 || (d != 64 && d != 128) ||
+        !splits_valid(num_splits))
+        return 0;
+    const int nw = num_splits == 0 ? kDefaultSplits : num_splits;
+    const int n_qsub = (h_q / h_kv + 15) / 16;
+    const size_t slots = (size_t)nw + (size_t)B * h_kv * n_qsub;
+    return round_up_256(slots * 16 * d * sizeof(float)) + round_up_256(slots * 16 * sizeof(float));
 }
 
 gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *seqlens, void *o, int B, int h_q, int h_kv, int S, int d,
-                      gqa_dtype dt, int chunk, void *workspace, size_t workspace_bytes,
+                      gqa_dtype dt, int num_splits, void *workspace, size_t workspace_bytes,
                       void *hip_stream) {
     if (!q || !k_cache || !v_cache || !seqlens || !o) return GQA_ERR_NULL_POINTER;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
@@ -128,10 +128,9 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
     if (h_q % h_kv != 0) return GQA_ERR_HEADS;
     if (d != 64 && d != 128) return GQA_ERR_HEAD_DIM;
     if (dt != GQA_BF16) return GQA_ERR_DTYPE;
-    if (!chunk_valid(chunk)) return GQA_ERR_SIZE;
-    if (B > 65535) return GQA_ERR_SIZE;  // grid z
-    const int ch = decode_chunk(chunk, S);
-    const size_t need = gqa_decode_workspace_bytes(B, h_q, S, d, chunk);
+    if (!splits_valid(num_splits)) return GQA_ERR_SIZE;
+    if ((int64_t)B * h_q > 0x7fffffff / 4) return GQA_ERR_SIZE;
+    const size_t need = gqa_decode_workspace_bytes(B, h_q, h_kv, d, num_splits);
     if (!workspace || !aligned16(workspace) || workspace_bytes < need) return GQA_ERR_WORKSPACE;
 
     gqa::DecodeArgs a;
@@ -145,14 +144,12 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
     a.h_kv = h_kv;
     a.G = h_q / h_kv;
     a.S = S;
-    a.CH = ch;
-    a.NC = (S + ch - 1) / ch;
+    a.NW = num_splits == 0 ? kDefaultSplits : num_splits;
     a.n_qsub = (a.G + 15) / 16;
-    if ((int64_t)h_kv * a.n_qsub > 65535) return GQA_ERR_SIZE;  // grid y
-    const size_t rows = (size_t)B * h_q * a.NC;
+    const size_t slots = (size_t)a.NW + (size_t)B * h_kv * a.n_qsub;
     a.opart = static_cast<float *>(workspace);
     a.lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                      round_up_256(rows * d * sizeof(float)));
+                                      round_up_256(slots * 16 * d * sizeof(float)));
     a.c = (float)(1.4426950408889634 / sqrt((double)d));
 
     gqa_status st = check_device();

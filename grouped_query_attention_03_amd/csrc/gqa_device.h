@@ -58,6 +58,16 @@ __device__ __forceinline__ float other_half(float x) {
     return __uint_as_float(threadIdx.x % 64 < 32 ? p[1] : p[0]);
 }
 
+// Read a kernel-lifetime read-only int32 array through the constant address
+// space, so that a wave-uniform index becomes a scalar (s_load) read.
+__device__ __forceinline__ int load_const(const int32_t *p, int i) {
+    return reinterpret_cast<const __attribute__((address_space(4))) int32_t *>(
+        reinterpret_cast<uintptr_t>(p))[i];
+}
+
+// Index of this wave in its work-group, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Work-group ids are handed to the 8 XCDs round-robin (id % 8).  Renumber them
@@ -69,6 +79,23 @@ __device__ __forceinline__ int xcd_contiguous_id(int id, int total) {
     int per = total / nx, rem = total % nx;
     int x = id % nx, slot = id / nx;
     return x * per + (x < rem ? x : rem) + slot;
+}
+
+// 16-byte direct load from global memory into LDS (global_load_lds_dwordx4):
+// lane l's 16 bytes land at LDS byte address lds_base + 16 * l.  lds_base must
+// be wave-uniform.  Issued from inline assembly so that the compiler neither
+// reorders it across other memory operations ("memory" clobber) nor inserts
+// its own conservative waits for it; the caller waits with s_waitcnt vmcnt
+// before reading the destination.  It has no register result.
+__device__ __forceinline__ void dma16_to_lds(const void *gptr, const GQA_LDS void *lds_base) {
+    const unsigned m0v = (unsigned)(uintptr_t)lds_base;
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(gptr), "s"(m0v)
+        : "memory", "m0");
 }
 
 __device__ __forceinline__ u32x4 load16(const void *p) {

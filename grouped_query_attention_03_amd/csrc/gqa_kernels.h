@@ -23,10 +23,10 @@ struct DecodeArgs {
     const void *q, *k_cache, *v_cache;
     const int32_t *seqlens;
     void *o;
-    float *opart;  // [B, h_q, NC, d] partial outputs (normalised per chunk)
-    float *lse;    // [B, h_q, NC] log2-sum-exp of each chunk, in scaled log2 units
+    float *opart;  // [NW + segments][16][d] per-slot partial outputs (normalised)
+    float *lse;    // [NW + segments][16] base-2 log-sum-exp of each partial, scaled units
     int B, h_q, h_kv, G, S;
-    int CH, NC;    // keys per chunk, chunks per sequence (ceil(S / CH))
+    int NW;        // waves in the split pass (number of slices of the block list)
     int n_qsub;    // query-head subgroups of at most 16 heads per key/value head
     float c;       // log2(e) / sqrt(d)
 };

@@ -45,7 +45,7 @@ enum {
     GQA_OK = 0,
     GQA_ERR_NULL_POINTER = 1,  /* a required pointer is NULL */
     GQA_ERR_ALIGNMENT = 2,     /* a pointer is not 16-byte aligned */
-    GQA_ERR_SIZE = 3,          /* a size is <= 0, too large, or a chunk size is invalid */
+    GQA_ERR_SIZE = 3,          /* a size or split count is out of range, or scale is not > 0 */
     GQA_ERR_HEADS = 4,         /* h_q is not a multiple of h_kv */
     GQA_ERR_HEAD_DIM = 5,      /* d is not 64 or 128 */
     GQA_ERR_DTYPE = 6,         /* dtype not supported by this entry point */
@@ -77,29 +77,32 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *o, int
  *   q, o               : [B, 1, h_q, d]  bf16
  *   k_cache, v_cache   : [B, h_kv, S, d] bf16
  *   seqlens            : [B] int32 on the device, each in [0, S]; not checked on
- *                        the device.  seqlens[b] == 0 yields a zero output row.
+ *                        the device (a value above S reads past the sequence's
+ *                        cache rows).  seqlens[b] == 0 yields a zero output row.
  *                        Cache rows at or beyond seqlens[b] are never read.
  *   scale is fixed to 1/sqrt(d).
- *   chunk: keys per split of the sequence; 0 picks the library default,
- *          otherwise a multiple of 64 in [64, 8192].  The result does not
- *          depend on it beyond floating-point rounding.
+ *   num_splits: how many slices the valid cache blocks are cut into (one wave
+ *          of the split pass per slice); 0 picks the library default, else
+ *          1 .. 2^20.  The result does not depend on it beyond floating-point
+ *          rounding.
  *   workspace: device buffer of at least gqa_decode_workspace_bytes(...) bytes
- *          holding per-split partial outputs and log-sum-exp values; its
+ *          holding per-slice partial outputs and log-sum-exp values; its
  *          contents on entry are ignored.
- * Two kernels run on `hip_stream`: a split pass over (sequence, key/value
- * head, chunk) and a log-sum-exp merge pass over (sequence, query head).
+ * Two kernels run on `hip_stream`: the split pass (each wave streams one
+ * contiguous, equally sized slice of all sequences' valid 32-key blocks) and a
+ * log-sum-exp merge pass over (sequence, query head).
  */
 gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *seqlens, void *o, int B, int h_q, int h_kv, int S, int d,
-                      gqa_dtype dt, int chunk, void *workspace, size_t workspace_bytes,
+                      gqa_dtype dt, int num_splits, void *workspace, size_t workspace_bytes,
                       void *hip_stream);
 
-/* Bytes of decode workspace needed for these sizes and chunk (0 = default);
- * returns 0 when the sizes or the chunk are invalid. */
-size_t gqa_decode_workspace_bytes(int B, int h_q, int S, int d, int chunk);
+/* Bytes of decode workspace needed for these sizes and num_splits (0 =
+ * default); returns 0 when an argument is invalid. */
+size_t gqa_decode_workspace_bytes(int B, int h_q, int h_kv, int d, int num_splits);
 
-/* The chunk size gqa_decode uses when passed chunk == 0. */
-int gqa_decode_default_chunk(int S);
+/* The number of slices gqa_decode uses when passed num_splits == 0. */
+int gqa_decode_default_splits(void);
 
 /* Static, NUL-terminated description of a status code. */
 const char *gqa_status_string(gqa_status s);

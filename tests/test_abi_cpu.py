@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("gqa_prefill", "gqa_decode", "gqa_decode_workspace_bytes",
-              "gqa_decode_default_chunk", "gqa_status_string"):
+              "gqa_decode_default_splits", "gqa_status_string"):
         assert n in names
 
 
@@ -75,10 +75,11 @@ def test_prefill_without_a_gpu_reports_the_device():
 
 
 def decode_status(q=A, kc=A, vc=A, sl=A, o=A, B=4, h_q=32, h_kv=8, S=1024, d=128, dt=1,
-                  chunk=0, ws=A, ws_bytes=None):
+                  splits=0, ws=A, ws_bytes=None):
     if ws_bytes is None:
-        ws_bytes = gqa.decode_workspace_bytes(B, h_q, S, d, chunk) if d in (64, 128) else 1 << 30
-    return gqa.lib().gqa_decode(q, kc, vc, sl, o, B, h_q, h_kv, S, d, dt, chunk, ws, ws_bytes,
+        ws_bytes = (gqa.decode_workspace_bytes(B, h_q, h_kv, d, splits)
+                    if d in (64, 128) and h_q % h_kv == 0 else 1 << 30)
+    return gqa.lib().gqa_decode(q, kc, vc, sl, o, B, h_q, h_kv, S, d, dt, splits, ws, ws_bytes,
                                 None)
 
 
@@ -87,7 +88,7 @@ def decode_status(q=A, kc=A, vc=A, sl=A, o=A, B=4, h_q=32, h_kv=8, S=1024, d=128
     (dict(vc=MIS), ALIGN), (dict(sl=A + 2), ALIGN),
     (dict(S=0), SIZE), (dict(B=0), SIZE),
     (dict(h_q=32, h_kv=5), HEADS), (dict(d=80), HEADDIM), (dict(dt=0), DTYPE),
-    (dict(chunk=100), SIZE), (dict(chunk=32), SIZE), (dict(chunk=16384), SIZE),
+    (dict(splits=-1), SIZE), (dict(splits=(1 << 20) + 1), SIZE),
     (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE), (dict(ws=A + 8), WORKSPACE),
 ])
 def test_decode_rejects_bad_arguments(kw, status):
@@ -101,23 +102,23 @@ def test_decode_without_a_gpu_reports_the_device():
     assert decode_status(sl=A + 4) == DEVICE  # int32 alignment is enough for seqlens
 
 
-@pytest.mark.parametrize("B,h_q,S,d,chunk", [(64, 32, 8192, 128, 0), (3, 8, 1000, 64, 64),
-                                             (1, 1, 1, 128, 8192), (2, 64, 5000, 128, 512)])
-def test_workspace_bytes(B, h_q, S, d, chunk):
-    ch = gqa.decode_default_chunk(S) if chunk == 0 else chunk
-    nc = -(-S // ch)
-    rows = B * h_q * nc
+@pytest.mark.parametrize("B,h_q,h_kv,d,splits", [(64, 32, 8, 128, 0), (3, 8, 4, 64, 64),
+                                                  (1, 1, 1, 128, 1), (2, 64, 2, 128, 512)])
+def test_workspace_bytes(B, h_q, h_kv, d, splits):
+    # one slot per (slice, segment) staircase step: at most splits + segments
+    nw = gqa.decode_default_splits() if splits == 0 else splits
+    segments = B * h_kv * (-(-(h_q // h_kv) // 16))
+    slots = nw + segments
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert gqa.decode_workspace_bytes(B, h_q, S, d, chunk) == up(rows * d * 4) + up(rows * 4)
+    assert gqa.decode_workspace_bytes(B, h_q, h_kv, d, splits) == up(slots * 16 * d * 4) + up(slots * 16 * 4)
 
 
 def test_workspace_bytes_invalid():
-    assert gqa.decode_workspace_bytes(0, 32, 8192, 128, 0) == 0
-    assert gqa.decode_workspace_bytes(1, 32, 8192, 96, 0) == 0
-    assert gqa.decode_workspace_bytes(1, 32, 8192, 128, 65) == 0
+    assert gqa.decode_workspace_bytes(0, 32, 8, 128, 0) == 0
+    assert gqa.decode_workspace_bytes(1, 32, 8, 96, 0) == 0
+    assert gqa.decode_workspace_bytes(1, 32, 5, 128, 0) == 0
+    assert gqa.decode_workspace_bytes(1, 32, 8, 128, -1) == 0
 
 
-def test_default_chunk_is_valid():
-    for S in (1, 100, 8192, 65536):
-        ch = gqa.decode_default_chunk(S)
-        assert ch % 64 == 0 and 64 <= ch <= 8192
+def test_default_splits_is_valid():
+    assert 1 <= gqa.decode_default_splits() <= (1 << 20)

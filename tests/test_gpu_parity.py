@@ -182,10 +182,10 @@ def test_workload_long_context_prefill(dev):
 
 # ------------------------------------------------------------------------- decode
 
-def run_decode(seqlens, q, kc, vc, dev, chunk=0, out_fill=float("nan")):
+def run_decode(seqlens, q, kc, vc, dev, splits=0, out_fill=float("nan")):
     qd, kd, vd, sd = q.to(dev), kc.to(dev), vc.to(dev), seqlens.to(dev)
     out = torch.full_like(qd, out_fill)
-    gqa.decode(qd, kd, vd, sd, out=out, chunk=chunk)
+    gqa.decode(qd, kd, vd, sd, out=out, num_splits=splits)
     torch.cuda.synchronize()
     return out
 
@@ -238,17 +238,17 @@ def test_decode_matches_oracle(case, dev):
             assert torch.equal(out[b], torch.zeros_like(out[b]))
 
 
-def test_decode_split_size_does_not_change_the_result(dev):
+def test_decode_split_count_does_not_change_the_result(dev):
     B, h_q, h_kv, S, d = 4, 32, 8, 3000, 128
     seqlens, q, kc, vc = wl.decode_inputs(B, h_q, h_kv, S, d, 41, (1, S))
     ref = decode_ref(seqlens, q, kc, vc)
     outs = {}
-    for ch in (64, 128, 512, 1024, 8192):
-        say(f"decode split identity chunk {ch}")
-        outs[ch] = run_decode(seqlens, q, kc, vc, dev, chunk=ch).cpu()
-        check(f64(outs[ch][:, 0]), ref, "bf16", f"chunk {ch} vs oracle")
-    for ch in outs:
-        check(f64(outs[ch]), f64(outs[8192]), "bf16", f"chunk {ch} vs chunk 8192")
+    for ns in (1, 3, 64, 1000, 5000, 0):
+        say(f"decode split identity num_splits {ns}")
+        outs[ns] = run_decode(seqlens, q, kc, vc, dev, splits=ns).cpu()
+        check(f64(outs[ns][:, 0]), ref, "bf16", f"num_splits {ns} vs oracle")
+    for ns in outs:
+        check(f64(outs[ns]), f64(outs[1]), "bf16", f"num_splits {ns} vs num_splits 1")
 
 
 def test_decode_is_deterministic(dev):
