@@ -15,32 +15,54 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libgqa_hip.so")
 SOURCES = ["gqa_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode_bf16.hip"]
+# Per-source additions.  The bf16 prefill kernel never orders NaNs (masked and
+# stale scores are replaced by -inf with a select before any max), so it runs
+# with the IEEE mode bit off: max/min then need no canonicalising copies.
+SOURCE_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from forming packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # select the VGPR form of MFMA instructions; the register allocator then
+    # moves only accumulator chains that never feed vector ALU work to AGPRs
+    # (prefill keeps its output accumulators there and its scores in VGPRs)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
+# hipcc's host pass does not know the packed-fp32 feature; that note is harmless
+_NOISE = "is not a recognized feature for this target"
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every HIP source into ``libgqa_hip.so`` (always recompiles)."""
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass does not know the packed-fp32 feature; that note is harmless
-    noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln]
+    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if _NOISE not in ln]
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB_PATH)
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every HIP source into ``libgqa_hip.so`` (always recompiles)."""
+    tag = ".tmp%d" % os.getpid()
+    objs = []
+    try:
+        for src in SOURCES:
+            obj = os.path.join(PKG_DIR, src + tag + ".o")
+            objs.append(obj)
+            _run([HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *extra_flags, "-I", INCLUDE,
+                  "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        tmp = LIB_PATH + tag
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, LIB_PATH)
+    finally:
+        for obj in objs:
+            if os.path.exists(obj):
+                os.remove(obj)
     return LIB_PATH
 
 

@@ -77,6 +77,9 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *o, int
     if (!(scale > 0.f) || !isfinite(scale)) return GQA_ERR_SIZE;
     const int64_t rows_q = (int64_t)B * L * h_q, rows_kv = (int64_t)B * L * h_kv;
     if (rows_q > (int64_t)1 << 31 || rows_kv > (int64_t)1 << 31) return GQA_ERR_SIZE;
+    // the bf16 kernel addresses one sequence's key/value rows of a head with
+    // 32-bit byte offsets: L rows at a stride of h_kv * d elements
+    if (dt == GQA_BF16 && (int64_t)L * h_kv * d * 2 > (int64_t)0xffffffff) return GQA_ERR_SIZE;
 
     gqa::PrefillArgs a;
     a.q = q;

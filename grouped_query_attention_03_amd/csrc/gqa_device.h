@@ -98,6 +98,37 @@ __device__ __forceinline__ void dma16_to_lds(const void *gptr, const GQA_LDS voi
         : "memory", "m0");
 }
 
+// Raw buffer resource for a byte range [base, base + bytes): reads at offsets
+// at or beyond `bytes` are out of range and return zeros.  All fields must be
+// wave-uniform so that the descriptor lives in scalar registers.
+__device__ __forceinline__ u32x4 make_buffer_rsrc(const void *base, unsigned bytes) {
+    const unsigned long long a = (unsigned long long)(uintptr_t)base;
+    // readfirstlane: the compiler may have computed a uniform value in vector
+    // registers, and the descriptor operand must be scalar
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((unsigned)a);
+    r[1] = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32) & 0xffffu);  // stride 0: raw bytes
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);                        // num_records, in bytes
+    r[3] = 0x00020000u;                                                  // 32-bit data format
+    return r;
+}
+
+// 16-byte direct load through a buffer resource into LDS
+// (buffer_load_dwordx4 ... lds): lane l reads bytes [voffset, voffset + 16)
+// of the resource's range (zeros when out of range) and its 16 bytes land at
+// lds_base + 16 * l.  Same ordering and waiting rules as dma16_to_lds.
+__device__ __forceinline__ void dma16_to_lds_buf(u32x4 rsrc, unsigned voffset,
+                                                 const GQA_LDS void *lds_base) {
+    const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_base);
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %1, 0 offen lds"
+        :
+        : "v"(voffset), "s"(rsrc), "s"(m0v)
+        : "memory", "m0");
+}
+
 __device__ __forceinline__ u32x4 load16(const void *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }

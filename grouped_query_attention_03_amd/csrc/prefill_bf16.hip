@@ -5,98 +5,109 @@
 // (1): GQA and RMSNorm", §2.1 formula, §2.3 grouping; "Attention in Qwen,
 // DeepSeek and LLaMA3", §2.2 head map).  The softmax is evaluated tile by tile
 // with running statistics (the on-chip, no-HBM-round-trip form that "What is
-// Grouped-Query Attention", §4.3 credits to FlashAttention), which is an exact
+// Grouped-Query Attention", §4.3 credits to FlashAttention), an exact
 // rearrangement of the row softmax.
 //
 // Work decomposition
-//   One work-group (4 waves) owns 256 query rows: GW query heads of ONE group
+//   One work-group (8 waves) owns 256 query rows: GW query heads of ONE group
 //   times BM = 256 / GW consecutive positions (GW = the largest power of two
 //   dividing G, at most 8; larger groups are split over G / GW work-groups).
-//   Each key/value tile is loaded into LDS once and used by all GW heads: this
-//   is the group-sharing saving, the key/value head is never copied per query
-//   head.  Rows are cut into 8 row blocks of 32 (one head x 32 positions);
-//   wave w owns row blocks 2w and 2w+1.
+//   Each key/value tile is loaded into LDS once and used by all GW heads: the
+//   group-sharing saving; the key/value head is never copied per query head.
+//   Wave w owns one row block of 32 rows (one head x 32 positions).
 //
 // Per wave and per key tile of 64 keys (S^T formulation)
 //   S^T[key][query] = K Q^T on v_mfma_f32_32x32x16_bf16: A = K rows read from
-//   LDS (16-byte reads), B = Q^T kept in registers for the whole kernel.  In
-//   the accumulator layout each lane holds 16 keys of ONE query column, so the
-//   row max and row sum are in-lane reductions plus one exchange with the
-//   other half-wave.
+//   LDS, B = Q^T held in registers for the whole kernel.  Each lane holds 16
+//   keys of ONE query column, so row max and row sum are in-lane reductions
+//   plus one exchange with the other half-wave.
 //   P = exp2(S * scale*log2(e) - m) with a lazily updated running max m: the
 //   accumulators are rescaled only when a row max grows by more than TAU (in
-//   log2 units), which keeps every P <= 2^TAU and skips almost all rescales.
+//   log2 units), so every P <= 2^TAU and almost no rescale is executed.
 //   O^T[d][query] += V^T P^T: P^T comes straight out of the S^T accumulators
 //   (keys permuted consistently on both operands), V^T is read from the
 //   row-major V tile with the transposing ds_read_b64_tr_b16.
-//   Causal: tiles wholly above the diagonal are never visited, the diagonal
-//   and the sequence tail are masked element-wise.
-#include <stdlib.h>
-
+//
+// Schedule
+//   Two waves share each SIMD, so one wave's matrix products run while the
+//   other computes exponentials or waits for LDS.
+//   K/V tiles move with direct buffer->LDS loads (waves 0-3 the K tile, waves
+//   4-7 the V tile) into a 4-slot ring: tile x is issued at the start of
+//   iteration x - 3 into slot x % 4, whose previous tile x - 4 was last read in
+//   iteration x - 4, before the barrier that ends it.  The buffer range ends at
+//   key row L - 1, so the rows of a ragged last tile past the sequence read as
+//   zeros.
+//   Each wave waits for its own share of the next tile (s_waitcnt vmcnt) before
+//   the barrier that ends an iteration, so after that barrier the whole tile is
+//   visible: one work-group barrier per tile.
+//   Scale * log2(e) is folded into Q once, and every QK accumulator chain
+//   starts from -mu (the MFMA C operand), so S arrives in log2 units already
+//   shifted by the running max; row sums are taken with v_dot2_f32_bf16 on the
+//   bf16-rounded P that the PV product uses.
+//   Causal: tiles wholly above the diagonal are never loaded or computed; the
+//   diagonal and the sequence tail are masked element-wise.
 #include "gqa_device.h"
 #include "gqa_kernels.h"
 
 namespace gqa {
 namespace {
 
-constexpr int PF_ROWS = 256;     // query rows per work-group (8 row blocks of 32)
+constexpr int PF_WAVES = 8;
+constexpr int PF_THREADS = 64 * PF_WAVES;
 constexpr int PF_BN = 64;       // keys per tile
+constexpr int PF_SLOTS = 4;     // LDS ring depth (tiles)
 constexpr float PF_TAU = 8.0f;  // lazy-rescale threshold, log2 units
+constexpr int PF_DIST = 3;      // tiles issued ahead of the one being computed
 
-template <int D, int THREADS>
-struct PfLayout {
-    // K rows padded by 16 bytes: 16 lanes reading 16 rows at one column hit
-    // 16 distinct 4-bank groups.  V rows padded so the 4-row x 32-byte blocks
-    // of a transposing read fall in distinct banks.
-    static constexpr int KS = D + 8;   // K row stride, elements
-    static constexpr int VS = D + 32;  // V row stride, elements
-    static constexpr int K_ELEMS = PF_BN * KS;
-    static constexpr int V_ELEMS = PF_BN * VS;
-    static constexpr int STAGE = K_ELEMS + V_ELEMS;
-    static constexpr int CHUNKS = PF_BN * D / 8;          // 16-byte chunks per tile
-    static constexpr int PER_THREAD = CHUNKS / THREADS;   // per K (and per V)
+template <int D>
+struct PfLay {
+    static constexpr int ROW_BYTES = 2 * D;
+    static constexpr int CPR = D / 8;                        // 16-byte chunks per row
+    static constexpr int ROWS_PER_DMA = 64 / CPR;            // rows per 64-lane 16-byte load
+    static constexpr int TILE_BYTES = PF_BN * ROW_BYTES;     // one K or V tile
+    static constexpr int DMA_PER_TENSOR = TILE_BYTES / 1024;
+    static constexpr int DMA_PER_WAVE = 2 * DMA_PER_TENSOR / PF_WAVES;
+    static constexpr int SLOT_BYTES = 2 * TILE_BYTES;        // K tile then V tile
+    static constexpr int ROWS_PER_SWEEP = 256 / ROW_BYTES;   // rows per pass over the banks
+    static constexpr int KSTEPS = D / 16;                    // MFMA k-steps over d
+    static constexpr int DB = D / 32;                        // 32-wide blocks of d
 };
 
-template <int D, int THREADS>
-__device__ __forceinline__ void pf_load_tile(const __bf16 *__restrict__ src, size_t row_stride,
-                                             int j0, int L,
-                                             u32x4 (&r)[PfLayout<D, THREADS>::PER_THREAD]) {
-    constexpr int CPR = D / 8;  // chunks per row
-#pragma unroll
-    for (int i = 0; i < PfLayout<D, THREADS>::PER_THREAD; ++i) {
-        int c = threadIdx.x + THREADS * i;
-        int row = c / CPR, col = c % CPR;
-        int key = j0 + row;
-        if (key < L)
-            r[i] = load16(src + (size_t)key * row_stride + 8 * col);
-        else
-            r[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+// Tiles are stored unpadded (each direct load writes 64 consecutive 16-byte
+// chunks); 16-byte chunk c of row r sits at chunk position c ^ swz(r).
+//   K: 16 lanes reading one chunk of 16 consecutive rows hit distinct banks.
+//   V: a half-wave transposing read (4 rows x 64 bytes) hits distinct banks.
+template <int D>
+__device__ __forceinline__ int pf_kswz(int r) {
+    using Lay = PfLay<D>;
+    return (r / Lay::ROWS_PER_SWEEP) % Lay::CPR;
+}
+template <int D>
+__device__ __forceinline__ int pf_vswz(int r) {
+    return D == 128 ? 4 * (r % 4) : 4 * ((r / 2) % 2);
 }
 
-template <int D, int THREADS, int STRIDE>
-__device__ __forceinline__ void pf_store_tile(__bf16 *lds,
-                                              const u32x4 (&r)[PfLayout<D, THREADS>::PER_THREAD]) {
-    constexpr int CPR = D / 8;
-#pragma unroll
-    for (int i = 0; i < PfLayout<D, THREADS>::PER_THREAD; ++i) {
-        int c = threadIdx.x + THREADS * i;
-        int row = c / CPR, col = c % CPR;
-        store16_lds(lds + row * STRIDE + 8 * col, r[i]);
-    }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// NW waves per work-group; each wave owns RB = 8 / NW row blocks of 32 rows.
-template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillArgs a) {
-    constexpr int THREADS = NW * 64;
-    constexpr int RB = 8 / NW;
-    using Lay = PfLayout<D, THREADS>;
-    constexpr int KSTEPS = D / 16;  // MFMA k-steps over the head dimension
-    constexpr int DB = D / 32;      // 32-wide blocks of the head dimension
-    __shared__ __attribute__((aligned(16))) __bf16 smem[2 * Lay::STAGE];
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("s_barrier" ::: "memory");
+}
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs a) {
+    using Lay = PfLay<D>;
+    constexpr int KSTEPS = Lay::KSTEPS, DB = Lay::DB, DPW = Lay::DMA_PER_WAVE;
+    __shared__ __attribute__((aligned(1024))) char smem[PF_SLOTS * Lay::SLOT_BYTES];
+
+    const int lane = threadIdx.x & 63, wave = wave_id();
+    // Lane id used for LDS/global address arithmetic inside the tile loop.  It
+    // is passed through an empty asm at every iteration so the compiler
+    // recomputes the (cheap) swizzled offsets instead of hoisting them out of
+    // the loop and spilling them.
+    int ln = lane;
     const int lid = xcd_contiguous_id(blockIdx.x, gridDim.x);
     const int unit = lid / a.n_qtiles;
     int qt = lid % a.n_qtiles;
@@ -109,222 +120,238 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(PrefillArgs a)
     const int PB = 8 / a.GW;  // 32-position blocks per work-group
     const int p0 = qt * a.BM;
 
-    const __bf16 *kbase = static_cast<const __bf16 *>(a.k) + ((size_t)b * L * a.h_kv + kvh) * D;
-    const __bf16 *vbase = static_cast<const __bf16 *>(a.v) + ((size_t)b * L * a.h_kv + kvh) * D;
-    const size_t kv_row = (size_t)a.h_kv * D;
-
-    int head[RB], pos0[RB];
-#pragma unroll
-    for (int t = 0; t < RB; ++t) {
-        int rb = RB * wave + t;
-        head[t] = kvh * a.G + sub * a.GW + rb / PB;
-        pos0[t] = p0 + 32 * (rb % PB);
-    }
-
-    // Q^T operands: lane holds 8 head-dim values of one query row.
-    bf16x8 qf[RB][KSTEPS];
-#pragma unroll
-    for (int t = 0; t < RB; ++t) {
-        int pos = pos0[t] + (lane & 31);
-        if (pos < L) {
-            const __bf16 *qp = static_cast<const __bf16 *>(a.q) +
-                               (((size_t)b * L + pos) * a.h_q + head[t]) * D + 8 * (lane >> 5);
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks)
-                qf[t][ks] = __builtin_bit_cast(bf16x8, load16(qp + 16 * ks));
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) qf[t][ks] = bf16x8{};
-        }
-    }
-
-    f32x16 acc[RB][DB];
-#pragma unroll
-    for (int t = 0; t < RB; ++t)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[t][db] = f32x16{};
-    float m_run[RB], l_run[RB];
-#pragma unroll
-    for (int t = 0; t < RB; ++t) {
-        m_run[t] = -INFINITY;
-        l_run[t] = 0.f;
-    }
-
+    const int head = kvh * a.G + sub * a.GW + wave / PB;
+    const int pos0 = p0 + 32 * (wave % PB);
     const int kv_end = CAUSAL ? min(L, p0 + a.BM) : L;
     const int ntiles = (kv_end + PF_BN - 1) / PF_BN;
-    int wave_last_pos = pos0[0] + 31, wave_first_pos = pos0[0];
+
+    // ---- direct loads: waves 0-3 stream the K tile and waves 4-7 the V tile;
+    // this wave moves 1 KiB pieces i0 .. i0 + DPW - 1 of every tile.
+    constexpr int NLO = Lay::CPR / 4;  // distinct per-lane offsets (period of the K swizzle)
+    static_assert(Lay::DMA_PER_TENSOR == DPW * PF_WAVES / 2, "half the waves load K, half V");
+    static_assert(DPW % NLO == 0, "per-lane offsets repeat with the K swizzle");
+    const bool loads_v = wave >= PF_WAVES / 2;
+    const int i0 = (wave % (PF_WAVES / 2)) * DPW;
+    const unsigned krb = (unsigned)(a.h_kv * D * 2);  // key row stride, bytes
+    // rows 0 .. L-1 of this (sequence, key/value head); L * krb < 2^32 is checked
+    // on the host.  Rows past the sequence end read as zeros.
+    const u32x4 rsrc = make_buffer_rsrc(
+        static_cast<const __bf16 *>(loads_v ? a.v : a.k) + ((size_t)b * L * a.h_kv + kvh) * D,
+        (unsigned)(L - 1) * krb + 2 * D);
+    // per-lane byte offset of piece i within its rows; depends on i only via i % NLO
+    unsigned loff[NLO];
 #pragma unroll
-    for (int t = 1; t < RB; ++t) {
-        wave_last_pos = max(wave_last_pos, pos0[t] + 31);
-        wave_first_pos = min(wave_first_pos, pos0[t]);
+    for (int u = 0; u < NLO; ++u) {
+        const int row = u * Lay::ROWS_PER_DMA + lane / Lay::CPR;
+        const int chunk = (lane % Lay::CPR) ^ (loads_v ? pf_vswz<D>(row) : pf_kswz<D>(row));
+        loff[u] = (unsigned)(lane / Lay::CPR) * krb + 16u * chunk;
     }
-    const bool wave_has_rows = wave_first_pos < L;
-    const float c = a.c;
-
-    u32x4 kr[Lay::PER_THREAD], vr[Lay::PER_THREAD];
-    pf_load_tile<D, THREADS>(kbase, kv_row, 0, L, kr);
-    pf_load_tile<D, THREADS>(vbase, kv_row, 0, L, vr);
-    pf_store_tile<D, THREADS, Lay::KS>(smem, kr);
-    pf_store_tile<D, THREADS, Lay::VS>(smem + Lay::K_ELEMS, vr);
-    __syncthreads();
-
-    for (int j = 0; j < ntiles; ++j) {
-        const int j0 = j * PF_BN;
-        const bool more = j + 1 < ntiles;
-        if (more) {
-            pf_load_tile<D, THREADS>(kbase, kv_row, j0 + PF_BN, L, kr);
-            pf_load_tile<D, THREADS>(vbase, kv_row, j0 + PF_BN, L, vr);
-        }
-        const __bf16 *ks_lds = smem + (j & 1) * Lay::STAGE;
-        const __bf16 *vs_lds = ks_lds + Lay::K_ELEMS;
-
-        if (wave_has_rows && (!CAUSAL || j0 <= wave_last_pos)) {
-            // ---- S^T = K Q^T for 2 key blocks x RB row blocks
-            f32x16 s[RB][2];
+    // this wave's share of the loads of tile x into ring slot x % PF_SLOTS
+    auto issue_tile = [&](int x) {
 #pragma unroll
-            for (int t = 0; t < RB; ++t) s[t][0] = s[t][1] = f32x16{};
+        for (int u = 0; u < DPW; ++u) {
+            const int i = i0 + u;
+            const unsigned row0 = (unsigned)(x * PF_BN + i * Lay::ROWS_PER_DMA);
+            dma16_to_lds_buf(rsrc, loff[u % NLO] + row0 * krb,
+                             (GQA_LDS char *)(smem + (x % PF_SLOTS) * Lay::SLOT_BYTES +
+                                              (loads_v ? Lay::TILE_BYTES : 0) + i * 1024));
+        }
+    };
+
+    // Q^T operand: lane holds 8 head-dim values of one query row.
+    bf16x8 qf[KSTEPS];
+    {
+        const int pos = pos0 + (lane & 31);
+        if (pos < L) {
+            const __bf16 *qp = static_cast<const __bf16 *>(a.q) +
+                               (((size_t)b * L + pos) * a.h_q + head) * D + 8 * (lane >> 5);
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
+                // fold scale * log2(e) into Q once (rounded to bf16): S^T then
+                // comes out of the MFMA already in log2 units
+                const bf16x8 raw = __builtin_bit_cast(bf16x8, load16(qp + 16 * ks));
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
-                        ks_lds + (32 * kb + (lane & 31)) * Lay::KS + 16 * ks + 8 * (lane >> 5));
-#pragma unroll
-                    for (int t = 0; t < RB; ++t) s[t][kb] = mfma32x32x16(ka, qf[t][ks], s[t][kb]);
-                }
+                for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)raw[e] * a.c);
             }
-            // ---- mask the diagonal tile and the tail of the sequence
-            const bool need_mask = (j0 + PF_BN > L) || (CAUSAL && j0 + PF_BN - 1 > wave_first_pos);
-            if (need_mask) {
+        } else {
 #pragma unroll
-                for (int t = 0; t < RB; ++t) {
-                    const int pos = pos0[t] + (lane & 31);
+            for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = bf16x8{};
+        }
+    }
+
+    f32x16 acc[DB];
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    // -mu in every element: the C operand of the first QK MFMA of each chain,
+    // so the accumulators hold S * scale*log2(e) - mu with no VALU work.
+    // mu is the running max (0 before the first tile).
+    f32x16 negm = f32x16{};
+    float mu = 0.f;
+    bf16x8 pb[2][2];  // P^T of the current tile: [key block][16-key half]
+    float m_run = -INFINITY, l_run = 0.f;
+    const bool has_rows = pos0 < L;
+    auto active = [&](int j) { return has_rows && (!CAUSAL || j * PF_BN <= pos0 + 31); };
+
+    // LDS operand reads for step st of the two products (16-byte K chunk;
+    // transposed V pair); st runs over (k-step, key block) for QK and over
+    // (key block, 16-key half, d block) for PV.
+    constexpr int NSTEP = 2 * KSTEPS;  // == 4 * DB
+    static_assert(NSTEP == 4 * DB, "QK and PV have the same number of MFMA steps");
+    auto kread = [&](const char *kt, int st) {
+        const int ks = st >> 1, kb = st & 1;
+        const int r = 32 * kb + (ln & 31);
+        const int ch = (2 * ks + (ln >> 5)) ^ pf_kswz<D>(r);
+        return *reinterpret_cast<const bf16x8 *>(kt + r * Lay::ROW_BYTES + 16 * ch);
+    };
+    auto vread = [&](const char *vt, int st) {
+        const int grp = ln >> 4, jl = ln & 15;
+        const int vrq = 4 * (grp >> 1) + (jl >> 2);      // V row within a 16-key step (+8 for hi)
+        const int vcq = 2 * (grp & 1) + ((jl & 3) >> 1);  // 16-byte chunk within a 32-wide d block
+        const int vsw = pf_vswz<D>(vrq);                  // same for vrq + 8 and every step
+        const int kh = st / DB, db = st % DB;             // kh = 2 * key block + half
+        const char *p0 = vt + vrq * Lay::ROW_BYTES + 8 * (jl & 1) + 16 * kh * Lay::ROW_BYTES +
+                         16 * ((4 * db + vcq) ^ vsw);
+        short4v lo = lds_read_tr16(reinterpret_cast<const __bf16 *>(p0));
+        short4v hi = lds_read_tr16(reinterpret_cast<const __bf16 *>(p0 + 8 * Lay::ROW_BYTES));
+        return join_tr(lo, hi);
+    };
+    auto qk = [&](int j) {  // S^T = K Q^T - mu for tile j
+        const char *kt = smem + (j % PF_SLOTS) * Lay::SLOT_BYTES;
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                            bool masked = key >= L || (CAUSAL && key > pos);
-                            s[t][kb][r] = masked ? -INFINITY : s[t][kb][r];
-                        }
-                }
-            }
-            // ---- running max with lazy rescale
-            float mnew[RB];
-            bool grow = false;
+        for (int st = 0; st < NSTEP; ++st) {
+            const int ks = st >> 1, kb = st & 1;
+            s[kb] = mfma32x32x16(kread(kt, st), qf[ks], ks == 0 ? negm : s[kb]);
+        }
+    };
+    auto pv = [&](int j) {  // O^T += V^T P^T for tile j
+        const char *vt = smem + (j % PF_SLOTS) * Lay::SLOT_BYTES + Lay::TILE_BYTES;
 #pragma unroll
-            for (int t = 0; t < RB; ++t) {
-                float mx = s[t][0][0];
-#pragma unroll
-                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[t][0][r]);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][1][r]);
-                mx = fmaxf(mx, other_half(mx));
-                mnew[t] = mx * c;
-                grow = grow || (mnew[t] > m_run[t] + PF_TAU);
-            }
-            if (__any(grow)) {
-#pragma unroll
-                for (int t = 0; t < RB; ++t) {
-                    float m2 = fmaxf(m_run[t], mnew[t]);
-                    float alpha = (m2 == -INFINITY) ? 1.f : fast_exp2(m_run[t] - m2);
-                    m_run[t] = m2;
-                    l_run[t] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) acc[t][db] *= alpha;
-                }
-            }
-            // ---- P = exp2(S*c - m), row sums, pack to bf16 as the B operand of PV
-            bf16x8 pb[RB][2][2];  // [row block][key block][16-key half]
-#pragma unroll
-            for (int t = 0; t < RB; ++t) {
-                const float mu = (m_run[t] == -INFINITY) ? 0.f : m_run[t];
-                float lsum = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            float p = fast_exp2(fmaf(s[t][kb][8 * hh + i], c, -mu));
-                            lsum += p;
-                            pb[t][kb][hh][i] = (__bf16)p;
-                        }
-                l_run[t] += lsum;
-            }
-            // ---- O^T += V^T P^T
-            const int grp = lane >> 4, jl = lane & 15;
-            const int vrow = 4 * (grp >> 1) + (jl >> 2);
-            const int vcol = 16 * (grp & 1) + 4 * (jl & 3);
+        for (int st = 0; st < NSTEP; ++st) {
+            const int kh = st / DB, db = st % DB;
+            acc[db] = mfma32x32x16(vread(vt, st), pb[kh >> 1][kh & 1], acc[db]);
+        }
+    };
+    // Softmax of tile j: mask, running max, P = exp2(S c - m), row sums.
+    // s holds S c - mu.  The max is raised (and O, l rescaled) only when a row's
+    // new max exceeds mu by more than TAU, or on the first tile.
+    auto softmax = [&](int j) {
+        const int j0 = j * PF_BN;
+        if (j0 + PF_BN > L || (CAUSAL && j0 + PF_BN - 1 > pos0)) {
+            const int pos = pos0 + (lane & 31);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const __bf16 *vp = vs_lds + (32 * kb + 16 * hh + vrow) * Lay::VS + vcol;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        short4v lo = lds_read_tr16(vp + 32 * db);
-                        short4v hi = lds_read_tr16(vp + 8 * Lay::VS + 32 * db);
-                        bf16x8 va = join_tr(lo, hi);
-#pragma unroll
-                        for (int t = 0; t < RB; ++t)
-                            acc[t][db] = mfma32x32x16(va, pb[t][kb][hh], acc[t][db]);
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    const bool masked = key >= L || (CAUSAL && key > pos);
+                    s[kb][r] = masked ? -INFINITY : s[kb][r];
                 }
         }
-        if (more) {
-            __bf16 *nxt = smem + ((j + 1) & 1) * Lay::STAGE;
-            pf_store_tile<D, THREADS, Lay::KS>(nxt, kr);
-            pf_store_tile<D, THREADS, Lay::VS>(nxt + Lay::K_ELEMS, vr);
+        float m8[8];  // pairwise tree: short dependency chains
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            m8[r] = fmaxf(fmaxf(s[0][2 * r], s[0][2 * r + 1]), fmaxf(s[1][2 * r], s[1][2 * r + 1]));
+#pragma unroll
+        for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+            for (int r = 0; r < w; ++r) m8[r] = fmaxf(m8[r], m8[r + w]);
+        const float mx = fmaxf(m8[0], other_half(m8[0]));  // tile row max, relative to mu
+        if (__any(m_run == -INFINITY || mx > PF_TAU)) {
+            const float m2 = m_run == -INFINITY ? mu + mx : fmaxf(m_run, mu + mx);
+            const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m2);
+            const float delta = (m2 == -INFINITY) ? 0.f : m2 - mu;
+            m_run = m2;
+            mu += delta;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) s[kb] -= delta;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) negm[r] = -mu;
         }
-        __syncthreads();
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int i = 0; i < 8; i += 2) {
+                    const bf16x2 p2 = {(__bf16)fast_exp2(s[kb][8 * hh + i]),
+                                       (__bf16)fast_exp2(s[kb][8 * hh + i + 1])};
+                    pb[kb][hh][i] = p2[0];
+                    pb[kb][hh][i + 1] = p2[1];
+                    // row sum of the bf16-rounded P that the PV product uses
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, l_run, false);
+                }
+    };
+
+    // V rows past the sequence end meet P = 0 and must be finite: zero the V
+    // halves of the ring once, in case an out-of-range load leaves its LDS
+    // bytes untouched.
+    for (int i = threadIdx.x; i < PF_SLOTS * Lay::TILE_BYTES / 16; i += PF_THREADS) {
+        const int sl = i / (Lay::TILE_BYTES / 16), off = i % (Lay::TILE_BYTES / 16);
+        store16_lds(smem + sl * Lay::SLOT_BYTES + Lay::TILE_BYTES + 16 * off, u32x4{0u, 0u, 0u, 0u});
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    block_barrier();
+    issue_tile(0);
+#pragma unroll
+    for (int x = 1; x < PF_DIST; ++x)
+        if (x < ntiles) issue_tile(x);
+    // tile 0 has landed once at most the loads of tiles 1 .. PF_DIST - 1 are pending
+    if (ntiles >= 3) wait_vmcnt<2 * DPW>();
+    else if (ntiles == 2) wait_vmcnt<DPW>();
+    else wait_vmcnt<0>();
+    block_barrier();
+    for (int j = 0; j < ntiles; ++j) {
+        ln = lane;
+        asm volatile("" : "+v"(ln));
+        if (j + PF_DIST < ntiles) issue_tile(j + PF_DIST);
+        if (active(j)) {
+            qk(j);
+            softmax(j);
+            pv(j);
+        }
+        // tile j + 1 must have landed; tiles j + 2 .. j + PF_DIST may be pending
+        const int pending = min(ntiles - 1, j + PF_DIST) - (j + 1);
+        if (pending >= 2) wait_vmcnt<2 * DPW>();
+        else if (pending == 1) wait_vmcnt<DPW>();
+        else wait_vmcnt<0>();
+        block_barrier();
     }
 
     // ---- epilogue: O / l, round to bf16, store
+    const float lt = l_run + other_half(l_run);
+    const int pos = pos0 + (lane & 31);
+    if (pos < L) {
+        const float inv = 1.f / lt;
+        __bf16 *op = static_cast<__bf16 *>(a.o) + (((size_t)b * L + pos) * a.h_q + head) * D +
+                     4 * (lane >> 5);
 #pragma unroll
-    for (int t = 0; t < RB; ++t) {
-        float lt = l_run[t] + other_half(l_run[t]);
-        float inv = 1.f / lt;
-        int pos = pos0[t] + (lane & 31);
-        if (pos < L) {
-            __bf16 *op = static_cast<__bf16 *>(a.o) +
-                         (((size_t)b * L + pos) * a.h_q + head[t]) * D + 4 * (lane >> 5);
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+            for (int rq = 0; rq < 4; ++rq) {
+                bf16x4 w;
 #pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    bf16x4 w;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[t][db][4 * rq + e] * inv);
-                    *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * rq) = w;
-                }
-        }
+                for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[db][4 * rq + e] * inv);
+                *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * rq) = w;
+            }
     }
-}
-
-template <int D, bool CAUSAL>
-void launch_variant(const PrefillArgs &a, hipStream_t stream) {
-    dim3 grid(a.n_units * a.n_qtiles);
-    // GQA_PREFILL_WAVES selects 4 or 8 waves per work-group (default 8)
-    static const int nw = [] {
-        const char *e = getenv("GQA_PREFILL_WAVES");
-        return (e && atoi(e) == 4) ? 4 : 8;
-    }();
-    if (nw == 4)
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, 4>), grid, dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, 8>), grid, dim3(512), 0, stream, a);
 }
 
 }  // namespace
 
 int launch_prefill_bf16(const PrefillArgs &a, int d, bool causal, hipStream_t stream) {
+    dim3 grid(a.n_units * a.n_qtiles), block(PF_THREADS);
     if (d == 128) {
-        if (causal) launch_variant<128, true>(a, stream);
-        else launch_variant<128, false>(a, stream);
+        if (causal) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, stream, a);
     } else {
-        if (causal) launch_variant<64, true>(a, stream);
-        else launch_variant<64, false>(a, stream);
+        if (causal) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, stream, a);
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -63,7 +63,9 @@ enum {
  *   dt: GQA_BF16 (bf16 MFMA path) or GQA_F32 (fp32 path).
  * The causal mask follows the masked_fill(mask == 0, -inf) form of
  * "Modern LLM architecture (1): GQA and RMSNorm", §2.1-§2.3.
- * Limits: B * h_q * L and B * h_kv * L must each fit in 2^31 elements of d.
+ * Limits: B * h_q * L and B * h_kv * L must each fit in 2^31 elements of d;
+ * for GQA_BF16 also L * h_kv * d * 2 (the bytes spanned by one sequence's
+ * key or value rows) must be below 2^32.  Larger calls return GQA_ERR_SIZE.
  */
 gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *o, int B, int L,
                        int h_q, int h_kv, int d, gqa_dtype dt, int causal, float scale,

@@ -60,6 +60,8 @@ def prefill_status(q=A, k=A, v=A, o=A, B=1, L=16, h_q=8, h_kv=2, d=64, dt=1, cau
     (dict(scale=0.0), SIZE), (dict(scale=-1.0), SIZE), (dict(scale=float("inf")), SIZE),
     (dict(scale=float("nan")), SIZE),
     (dict(B=1 << 16, L=1 << 14, h_q=16, h_kv=16), SIZE),
+    # one sequence's bf16 key rows would span 2^33 bytes (32-bit offsets)
+    (dict(B=1, L=1 << 20, h_q=32, h_kv=32, d=128), SIZE),
 ])
 def test_prefill_rejects_bad_arguments(kw, status):
     assert prefill_status(**kw) == status
