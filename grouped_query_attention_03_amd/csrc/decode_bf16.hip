@@ -31,8 +31,9 @@
 namespace gqa {
 namespace {
 
-constexpr int DC_THREADS = 256;
-constexpr int DC_WAVES = 4;
+constexpr int DC_WAVES = kDecodeWaves;      // waves per work-group of the split pass
+constexpr int DC_THREADS = 64 * DC_WAVES;
+constexpr int DC_LDS_BYTES = 160 * 1024;    // LDS of one CU
 constexpr int DC_BK = 32;          // keys per block
 constexpr float DC_TAU = 8.0f;     // lazy-rescale threshold, log2 units
 
@@ -163,20 +164,30 @@ __device__ __forceinline__ long long dc_slice_start(int w, long long T, int NW) 
     return (long long)w * T / NW;
 }
 
+// Ring depth per wave: as many (Q, K, V) slots as the CU's LDS holds for
+// DC_WAVES waves, at most 4, and few enough that the loads of the other slots
+// fit the 6-bit s_waitcnt vmcnt count.
+template <int D, int QD>
+constexpr int dc_slots() {
+    constexpr int per_slot = QD * 1024 + 2 * DcLayout<D>::TILE;
+    constexpr int ops = QD + 2 * DcLayout<D>::KV_DMA;
+    constexpr int by_lds = DC_LDS_BYTES / (DC_WAVES * per_slot);
+    constexpr int by_count = 63 / ops + 1;
+    return by_lds < by_count ? (by_lds < 4 ? by_lds : 4) : (by_count < 4 ? by_count : 4);
+}
+
 // QD = 1 KiB loads per block for the query tile (ceil(query heads x 2d / 1024)).
 template <int D, int QD>
 __global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs a) {
     using Lay = DcLayout<D>;
     constexpr int DB = D / 16;  // 16-wide blocks of the head dimension
     constexpr int OPS = QD + 2 * Lay::KV_DMA;  // memory instructions issued per block
-    // two slots per wave, each with its own Q, K and V tiles (separate arrays,
-    // so loads into one slot are visibly independent of reads from the other)
-    __shared__ __attribute__((aligned(1024))) char qA_s[DC_WAVES][QD * 1024];
-    __shared__ __attribute__((aligned(1024))) char kA_s[DC_WAVES][Lay::TILE];
-    __shared__ __attribute__((aligned(1024))) char vA_s[DC_WAVES][Lay::TILE];
-    __shared__ __attribute__((aligned(1024))) char qB_s[DC_WAVES][QD * 1024];
-    __shared__ __attribute__((aligned(1024))) char kB_s[DC_WAVES][Lay::TILE];
-    __shared__ __attribute__((aligned(1024))) char vB_s[DC_WAVES][Lay::TILE];
+    constexpr int DC_SLOTS = dc_slots<D, QD>();
+    static_assert(DC_SLOTS >= 2, "double buffering fits");
+    // a ring of DC_SLOTS slots per wave, each with its own Q, K and V tiles
+    __shared__ __attribute__((aligned(1024))) char q_s[DC_WAVES][DC_SLOTS][QD * 1024];
+    __shared__ __attribute__((aligned(1024))) char k_s[DC_WAVES][DC_SLOTS][Lay::TILE];
+    __shared__ __attribute__((aligned(1024))) char v_s[DC_WAVES][DC_SLOTS][Lay::TILE];
 
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int w = blockIdx.x * DC_WAVES + wave;
@@ -267,10 +278,10 @@ __global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs 
             l_run = 0.f;
             seg_open = true;
         }
-        // this slot's loads are complete once at most the OPS loads of the other
-        // slot (issued after them) are still in flight; stores issued in between
-        // only make the wait stricter
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(OPS) : "memory");
+        // this slot's loads are complete once at most the loads of the other
+        // DC_SLOTS - 1 slots (issued after them) are still in flight; stores
+        // issued in between only make the wait stricter
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DC_SLOTS - 1) * OPS) : "memory");
         dc_block<D, QD * Lay::ROWS_PER_DMA>(qt, kt, vt, DC_BK * cur.blk, load_const(a.seqlens, cur.b),
                     qcol < heads_in(cur), c, m_run, l_run, acc);
         --left;
@@ -284,14 +295,19 @@ __global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs 
         issue(nxt, qt, kt, vt);
     };
 
-    GQA_LDS char *qA = (GQA_LDS char *)qA_s[wave], *kA = (GQA_LDS char *)kA_s[wave], *vA = (GQA_LDS char *)vA_s[wave];
-    GQA_LDS char *qB = (GQA_LDS char *)qB_s[wave], *kB = (GQA_LDS char *)kB_s[wave], *vB = (GQA_LDS char *)vB_s[wave];
-    next_issue(qA, kA, vA);
+    // block i of the slice lives in slot i % DC_SLOTS; block i + DC_SLOTS - 1
+    // is issued into the slot of block i - 1, whose reads are complete
+    auto qs_ = [&](int i) { return (GQA_LDS char *)q_s[wave][i]; };
+    auto ks_ = [&](int i) { return (GQA_LDS char *)k_s[wave][i]; };
+    auto vs_ = [&](int i) { return (GQA_LDS char *)v_s[wave][i]; };
+#pragma unroll
+    for (int i = 0; i < DC_SLOTS - 1; ++i) next_issue(qs_(i), ks_(i), vs_(i));
+    int si = 0;  // slot of the block computed next
     while (left > 0) {
-        next_issue(qB, kB, vB);
-        step(qA, kA, vA);
-        next_issue(qA, kA, vA);
-        if (left > 0) step(qB, kB, vB);
+        const int sn = si == 0 ? DC_SLOTS - 1 : si - 1;
+        next_issue(qs_(sn), ks_(sn), vs_(sn));
+        step(qs_(si), ks_(si), vs_(si));
+        si = si + 1 == DC_SLOTS ? 0 : si + 1;
     }
 }
 
@@ -361,7 +377,7 @@ void launch_split(const DecodeArgs &a, hipStream_t stream) {
 int launch_decode_bf16(const DecodeArgs &a, int d, hipStream_t stream) {
     const int qh = a.G < 16 ? a.G : 16;  // query heads per subgroup
     const int qkib = (qh * 2 * d + 1023) / 1024;
-    dim3 grid2((a.B * a.h_q + 3) / 4), block(DC_THREADS);
+    dim3 grid2((a.B * a.h_q + 3) / 4), block(256);  // merge: one wave per (sequence, head)
     if (d == 128) {
         if (qkib <= 1) launch_split<128, 1>(a, stream);
         else if (qkib <= 2) launch_split<128, 2>(a, stream);

@@ -40,7 +40,7 @@ int heads_per_workgroup(int G) {
     return gw;
 }
 
-constexpr int kDefaultSplits = 1024;  // 256 CUs x 4 resident waves of the split pass
+constexpr int kDefaultSplits = 256 * gqa::kDecodeWaves;  // every wave of the split pass resident on 256 CUs
 constexpr int kMaxSplits = 1 << 20;
 
 bool splits_valid(int n) { return n >= 0 && n <= kMaxSplits; }

@@ -19,6 +19,10 @@ struct PrefillArgs {
     float c;       // scale * log2(e)
 };
 
+// Waves per work-group of the decode split pass; with one work-group per CU
+// resident (its LDS ring fills the CU), 256 CUs x kDecodeWaves waves run at once.
+constexpr int kDecodeWaves = 4;
+
 struct DecodeArgs {
     const void *q, *k_cache, *v_cache;
     const int32_t *seqlens;
