@@ -6,8 +6,10 @@
 
 Prints ONE JSON line on stdout.  A step is one call of the prefill entry point
 on the selected workload (default: the pages' worked example, B=32, L=1024,
-8 query heads over 4 key/value heads, d=64, bf16, non-causal).  K steps are
-timed back to back between two device synchronisations; ``value`` is the
+8 query heads over 4 key/value heads, d=64, bf16, non-causal).  Before the W warmup
+steps the same step runs untimed for --settle-seconds (default 0.5 s) so the GPU
+reaches its working clocks; then K steps are timed back to back between two
+device synchronisations; ``value`` is the
 algorithmic TFLOP/s of that timed region (4 * B * h_q * d * visible (query,
 key) pairs per step; causal counts L(L+1)/2 pairs per head).
 
@@ -120,7 +122,26 @@ def time_launches(fn, steps, before=None):
     return wall, [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
 
-def bench_prefill(w, steps, warmup):
+def settle_clocks(fn, seconds):
+    """Run fn() untimed for about `seconds` of wall time.
+
+    From idle, the GPU's power management takes tens of milliseconds of
+    sustained load to reach its working clocks (the worked-example prefill
+    runs at 154 us per launch for its first 25 launches and at 84 us after
+    about 300); the timed region measures the kernel at those clocks.
+    """
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        n += 10
+    return n
+
+
+def bench_prefill(w, steps, warmup, settle_s=0.0):
     import torch
     import gqa_workloads as wl
     import grouped_query_attention_03_amd as gqa
@@ -131,6 +152,7 @@ def bench_prefill(w, steps, warmup):
     def step():
         gqa.prefill(q, k, v, causal=w.causal, scale=w.scale, out=out)
 
+    settle_clocks(step, settle_s)
     for _ in range(warmup):
         step()
     wall, ev = time_launches(step, steps)
@@ -244,6 +266,8 @@ def main(argv=None):
                     choices=["none"] + [n for n in wl.WORKLOAD_ORDER
                                         if wl.WORKLOADS[n].path == "decode"])
     ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--settle-seconds", type=float, default=0.5,
+                    help="untimed runs of the step before the warmup, to reach working clocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args(argv)
@@ -264,7 +288,7 @@ def main(argv=None):
 
     w = wl.WORKLOADS[args.workload]
     log(f"prefill {w.name}: {w.description}; steps {args.steps} warmup {args.warmup}")
-    pf = bench_prefill(w, args.steps, args.warmup)
+    pf = bench_prefill(w, args.steps, args.warmup, args.settle_seconds)
     peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
     achieved = pf["flops_per_launch"] / (pf["kernel_ms_avg"] * 1e-3) / 1e12
     line = {
@@ -274,6 +298,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": args.settle_seconds,
         "ms_per_step": pf["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
