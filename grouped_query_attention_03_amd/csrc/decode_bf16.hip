@@ -164,6 +164,67 @@ __device__ __forceinline__ long long dc_slice_start(int w, long long T, int NW) 
     return (long long)w * T / NW;
 }
 
+// A wave-uniform 64-bit value held in vector registers, made scalar.
+__device__ __forceinline__ long long dc_uniform(long long x) {
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)(unsigned long long)x);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)x >> 32));
+    return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+__device__ __forceinline__ long long dc_wave_sum(long long x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+// Blocks of the whole list (T) and blocks of the sequences before `upto` (P),
+// one sequence per lane, 64 at a time.
+__device__ __forceinline__ void dc_block_totals(const int32_t *seqlens, int B, int segs_per_b,
+                                                int upto, long long &T, long long &P) {
+    const int lane = threadIdx.x & 63;
+    long long t = 0, p = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+        const int bb = b0 + lane;
+        if (bb < B) {
+            const long long n = (long long)((seqlens[bb] + DC_BK - 1) / DC_BK) * segs_per_b;
+            t += n;
+            if (bb < upto) p += n;
+        }
+    }
+    T = dc_uniform(dc_wave_sum(t));
+    P = dc_uniform(dc_wave_sum(p));
+}
+
+// The sequence whose segments hold global block `pos` (0 <= pos < T) and the
+// number of blocks before its first segment: an inclusive scan over 64
+// sequences at a time and a ballot.
+__device__ __forceinline__ void dc_locate(const int32_t *seqlens, int B, int segs_per_b,
+                                          long long pos, int &b_out, long long &cum_out) {
+    const int lane = threadIdx.x & 63;
+    long long base = 0;
+    b_out = B;
+    cum_out = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+        const int bb = b0 + lane;
+        const long long n =
+            bb < B ? (long long)((seqlens[bb] + DC_BK - 1) / DC_BK) * segs_per_b : 0;
+        long long incl = n;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const long long up = __shfl_up(incl, off);
+            if (lane >= off) incl += up;
+        }
+        const unsigned long long hit = __ballot(bb < B && pos < base + incl);
+        if (hit) {
+            const int l = __ffsll((long long)hit) - 1;
+            b_out = b0 + l;
+            cum_out = dc_uniform(base + __shfl(incl - n, l));
+            return;
+        }
+        base = dc_uniform(base + __shfl(incl, 63));
+    }
+}
+
 // Ring depth per wave: as many (Q, K, V) slots as the CU's LDS holds for
 // DC_WAVES waves, at most 4, and few enough that the loads of the other slots
 // fit the 6-bit s_waitcnt vmcnt count.
@@ -196,8 +257,8 @@ __global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs 
     const int segs_per_b = a.h_kv * a.n_qsub;
 
     // total blocks and this wave's slice
-    long long T = 0;
-    for (int b = 0; b < a.B; ++b) T += (long long)dc_nblk(a.seqlens, b) * segs_per_b;
+    long long T, unused;
+    dc_block_totals(a.seqlens, a.B, segs_per_b, 0, T, unused);
     const long long pos = dc_slice_start(w, T, a.NW);
     const long long end = dc_slice_start(w + 1, T, a.NW);
     if (pos >= end) return;
@@ -207,15 +268,12 @@ __global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs 
     };
     Cur cur{0, 0, 0};
     {
-        long long cum = 0;
-        for (int b = 0; b < a.B; ++b) {
-            const long long nb = dc_nblk(a.seqlens, b);
-            if (pos < cum + nb * segs_per_b) {
-                cur = Cur{b, (int)((pos - cum) / nb), (int)((pos - cum) % nb)};
-                break;
-            }
-            cum += nb * segs_per_b;
-        }
+        int b0;
+        long long cum;
+        dc_locate(a.seqlens, a.B, segs_per_b, pos, b0, cum);
+        b0 = __builtin_amdgcn_readfirstlane(b0);
+        const long long nb = dc_nblk(a.seqlens, b0);  // > 0: the block at pos lies in b0
+        cur = Cur{b0, (int)((pos - cum) / nb), (int)((pos - cum) % nb)};
     }
     const float c = a.c;
 
@@ -327,12 +385,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
         for (int e = 0; e < PER; ++e) op[e] = (__bf16)0.f;
         return;
     }
-    long long T = 0, P = 0;
-    for (int bb = 0; bb < a.B; ++bb) {
-        const long long n = (long long)dc_nblk(a.seqlens, bb) * segs_per_b;
-        if (bb < b) P += n;
-        T += n;
-    }
+    long long T, P;
+    dc_block_totals(a.seqlens, a.B, segs_per_b, b, T, P);
     const int seg_in_b = kvh * a.n_qsub + qs;
     P += (long long)seg_in_b * nb;  // first block of this segment
     const long long seg_global = (long long)b * segs_per_b + seg_in_b;
@@ -340,26 +394,57 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     int w0 = (int)min((long long)a.NW - 1, P * a.NW / T);
     while (w0 > 0 && dc_slice_start(w0, T, a.NW) > P) --w0;
     while (dc_slice_start(w0 + 1, T, a.NW) <= P) ++w0;
-    // lane j handles wave w0 + j (and + 64, ...)
-    float M = -INFINITY;
-    for (int w = w0 + lane; w < a.NW && dc_slice_start(w, T, a.NW) < P + nb; w += 64) {
-        if (dc_slice_start(w + 1, T, a.NW) > dc_slice_start(w, T, a.NW))
-            M = fmaxf(M, a.lse[((size_t)w + seg_global) * 16 + qcol]);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    // Rounds of 64 waves (one round unless more than 64 waves cover the
+    // segment): lane j holds the log-sum-exp of wave wb + j, or -inf for an
+    // empty slice or a wave past the segment; the partial rows of up to four
+    // waves are fetched together, then combined.
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    float wsum = 0.f;
-    for (int w = w0; w < a.NW && dc_slice_start(w, T, a.NW) < P + nb; ++w) {
-        if (dc_slice_start(w + 1, T, a.NW) <= dc_slice_start(w, T, a.NW)) continue;  // empty slice
-        const size_t slot = (size_t)w + seg_global;
-        const float f = fast_exp2(a.lse[slot * 16 + qcol] - M);
-        wsum += f;
-        const float *pp = a.opart + (slot * 16 + qcol) * D + PER * lane;
+    float wsum = 0.f, Mrun = -INFINITY;
+    const long long seg_end = P + nb;
+    for (int wb = w0; wb < a.NW && dc_slice_start(wb, T, a.NW) < seg_end; wb += 64) {
+        const int wl = wb + lane;
+        float lse_l = -INFINITY;
+        if (wl < a.NW && dc_slice_start(wl, T, a.NW) < seg_end &&
+            dc_slice_start(wl + 1, T, a.NW) > dc_slice_start(wl, T, a.NW))
+            lse_l = a.lse[((size_t)wl + seg_global) * 16 + qcol];
+        float M = lse_l;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(f, pp[e], acc[e]);
+        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        const float Mnew = fmaxf(Mrun, M);
+        if (Mrun != -INFINITY && Mnew > Mrun) {  // earlier rounds to the new max
+            const float sc = fast_exp2(Mrun - Mnew);
+            wsum *= sc;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] *= sc;
+        }
+        Mrun = Mnew;
+        const unsigned long long live = __ballot(lse_l != -INFINITY);
+        const int n_live = live ? 64 - __clzll((long long)live) : 0;  // highest live lane + 1
+        for (int u0 = 0; u0 < n_live; u0 += 4) {
+            float f[4], v[4][PER];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float lu = __shfl(lse_l, min(u0 + u, 63));
+                const bool ok = u0 + u < n_live && lu != -INFINITY;
+                f[u] = ok ? fast_exp2(lu - Mrun) : 0.f;
+#pragma unroll
+                for (int e = 0; e < PER; ++e) v[u][e] = 0.f;
+                if (ok) {
+                    const size_t slot = (size_t)(wb + u0 + u) + seg_global;
+                    const float *pp = a.opart + (slot * 16 + qcol) * D + PER * lane;
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) v[u][e] = pp[e];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                wsum += f[u];
+#pragma unroll
+                for (int e = 0; e < PER; ++e) acc[e] = fmaf(f[u], v[u][e], acc[e]);
+            }
+        }
     }
     const float inv = 1.f / wsum;
 #pragma unroll

@@ -238,6 +238,23 @@ def test_decode_matches_oracle(case, dev):
             assert torch.equal(out[b], torch.zeros_like(out[b]))
 
 
+def test_decode_many_sequences(dev):
+    # more sequences than one wave has lanes: the block-list totals and the
+    # per-wave start search run over several 64-sequence chunks
+    B, h_q, h_kv, S, d = 150, 8, 2, 160, 64
+    g = torch.Generator().manual_seed(77)
+    lens = torch.randint(0, S + 1, (B,), generator=g).to(torch.int32)
+    lens[[0, 63, 64, 65, 127, 128, 149]] = torch.tensor([0, S, 0, 1, 33, 0, S], dtype=torch.int32)
+    _, q, kc, vc = wl.decode_inputs(B, h_q, h_kv, S, d, 78, (1, S))
+    say(f"decode many sequences B={B}")
+    for splits in (0, 7, 300):
+        out = run_decode(lens, q, kc, vc, dev, splits=splits).cpu()
+        check(f64(out[:, 0]), decode_ref(lens, q, kc, vc), "bf16", f"decode B={B} splits={splits}")
+        for b in range(B):
+            if int(lens[b]) == 0:
+                assert torch.equal(out[b], torch.zeros_like(out[b]))
+
+
 def test_decode_split_count_does_not_change_the_result(dev):
     B, h_q, h_kv, S, d = 4, 32, 8, 3000, 128
     seqlens, q, kc, vc = wl.decode_inputs(B, h_q, h_kv, S, d, 41, (1, S))
