@@ -29,8 +29,9 @@
 //   row-major V tile with the transposing ds_read_b64_tr_b16.
 //
 // Schedule
-//   Two waves share each SIMD, so one wave's matrix products run while the
-//   other computes exponentials or waits for LDS.
+//   Two waves of a work-group share each SIMD (and at d = 64, where two
+//   work-groups fit in a CU's LDS and registers, four), so one wave's matrix
+//   products run while another computes exponentials or waits for LDS.
 //   K/V tiles move with direct buffer->LDS loads (waves 0-3 the K tile, waves
 //   4-7 the V tile) into a 4-slot ring: tile x is issued at the start of
 //   iteration x - 3 into slot x % 4, whose previous tile x - 4 was last read in
@@ -134,7 +135,10 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
     const int i0 = (wave % (PF_WAVES / 2)) * DPW;
     const unsigned krb = (unsigned)(a.h_kv * D * 2);  // key row stride, bytes
     // rows 0 .. L-1 of this (sequence, key/value head); L * krb < 2^32 is checked
-    // on the host.  Rows past the sequence end read as zeros.
+    // on the host.  Rows past the sequence end read as zeros; for the ragged
+    // last tile of a sequence spanning nearly 2^32 bytes a row offset may wrap,
+    // and then reads zeros or finite data of the same tensor, which the mask
+    // discards.
     const u32x4 rsrc = make_buffer_rsrc(
         static_cast<const __bf16 *>(loads_v ? a.v : a.k) + ((size_t)b * L * a.h_kv + kvh) * D,
         (unsigned)(L - 1) * krb + 2 * D);
