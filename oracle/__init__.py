@@ -62,6 +62,12 @@ def _load():
     lib.gqa_oracle_prefill_rows.argtypes = [P, P, ctypes.c_int64, P, P, I, I, I, I, I, I,
                                            ctypes.c_double, P, P]
     lib.gqa_oracle_prefill_rows.restype = I
+    lib.gqa_oracle_prefill_cached.argtypes = [P, P, P, P, I, I, I, I, I, I, I,
+                                              ctypes.c_double, P]
+    lib.gqa_oracle_prefill_cached.restype = I
+    lib.gqa_oracle_prefill_cached_rows.argtypes = [P, P, ctypes.c_int64, P, P, I, I, I, I, I,
+                                                   I, I, ctypes.c_double, P]
+    lib.gqa_oracle_prefill_cached_rows.restype = I
     lib.gqa_oracle_decode.argtypes = [P, P, P, P, P, I, I, I, I, I]
     lib.gqa_oracle_decode.restype = I
     lib.gqa_oracle_num_threads.argtypes = []
@@ -123,6 +129,46 @@ def prefill_rows(q_rows, rows_bih, k, v, h_q: int, causal: bool, scale: float):
                                          _ptr(out), None)
     if rc != 0:
         raise ValueError("oracle prefill_rows rejected its arguments (rc=%d)" % rc)
+    return out
+
+
+def prefill_cached(q, k, v, causal: bool, scale: float, return_probs: bool = False):
+    """Prefill of L_q new positions against L_k keys (1 <= L_q <= L_k).
+
+    q [B,L_q,h_q,d], k/v [B,L_k,h_kv,d] -> o [B,L_q,h_q,d] (float64).  Query
+    row i sits at position L_k - L_q + i, so causally it sees keys
+    0 .. L_k - L_q + i.  With ``return_probs`` also returns [B, h_q, L_q, L_k].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Lq, h_q, d = q.shape
+    Lk, h_kv = k.shape[1], k.shape[2]
+    if k.shape != (B, Lk, h_kv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, L_k, h_kv, d] matching q")
+    o = np.empty_like(q)
+    probs = np.empty((B, h_q, Lq, Lk)) if return_probs else None
+    rc = _load().gqa_oracle_prefill_cached(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Lq, Lk, h_q,
+                                           h_kv, d, int(bool(causal)), float(scale),
+                                           _ptr(probs) if probs is not None else None)
+    if rc != 0:
+        raise ValueError("oracle prefill_cached rejected its arguments (rc=%d)" % rc)
+    return (o, probs) if return_probs else o
+
+
+def prefill_cached_rows(q_rows, rows_bih, k, v, h_q: int, Lq: int, causal: bool, scale: float):
+    """prefill_cached output of selected rows (b, i, h), 0 <= i < Lq; returns [n, d]."""
+    q_rows = _f64(q_rows)
+    rows = np.ascontiguousarray(np.asarray(rows_bih, dtype=np.int64).reshape(-1, 3))
+    k, v = _f64(k), _f64(v)
+    B, Lk, h_kv, d = k.shape
+    n = rows.shape[0]
+    if q_rows.shape != (n, d):
+        raise ValueError("q_rows must be [n, d]")
+    out = np.empty((n, d))
+    rc = _load().gqa_oracle_prefill_cached_rows(_ptr(q_rows), _ptr(rows), n, _ptr(k), _ptr(v),
+                                                B, Lq, Lk, h_q, h_kv, d, int(bool(causal)),
+                                                float(scale), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle prefill_cached_rows rejected its arguments (rc=%d)" % rc)
     return out
 
 

@@ -55,6 +55,27 @@ def prefill(q, k, v, causal, scale):
     return o, probs
 
 
+def prefill_cached(q, k, v, causal, scale):
+    """q [B][Lq][h_q][d], k/v [B][Lk][h_kv][d] -> o [B][Lq][h_q][d]; query row i is
+    position Lk - Lq + i (the Lq newest of Lk positions)."""
+    B, Lq, h_q = len(q), len(q[0]), len(q[0][0])
+    Lk, h_kv = len(k[0]), len(k[0][0])
+    if h_q % h_kv or Lq > Lk:
+        raise ValueError("need h_q a multiple of h_kv and Lq <= Lk")
+    G = h_q // h_kv
+    o = [[[None] * h_q for _ in range(Lq)] for _ in range(B)]
+    for b in range(B):
+        for h in range(h_q):
+            g = h // G
+            for i in range(Lq):
+                pos = Lk - Lq + i
+                last = pos + 1 if causal else Lk
+                out, _ = _softmax_average(q[b][i][h], [k[b][j][g] for j in range(last)],
+                                          [v[b][j][g] for j in range(last)], scale)
+                o[b][i][h] = out
+    return o
+
+
 def decode(q, k_cache, v_cache, seqlens):
     """q [B][h_q][d], caches [B][h_kv][S][d], seqlens [B] -> o [B][h_q][d]."""
     B, h_q, d = len(q), len(q[0]), len(q[0][0])

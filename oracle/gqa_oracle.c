@@ -25,6 +25,16 @@
  *   Causal masking keeps key j for query i iff j <= i (square alignment; the
  *   masked_fill(mask == 0, -inf) convention of the same page, §2.1-§2.3).
  *
+ *   Prefill against existing keys (chunked prefill): L_q new positions whose
+ *   keys and values were appended after L_k - L_q earlier ones attend to all
+ *   L_k keys of their sequence ("What is Grouped-Query Attention", §3.2:
+ *   append to the cache, then attend).  Query row i of the chunk sits at
+ *   position L_k - L_q + i, so causally it sees keys 0 .. L_k - L_q + i
+ *   (bottom-right alignment; L_q == L_k is the square case above).  Run chunk
+ *   by chunk this reproduces one full causal prefill, which processing each
+ *   chunk on its own ("Implementing GQA from scratch in PyTorch", §4.3) does
+ *   not.
+ *
  *   Decode: one new query token per sequence attends over the cache rows
  *   [0, seqlens[b]) of a head-major cache [B, h_kv, S, d]
  *   ("What is Grouped-Query Attention", §2.2 step 2 for the cache layout and
@@ -116,27 +126,29 @@ static int check_heads(int h_q, int h_kv) {
 }
 
 /*
- * Prefill for a list of query rows.
+ * Prefill for a list of query rows against L_k keys per sequence.
  *   q_rows  [n_rows][d]   the query vectors of the listed rows
- *   row_bih [n_rows][3]   (b, i, h) of each listed row
- *   k, v    [B][L][h_kv][d]
+ *   row_bih [n_rows][3]   (b, i, h) of each listed row, 0 <= i < L_q
+ *   k, v    [B][L_k][h_kv][d]
  *   out     [n_rows][d]
- *   probs   NULL, or [n_rows][L]: the softmax row (zeros beyond the visible keys)
- * Rows are processed in groups that share (b, h) so the repeated slab of their
- * head is built once per group; rows must be sorted by (b, h) for that to help,
- * but any order is correct.
+ *   probs   NULL, or [n_rows][L_k]: the softmax row (zeros beyond the visible keys)
+ * Query row i sits at position L_k - L_q + i (1 <= L_q <= L_k).  Rows are
+ * processed in groups that share (b, h) so the repeated slab of their head is
+ * built once per group; rows must be sorted by (b, h) for that to help, but
+ * any order is correct.
  */
-int gqa_oracle_prefill_rows(const double *q_rows, const int64_t *row_bih, int64_t n_rows,
-                            const double *k, const double *v, int B, int L, int h_q,
-                            int h_kv, int d, int causal, double scale, double *out,
-                            double *probs) {
-    if (B <= 0 || L <= 0 || d <= 0 || n_rows < 0) return ORACLE_ERR_ARG;
+static int prefill_rows_general(const double *q_rows, const int64_t *row_bih, int64_t n_rows,
+                                const double *k, const double *v, int B, int Lq, int Lk,
+                                int h_q, int h_kv, int d, int causal, double scale,
+                                double *out, double *probs) {
+    if (B <= 0 || Lq <= 0 || Lk < Lq || d <= 0 || n_rows < 0) return ORACLE_ERR_ARG;
     if (check_heads(h_q, h_kv)) return ORACLE_ERR_ARG;
     for (int64_t r = 0; r < n_rows; ++r) {
         int64_t b = row_bih[3 * r], i = row_bih[3 * r + 1], h = row_bih[3 * r + 2];
-        if (b < 0 || b >= B || i < 0 || i >= L || h < 0 || h >= h_q) return ORACLE_ERR_ARG;
+        if (b < 0 || b >= B || i < 0 || i >= Lq || h < 0 || h >= h_q) return ORACLE_ERR_ARG;
     }
-    const long sh = d, sj = (long)h_kv * d, sb = (long)L * sj;
+    const long sh = d, sj = (long)h_kv * d, sb = (long)Lk * sj;
+    const int first = Lk - Lq; /* position of query row 0 */
 
     /* Split the row list into runs of equal (b, h). */
     int64_t *run_start = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_rows + 1));
@@ -152,9 +164,9 @@ int gqa_oracle_prefill_rows(const double *q_rows, const int64_t *row_bih, int64_
     int failed = 0;
 #pragma omp parallel
     {
-        double *krep = (double *)malloc(sizeof(double) * (size_t)L * d);
-        double *vrep = (double *)malloc(sizeof(double) * (size_t)L * d);
-        double *scores = (double *)malloc(sizeof(double) * (size_t)L);
+        double *krep = (double *)malloc(sizeof(double) * (size_t)Lk * d);
+        double *vrep = (double *)malloc(sizeof(double) * (size_t)Lk * d);
+        double *scores = (double *)malloc(sizeof(double) * (size_t)Lk);
         if (!krep || !vrep || !scores) {
 #pragma omp atomic write
             failed = 1;
@@ -165,15 +177,15 @@ int gqa_oracle_prefill_rows(const double *q_rows, const int64_t *row_bih, int64_
                 int b = (int)row_bih[3 * r0], h = (int)row_bih[3 * r0 + 2];
                 int kvh = kv_head_of(h, h_q, h_kv);
                 /* explicit repeat of this head's keys and values */
-                repeat_kv_slab(k, sb, sj, sh, b, kvh, L, d, krep);
-                repeat_kv_slab(v, sb, sj, sh, b, kvh, L, d, vrep);
+                repeat_kv_slab(k, sb, sj, sh, b, kvh, Lk, d, krep);
+                repeat_kv_slab(v, sb, sj, sh, b, kvh, Lk, d, vrep);
                 for (int64_t r = r0; r < r1; ++r) {
                     int i = (int)row_bih[3 * r + 1];
-                    int n_vis = causal ? i + 1 : L;
+                    int n_vis = causal ? first + i + 1 : Lk;
                     double *prow = NULL;
                     if (probs) {
-                        prow = probs + r * (int64_t)L;
-                        for (int j = 0; j < L; ++j) prow[j] = 0.0;
+                        prow = probs + r * (int64_t)Lk;
+                        for (int j = 0; j < Lk; ++j) prow[j] = 0.0;
                     }
                     attend_one_row(q_rows + r * (int64_t)d, krep, vrep, n_vis, d, scale,
                                    scores, out + r * (int64_t)d, prow);
@@ -188,16 +200,35 @@ int gqa_oracle_prefill_rows(const double *q_rows, const int64_t *row_bih, int64_
     return failed ? ORACLE_ERR_NOMEM : 0;
 }
 
+/* Square prefill rows: L_q == L_k == L (see prefill_rows_general). */
+int gqa_oracle_prefill_rows(const double *q_rows, const int64_t *row_bih, int64_t n_rows,
+                            const double *k, const double *v, int B, int L, int h_q,
+                            int h_kv, int d, int causal, double scale, double *out,
+                            double *probs) {
+    return prefill_rows_general(q_rows, row_bih, n_rows, k, v, B, L, L, h_q, h_kv, d, causal,
+                                scale, out, probs);
+}
+
+/* Rows of a prefill against L_k keys, L_q new positions (see prefill_rows_general). */
+int gqa_oracle_prefill_cached_rows(const double *q_rows, const int64_t *row_bih,
+                                   int64_t n_rows, const double *k, const double *v, int B,
+                                   int Lq, int Lk, int h_q, int h_kv, int d, int causal,
+                                   double scale, double *out) {
+    return prefill_rows_general(q_rows, row_bih, n_rows, k, v, B, Lq, Lk, h_q, h_kv, d, causal,
+                                scale, out, NULL);
+}
+
 /*
- * Full prefill:  q, o [B][L][h_q][d];  k, v [B][L][h_kv][d].
- * probs: NULL, or [B][h_q][L][L] softmax matrices (zeros where masked).
+ * Full prefill of L_q positions against L_k keys per sequence:
+ *   q, o [B][L_q][h_q][d];  k, v [B][L_k][h_kv][d].
+ * probs: NULL, or [B][h_q][L_q][L_k] softmax matrices (zeros where masked).
  */
-int gqa_oracle_prefill(const double *q, const double *k, const double *v, double *o, int B,
-                       int L, int h_q, int h_kv, int d, int causal, double scale,
-                       double *probs) {
-    if (B <= 0 || L <= 0 || d <= 0) return ORACLE_ERR_ARG;
+static int prefill_general(const double *q, const double *k, const double *v, double *o, int B,
+                           int Lq, int Lk, int h_q, int h_kv, int d, int causal, double scale,
+                           double *probs) {
+    if (B <= 0 || Lq <= 0 || Lk < Lq || d <= 0) return ORACLE_ERR_ARG;
     if (check_heads(h_q, h_kv)) return ORACLE_ERR_ARG;
-    int64_t n = (int64_t)B * h_q * L;
+    int64_t n = (int64_t)B * h_q * Lq;
     int64_t *bih = (int64_t *)malloc(sizeof(int64_t) * 3 * (size_t)n);
     double *qr = (double *)malloc(sizeof(double) * (size_t)(n * d));
     double *orow = (double *)malloc(sizeof(double) * (size_t)(n * d));
@@ -211,27 +242,48 @@ int gqa_oracle_prefill(const double *q, const double *k, const double *v, double
     int64_t r = 0;
     for (int b = 0; b < B; ++b)
         for (int h = 0; h < h_q; ++h)
-            for (int i = 0; i < L; ++i, ++r) {
+            for (int i = 0; i < Lq; ++i, ++r) {
                 bih[3 * r] = b;
                 bih[3 * r + 1] = i;
                 bih[3 * r + 2] = h;
-                memcpy(qr + r * d, q + (((int64_t)b * L + i) * h_q + h) * d,
+                memcpy(qr + r * d, q + (((int64_t)b * Lq + i) * h_q + h) * d,
                        sizeof(double) * (size_t)d);
             }
-    int rc = gqa_oracle_prefill_rows(qr, bih, n, k, v, B, L, h_q, h_kv, d, causal, scale,
-                                     orow, probs);
+    int rc = prefill_rows_general(qr, bih, n, k, v, B, Lq, Lk, h_q, h_kv, d, causal, scale,
+                                  orow, probs);
     if (rc == 0) {
         r = 0;
         for (int b = 0; b < B; ++b)
             for (int h = 0; h < h_q; ++h)
-                for (int i = 0; i < L; ++i, ++r)
-                    memcpy(o + (((int64_t)b * L + i) * h_q + h) * d, orow + r * d,
+                for (int i = 0; i < Lq; ++i, ++r)
+                    memcpy(o + (((int64_t)b * Lq + i) * h_q + h) * d, orow + r * d,
                            sizeof(double) * (size_t)d);
     }
     free(bih);
     free(qr);
     free(orow);
     return rc;
+}
+
+/*
+ * Full prefill:  q, o [B][L][h_q][d];  k, v [B][L][h_kv][d].
+ * probs: NULL, or [B][h_q][L][L] softmax matrices (zeros where masked).
+ */
+int gqa_oracle_prefill(const double *q, const double *k, const double *v, double *o, int B,
+                       int L, int h_q, int h_kv, int d, int causal, double scale,
+                       double *probs) {
+    return prefill_general(q, k, v, o, B, L, L, h_q, h_kv, d, causal, scale, probs);
+}
+
+/*
+ * Prefill of L_q new positions against L_k keys (chunked prefill):
+ *   q, o [B][L_q][h_q][d];  k, v [B][L_k][h_kv][d];  1 <= L_q <= L_k.
+ * probs: NULL, or [B][h_q][L_q][L_k].
+ */
+int gqa_oracle_prefill_cached(const double *q, const double *k, const double *v, double *o,
+                              int B, int Lq, int Lk, int h_q, int h_kv, int d, int causal,
+                              double scale, double *probs) {
+    return prefill_general(q, k, v, o, B, Lq, Lk, h_q, h_kv, d, causal, scale, probs);
 }
 
 /*

@@ -287,10 +287,78 @@ def pin_argument_errors():
         raise AssertionError("h_q % h_kv != 0 must be rejected")
 
 
+# ------------------------------------------------- prefill against cached keys
+
+def pin_chunk_golden():
+    """Hand-derived 2-of-3 case: bottom-right causal alignment, closed forms."""
+    g = _golden("chunk_2_of_3.json")
+    q, k, v = np.array(g["q"]), np.array(g["k"]), np.array(g["v"])
+    for causal, key in ((True, "expected_causal"), (False, "expected_noncausal")):
+        _close(oracle.prefill_cached(q, k, v, causal, g["scale"]), g[key], g["tolerance"],
+               f"chunk golden causal={causal}")
+        _close(brute.prefill_cached(q.tolist(), k.tolist(), v.tolist(), causal, g["scale"]),
+               g[key], g["tolerance"], f"brute chunk golden causal={causal}")
+
+
+def pin_chunked_equals_full():
+    """Chunk by chunk against the growing key set == one full prefill, row for row."""
+    B, L, h_q, h_kv, d = 2, 37, 4, 2, 8
+    q, k, v = _rand((B, L, h_q, d), 110), _rand((B, L, h_kv, d), 111), _rand((B, L, h_kv, d), 112)
+    scale = 1 / math.sqrt(d)
+    full = oracle.prefill(q, k, v, causal=True, scale=scale)
+    for c0, c1 in ((0, 10), (10, 11), (11, 30), (30, 37)):
+        part = oracle.prefill_cached(q[:, c0:c1], k[:, :c1], v[:, :c1], True, scale)
+        _close(part, full[:, c0:c1], 1e-13, f"causal chunk [{c0},{c1}) vs full prefill")
+    full_nc = oracle.prefill(q, k, v, causal=False, scale=scale)
+    part = oracle.prefill_cached(q[:, 5:9], k, v, False, scale)
+    _close(part, full_nc[:, 5:9], 1e-13, "non-causal rows against all keys vs full prefill")
+
+
+def pin_chunk_single_query_is_decode():
+    """One new query against n keys == decode over a cache of n rows."""
+    B, n, h_q, h_kv, d = 3, 9, 8, 2, 16
+    q, k, v = _rand((B, 1, h_q, d), 120), _rand((B, n, h_kv, d), 121), _rand((B, n, h_kv, d), 122)
+    o = oracle.prefill_cached(q, k, v, True, 1 / math.sqrt(d))
+    kc = np.ascontiguousarray(k.transpose(0, 2, 1, 3))
+    vc = np.ascontiguousarray(v.transpose(0, 2, 1, 3))
+    _close(o[:, 0], oracle.decode(q[:, 0], kc, vc, [n] * B), 1e-13, "L_q = 1 vs decode")
+
+
+def pin_chunk_brute_and_library():
+    """Random tiny shapes: the brute force, and fp64 SDPA with a bottom-right mask."""
+    B, Lq, Lk, h_q, h_kv, d = 2, 3, 7, 4, 2, 5
+    q, k, v = _rand((B, Lq, h_q, d), 130), _rand((B, Lk, h_kv, d), 131), _rand((B, Lk, h_kv, d), 132)
+    for causal in (True, False):
+        o = oracle.prefill_cached(q, k, v, causal, 0.4)
+        _close(o, brute.prefill_cached(q.tolist(), k.tolist(), v.tolist(), causal, 0.4), 1e-12,
+               f"chunk vs brute causal={causal}")
+        mask = None
+        if causal:  # key j visible to row i iff j <= Lk - Lq + i
+            mask = torch.tensor([[j <= Lk - Lq + i for j in range(Lk)] for i in range(Lq)])
+        tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+        tk = torch.from_numpy(k).permute(0, 2, 1, 3)
+        tv = torch.from_numpy(v).permute(0, 2, 1, 3)
+        ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.4,
+                                             enable_gqa=True).permute(0, 2, 1, 3).numpy()
+        _close(o, ref, 1e-12, f"chunk vs SDPA causal={causal}")
+
+
+def pin_chunk_rows_match_full():
+    B, Lq, Lk, h_q, h_kv, d = 2, 5, 11, 4, 1, 3
+    q, k, v = _rand((B, Lq, h_q, d), 140), _rand((B, Lk, h_kv, d), 141), _rand((B, Lk, h_kv, d), 142)
+    full = oracle.prefill_cached(q, k, v, True, 0.7)
+    rows = [(1, 4, 3), (0, 0, 0), (1, 2, 1)]
+    qr = np.array([q[b, i, h] for b, i, h in rows])
+    out = oracle.prefill_cached_rows(qr, rows, k, v, h_q, Lq, True, 0.7)
+    _close(out, np.array([full[b, i, h] for b, i, h in rows]), 0.0, "chunk rows vs full")
+
+
 ALL_PINS = [pin_hand_2x2, pin_head_map, pin_decode_golden, pin_mha_reduction,
             pin_mqa_reduction, pin_gqa_library, pin_rows_sum_to_one, pin_k_zero_mean,
             pin_causal_row0, pin_identical_heads, pin_invariances, pin_cross_path,
-            pin_rows_match_full, pin_decode_tail_ignored, pin_argument_errors]
+            pin_rows_match_full, pin_decode_tail_ignored, pin_argument_errors,
+            pin_chunk_golden, pin_chunked_equals_full, pin_chunk_single_query_is_decode,
+            pin_chunk_brute_and_library, pin_chunk_rows_match_full]
 
 
 def main(argv):

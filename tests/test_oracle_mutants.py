@@ -18,11 +18,14 @@ SRC = os.path.join(ROOT, "oracle", "gqa_oracle.c")
 MUTANTS = {
     "modulo_head_map": ("return h / group_size;", "return h % h_kv;"),
     "scale_dropped": ("scores[j] = scale * dot;", "scores[j] = dot;"),
-    "causal_off_by_one": ("int n_vis = causal ? i + 1 : L;", "int n_vis = causal ? i : L;"),
+    "causal_off_by_one": ("int n_vis = causal ? first + i + 1 : Lk;",
+                          "int n_vis = causal ? first + i : Lk;"),
+    "top_left_alignment": ("int n_vis = causal ? first + i + 1 : Lk;",
+                           "int n_vis = causal ? i + 1 : Lk;"),
     "softmax_sign": ("scores[j] = exp(scores[j] - m);", "scores[j] = exp(m - scores[j]);"),
     "no_normalisation": ("double p = scores[j] / z;", "double p = scores[j];"),
-    "k_v_swapped": ("repeat_kv_slab(k, sb, sj, sh, b, kvh, L, d, krep);",
-                    "repeat_kv_slab(v, sb, sj, sh, b, kvh, L, d, krep);"),
+    "k_v_swapped": ("repeat_kv_slab(k, sb, sj, sh, b, kvh, Lk, d, krep);",
+                    "repeat_kv_slab(v, sb, sj, sh, b, kvh, Lk, d, krep);"),
     "transposed_key_index": ("dot += q[c] * krep[(long)j * d + c];",
                              "dot += q[c] * krep[(long)c * n_vis + j];"),
     "decode_reads_whole_cache": ("int n = seqlens[b];", "int n = S;"),
