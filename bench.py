@@ -58,9 +58,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def visible_pairs(Lq: int, Lk: int, causal: bool) -> int:
+    """(query, key) pairs that take part: the Lq newest of Lk positions, causal or not."""
+    if not causal:
+        return Lq * Lk
+    first = Lk - Lq  # query row i sees keys 0 .. first + i
+    return Lq * (first + 1) + Lq * (Lq - 1) // 2
+
+
 def prefill_flops(w) -> float:
-    pairs = w.L * (w.L + 1) // 2 if w.causal else w.L * w.L
-    return 4.0 * w.B * w.h_q * w.d * pairs
+    Lk = w.Lk if w.path == "prefill_chunk" else w.L
+    return 4.0 * w.B * w.h_q * w.d * visible_pairs(w.L, Lk, w.causal)
 
 
 def decode_kv_bytes(w, seqlens) -> float:
@@ -149,8 +157,10 @@ def bench_prefill(w, steps, warmup, settle_s=0.0):
     q, k, v = (t.to(dev) for t in wl.workload_inputs(w))
     out = torch.empty_like(q)
 
+    call = gqa.prefill_chunk if w.path == "prefill_chunk" else gqa.prefill
+
     def step():
-        gqa.prefill(q, k, v, causal=w.causal, scale=w.scale, out=out)
+        call(q, k, v, causal=w.causal, scale=w.scale, out=out)
 
     settle_clocks(step, settle_s)
     for _ in range(warmup):
@@ -224,6 +234,9 @@ def cpu_baseline(w, budget_s=12.0):
     q, k, v = wl.workload_inputs(w)
     qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
 
+    if w.path == "prefill_chunk":
+        return _cpu_baseline_chunk(w, qd, kd, vd, budget_s)
+
     def run(nb):
         t0 = time.perf_counter()
         oracle.prefill(qd[:nb], kd[:nb], vd[:nb], causal=w.causal, scale=w.scale)
@@ -240,6 +253,27 @@ def cpu_baseline(w, budget_s=12.0):
             "cores": oracle.num_threads(), "kind": "oracle", "seconds": total,
             "sample": f"{nb} of {w.B} batch elements of {w.name} (all {w.h_q} heads x {w.L} "
                       f"positions each), run {reps} time(s), fp64"}
+
+
+def _cpu_baseline_chunk(w, qd, kd, vd, budget_s):
+    """The oracle on the newest m query rows of the chunk against all L_k keys
+    (the same form of work), m sized to about budget_s seconds."""
+    import oracle
+
+    def run(m):
+        t0 = time.perf_counter()
+        oracle.prefill_cached(qd[:1, -m:], kd[:1], vd[:1], causal=w.causal, scale=w.scale)
+        return time.perf_counter() - t0
+
+    m0 = min(16, w.L)
+    t1 = run(m0)
+    m = int(max(m0, min(w.L, round(m0 * budget_s / max(t1, 1e-3)))))
+    t = run(m) if m != m0 else t1
+    flops = 4.0 * w.h_q * w.d * visible_pairs(m, w.Lk, w.causal)
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": t,
+            "sample": f"the newest {m} of the {w.L} query positions of one sequence of {w.name} "
+                      f"against all {w.Lk} keys, all {w.h_q} heads, fp64"}
 
 
 def copy_calibration():
@@ -261,7 +295,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="worked_example_prefill_bf16",
-                    choices=[n for n in wl.WORKLOAD_ORDER if wl.WORKLOADS[n].path == "prefill"])
+                    choices=[n for n in wl.WORKLOAD_ORDER
+                             if wl.WORKLOADS[n].path in ("prefill", "prefill_chunk")])
     ap.add_argument("--decode-workload", default="batched_decode_bf16",
                     choices=["none"] + [n for n in wl.WORKLOAD_ORDER
                                         if wl.WORKLOADS[n].path == "decode"])
@@ -305,7 +340,7 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic: seeded i.i.d. normal draws cast to the compute dtype (no dataset)",
-        "config": {"workload": w.name, "path": "prefill", "B": w.B, "L": w.L, "h_q": w.h_q,
+        "config": {"workload": w.name, "path": w.path, "B": w.B, "L": w.L, "h_q": w.h_q,
                    "h_kv": w.h_kv, "d": w.d, "causal": w.causal, "scale": w.scale,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": achieved,
@@ -313,6 +348,8 @@ def main(argv=None):
                      "traffic": recorded_traffic("prefill", w.name),
                      "kernel_ms_avg": pf["kernel_ms_avg"], "kernel_ms_min": pf["kernel_ms_min"]},
     }
+    if w.path == "prefill_chunk":
+        line["config"]["L_k"] = w.Lk
     log(f"prefill: {pf['value']:.1f} TFLOP/s wall, kernel avg {pf['kernel_ms_avg']:.4f} ms "
         f"({achieved:.1f} TFLOP/s, {100 * achieved / peak:.1f}% of peak)")
     if args.decode_workload != "none":

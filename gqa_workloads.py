@@ -13,6 +13,11 @@ Recipe (one fixed rule for every workload):
 * a standard deviation other than 1 is applied in float32 before the cast;
 * the cast to bfloat16 is torch's round-to-nearest-even.
 
+The chunked prefill runs the last 2048 of 32768 positions of the 64/8-head
+shape against all 32768 keys, the exact form of processing a long sequence
+chunk by chunk ("Implementing GQA from scratch", §4.3; "What is Grouped-Query
+Attention", §3.2).
+
 Shapes follow the pages' workloads: the worked example of "Implementing GQA
 from scratch" (§5: B=32, L=1024, 8 heads, d_model=512, 4 key/value heads), the
 Llama-2-7B style 32/8 head split with d=128 ("What is Grouped-Query
@@ -31,13 +36,14 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    path: str  # "prefill" or "decode"
+    path: str  # "prefill", "prefill_chunk" or "decode"
     dtype: str  # "f32" or "bf16"
     B: int
     h_q: int
     h_kv: int
     d: int
-    L: int = 1  # prefill sequence length
+    L: int = 1  # prefill sequence length (prefill_chunk: the new positions L_q)
+    Lk: int = 0  # prefill_chunk: keys per sequence L_k (the new positions are the last L_q)
     S: int = 0  # decode cache capacity
     causal: bool = False
     std: float = 1.0
@@ -78,11 +84,17 @@ WORKLOADS = {
         "long_context_prefill_bf16", "prefill", "bf16", B=1, L=32768, h_q=64, h_kv=8, d=128,
         causal=True, std=1.0 / math.sqrt(2.0), seed=5,
         description="bf16 causal prefill, B=1 L=32768 h_q=64 h_kv=8 d=128"),
+    "chunked_prefill_bf16": Workload(
+        "chunked_prefill_bf16", "prefill_chunk", "bf16", B=1, L=2048, Lk=32768, h_q=64, h_kv=8,
+        d=128, causal=True, std=1.0 / math.sqrt(2.0), seed=6,
+        description="bf16 causal chunked prefill: the last 2048 of 32768 positions, "
+                    "B=1 h_q=64 h_kv=8 d=128"),
 }
 
-# Order in which the five workloads are listed everywhere.
+# Order in which the workloads are listed everywhere: the five of the core
+# path, then the chunked prefill against existing keys.
 WORKLOAD_ORDER = ["tiny_prefill_f32", "worked_example_prefill_bf16", "llama2_7b_prefill_bf16",
-                  "batched_decode_bf16", "long_context_prefill_bf16"]
+                  "batched_decode_bf16", "long_context_prefill_bf16", "chunked_prefill_bf16"]
 
 
 def _draw(gen, shape, std, dtype):
@@ -101,6 +113,15 @@ def prefill_inputs(B, L, h_q, h_kv, d, seed, std=1.0, dtype=torch.bfloat16):
     return q, k, v
 
 
+def prefill_chunk_inputs(B, Lq, Lk, h_q, h_kv, d, seed, std=1.0, dtype=torch.bfloat16):
+    """Seeded CPU tensors q [B,Lq,h_q,d] (the last Lq positions), k, v [B,Lk,h_kv,d]."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    q = _draw(gen, (B, Lq, h_q, d), std, dtype)
+    k = _draw(gen, (B, Lk, h_kv, d), std, dtype)
+    v = _draw(gen, (B, Lk, h_kv, d), std, dtype)
+    return q, k, v
+
+
 def decode_inputs(B, h_q, h_kv, S, d, seed, seqlen_range, std=1.0, dtype=torch.bfloat16):
     """Seeded CPU tensors: seqlens [B] int32, q [B,1,h_q,d], k_cache, v_cache [B,h_kv,S,d]."""
     lo, hi = seqlen_range
@@ -116,6 +137,9 @@ def workload_inputs(w: Workload):
     """Inputs of a named workload, as CPU tensors (see prefill_inputs/decode_inputs)."""
     if w.path == "prefill":
         return prefill_inputs(w.B, w.L, w.h_q, w.h_kv, w.d, w.seed, w.std, w.torch_dtype())
+    if w.path == "prefill_chunk":
+        return prefill_chunk_inputs(w.B, w.L, w.Lk, w.h_q, w.h_kv, w.d, w.seed, w.std,
+                                    w.torch_dtype())
     return decode_inputs(w.B, w.h_q, w.h_kv, w.S, w.d, w.seed, w.seqlen_range, w.std,
                          w.torch_dtype())
 

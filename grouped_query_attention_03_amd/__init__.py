@@ -9,6 +9,10 @@ the device is not a gfx950 GPU, the calls raise.
         q [B, L, h_q, d], k/v [B, L, h_kv, d] (bf16 or fp32, contiguous, on the
         GPU) -> o [B, L, h_q, d].  Query head h reads key/value head
         h // (h_q // h_kv).
+    prefill_chunk(q, k, v, causal=..., scale=None, out=None)
+        q [B, L_q, h_q, d] against k/v [B, L_k, h_kv, d] (L_q <= L_k): the L_q
+        newest positions attend to all L_k keys (causally, row i sees keys
+        0 .. L_k - L_q + i).
     decode(q, k_cache, v_cache, seqlens, out=None, workspace=None, num_splits=0)
         q [B, 1, h_q, d] bf16, caches [B, h_kv, S, d] bf16, seqlens [B] int32
         -> o [B, 1, h_q, d].
@@ -50,6 +54,8 @@ def lib() -> ctypes.CDLL:
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     L.gqa_prefill.argtypes = [P, P, P, P, I, I, I, I, I, I, I, F, P]
     L.gqa_prefill.restype = I
+    L.gqa_prefill_chunk.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, F, P]
+    L.gqa_prefill_chunk.restype = I
     L.gqa_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, ctypes.c_size_t, P]
     L.gqa_decode.restype = I
     L.gqa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -111,6 +117,35 @@ def prefill(q, k, v, *, causal: bool, scale: float | None = None, out=None):
                            h_kv, d, _dtype_code(q), int(bool(causal)), float(scale), _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_prefill")
+    return out
+
+
+def prefill_chunk(q, k, v, *, causal: bool, scale: float | None = None, out=None):
+    """The L_q newest positions against all L_k keys: q [B,L_q,h_q,d], k/v
+    [B,L_k,h_kv,d] -> o [B,L_q,h_q,d]; causally, query row i sees keys
+    0 .. L_k - L_q + i."""
+    _check(q, "q", 4)
+    _check(k, "k", 4)
+    _check(v, "v", 4)
+    B, Lq, h_q, d = q.shape
+    Lk, h_kv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Lk, h_kv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, L_k, h_kv, d] with q's B and d")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", 4)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().gqa_prefill_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Lq,
+                                 Lk, h_q, h_kv, d, _dtype_code(q), int(bool(causal)),
+                                 float(scale), _stream(q))
+    if st != 0:
+        raise GQAError(st, "gqa_prefill_chunk")
     return out
 
 

@@ -65,21 +65,27 @@ const char *gqa_status_string(gqa_status s) {
     }
 }
 
-gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *o, int B, int L,
-                       int h_q, int h_kv, int d, gqa_dtype dt, int causal, float scale,
-                       void *hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by both prefill entry points: Lq query positions per sequence attend
+// to Lk >= Lq keys, query row i sitting at position Lk - Lq + i.
+gqa_status prefill_impl(const void *q, const void *k, const void *v, void *o, int B, int Lq,
+                        int Lk, int h_q, int h_kv, int d, gqa_dtype dt, int causal, float scale,
+                        void *hip_stream) {
     if (!q || !k || !v || !o) return GQA_ERR_NULL_POINTER;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GQA_ERR_ALIGNMENT;
-    if (B <= 0 || L <= 0 || h_q <= 0 || h_kv <= 0) return GQA_ERR_SIZE;
+    if (B <= 0 || Lq <= 0 || Lk < Lq || h_q <= 0 || h_kv <= 0) return GQA_ERR_SIZE;
     if (h_q % h_kv != 0) return GQA_ERR_HEADS;
     if (d != 64 && d != 128) return GQA_ERR_HEAD_DIM;
     if (dt != GQA_F32 && dt != GQA_BF16) return GQA_ERR_DTYPE;
     if (!(scale > 0.f) || !isfinite(scale)) return GQA_ERR_SIZE;
-    const int64_t rows_q = (int64_t)B * L * h_q, rows_kv = (int64_t)B * L * h_kv;
+    const int64_t rows_q = (int64_t)B * Lq * h_q, rows_kv = (int64_t)B * Lk * h_kv;
     if (rows_q > (int64_t)1 << 31 || rows_kv > (int64_t)1 << 31) return GQA_ERR_SIZE;
     // the bf16 kernel addresses one sequence's key/value rows of a head with
-    // 32-bit byte offsets: L rows at a stride of h_kv * d elements
-    if (dt == GQA_BF16 && (int64_t)L * h_kv * d * 2 > (int64_t)0xffffffff) return GQA_ERR_SIZE;
+    // 32-bit byte offsets: Lk rows at a stride of h_kv * d elements
+    if (dt == GQA_BF16 && (int64_t)Lk * h_kv * d * 2 > (int64_t)0xffffffff) return GQA_ERR_SIZE;
 
     gqa::PrefillArgs a;
     a.q = q;
@@ -87,7 +93,9 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *o, int
     a.v = v;
     a.o = o;
     a.B = B;
-    a.L = L;
+    a.L = Lq;
+    a.Lk = Lk;
+    a.off = Lk - Lq;
     a.h_q = h_q;
     a.h_kv = h_kv;
     a.G = h_q / h_kv;
@@ -95,7 +103,7 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *o, int
     a.nsub = a.G / a.GW;
     a.BM = 32 * (8 / a.GW);
     a.n_units = B * h_kv * a.nsub;
-    a.n_qtiles = (L + a.BM - 1) / a.BM;
+    a.n_qtiles = (Lq + a.BM - 1) / a.BM;
     a.c = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
     if ((int64_t)a.n_units * a.n_qtiles > 0x7fffffff) return GQA_ERR_SIZE;
 
@@ -105,6 +113,22 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *o, int
     int rc = dt == GQA_BF16 ? gqa::launch_prefill_bf16(a, d, causal != 0, stream)
                             : gqa::launch_prefill_f32(a, d, causal != 0, stream);
     return rc == 0 ? GQA_OK : GQA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *o, int B, int L,
+                       int h_q, int h_kv, int d, gqa_dtype dt, int causal, float scale,
+                       void *hip_stream) {
+    return prefill_impl(q, k, v, o, B, L, L, h_q, h_kv, d, dt, causal, scale, hip_stream);
+}
+
+gqa_status gqa_prefill_chunk(const void *q, const void *k, const void *v, void *o, int B,
+                             int L_q, int L_k, int h_q, int h_kv, int d, gqa_dtype dt,
+                             int causal, float scale, void *hip_stream) {
+    return prefill_impl(q, k, v, o, B, L_q, L_k, h_q, h_kv, d, dt, causal, scale, hip_stream);
 }
 
 int gqa_decode_default_splits(void) { return kDefaultSplits; }

@@ -9,10 +9,12 @@ namespace gqa {
 
 // Prefill work map: a work-group covers GW query heads of one group (a
 // "subgroup"; nsub = G / GW of them per key/value head) times BM positions.
+// L query positions attend to Lk >= L keys per sequence; query row i sits at
+// position off + i, off = Lk - L (0 for the square prefill).
 struct PrefillArgs {
     const void *q, *k, *v;
     void *o;
-    int B, L, h_q, h_kv, G;
+    int B, L, Lk, off, h_q, h_kv, G;
     int GW, nsub, BM;
     int n_units;   // B * h_kv * nsub
     int n_qtiles;  // ceil(L / BM)

@@ -117,13 +117,13 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
     const int bk = unit / a.nsub;
     const int kvh = bk % a.h_kv;
     const int b = bk / a.h_kv;
-    const int L = a.L;
+    const int L = a.L, Lk = a.Lk, off = a.off;  // query rows, keys, position of row 0
     const int PB = 8 / a.GW;  // 32-position blocks per work-group
     const int p0 = qt * a.BM;
 
     const int head = kvh * a.G + sub * a.GW + wave / PB;
     const int pos0 = p0 + 32 * (wave % PB);
-    const int kv_end = CAUSAL ? min(L, p0 + a.BM) : L;
+    const int kv_end = CAUSAL ? min(Lk, off + p0 + a.BM) : Lk;
     const int ntiles = (kv_end + PF_BN - 1) / PF_BN;
 
     // ---- direct loads: waves 0-3 stream the K tile and waves 4-7 the V tile;
@@ -134,14 +134,14 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
     const bool loads_v = wave >= PF_WAVES / 2;
     const int i0 = (wave % (PF_WAVES / 2)) * DPW;
     const unsigned krb = (unsigned)(a.h_kv * D * 2);  // key row stride, bytes
-    // rows 0 .. L-1 of this (sequence, key/value head); L * krb < 2^32 is checked
+    // rows 0 .. Lk-1 of this (sequence, key/value head); Lk * krb < 2^32 is checked
     // on the host.  Rows past the sequence end read as zeros; for the ragged
     // last tile of a sequence spanning nearly 2^32 bytes a row offset may wrap,
     // and then reads zeros or finite data of the same tensor, which the mask
     // discards.
     const u32x4 rsrc = make_buffer_rsrc(
-        static_cast<const __bf16 *>(loads_v ? a.v : a.k) + ((size_t)b * L * a.h_kv + kvh) * D,
-        (unsigned)(L - 1) * krb + 2 * D);
+        static_cast<const __bf16 *>(loads_v ? a.v : a.k) + ((size_t)b * Lk * a.h_kv + kvh) * D,
+        (unsigned)(Lk - 1) * krb + 2 * D);
     // per-lane byte offset of piece i within its rows; depends on i only via i % NLO
     unsigned loff[NLO];
 #pragma unroll
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
     bf16x8 pb[2][2];  // P^T of the current tile: [key block][16-key half]
     float m_run = -INFINITY, l_run = 0.f;
     const bool has_rows = pos0 < L;
-    auto active = [&](int j) { return has_rows && (!CAUSAL || j * PF_BN <= pos0 + 31); };
+    auto active = [&](int j) { return has_rows && (!CAUSAL || j * PF_BN <= off + pos0 + 31); };
 
     // LDS operand reads for step st of the two products (16-byte K chunk;
     // transposed V pair); st runs over (k-step, key block) for QK and over
@@ -241,14 +241,14 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
     // new max exceeds mu by more than TAU, or on the first tile.
     auto softmax = [&](int j) {
         const int j0 = j * PF_BN;
-        if (j0 + PF_BN > L || (CAUSAL && j0 + PF_BN - 1 > pos0)) {
+        if (j0 + PF_BN > Lk || (CAUSAL && j0 + PF_BN - 1 > off + pos0)) {
             const int pos = pos0 + (lane & 31);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    const bool masked = key >= L || (CAUSAL && key > pos);
+                    const bool masked = key >= Lk || (CAUSAL && key > off + pos);
                     s[kb][r] = masked ? -INFINITY : s[kb][r];
                 }
         }

@@ -31,15 +31,15 @@ __global__ __launch_bounds__(PF32_THREADS) void prefill_f32_kernel(PrefillArgs a
     const int bk = unit / a.nsub;
     const int kvh = bk % a.h_kv;
     const int b = bk / a.h_kv;
-    const int L = a.L;
+    const int L = a.L, Lk = a.Lk, off = a.off;  // query rows, keys, position of row 0
     const int p0 = qt * a.BM;
     const int hl = tid / a.BM, pp = tid % a.BM;
     const int pos = p0 + pp;
     const int head = kvh * a.G + sub * a.GW + hl;
 
     const float *qg = static_cast<const float *>(a.q);
-    const float *kg = static_cast<const float *>(a.k) + ((size_t)b * L * a.h_kv + kvh) * D;
-    const float *vg = static_cast<const float *>(a.v) + ((size_t)b * L * a.h_kv + kvh) * D;
+    const float *kg = static_cast<const float *>(a.k) + ((size_t)b * Lk * a.h_kv + kvh) * D;
+    const float *vg = static_cast<const float *>(a.v) + ((size_t)b * Lk * a.h_kv + kvh) * D;
     const size_t kv_row = (size_t)a.h_kv * D;
 
     float qv[D], ov[D];
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(PF32_THREADS) void prefill_f32_kernel(PrefillArgs a
     for (int cc = 0; cc < D; ++cc) ov[cc] = 0.f;
     float m = -INFINITY, l = 0.f;
 
-    const int kv_end = CAUSAL ? min(L, p0 + a.BM) : L;
+    const int kv_end = CAUSAL ? min(Lk, off + p0 + a.BM) : Lk;
     for (int j0 = 0; j0 < kv_end; j0 += PF32_BN) {
         __syncthreads();
         constexpr int F4_PER_ROW = D / 4;
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(PF32_THREADS) void prefill_f32_kernel(PrefillArgs a
             int row = idx / F4_PER_ROW, col = idx % F4_PER_ROW;
             int key = j0 + row;
             float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
-            if (key < L) {
+            if (key < Lk) {
                 kx = *reinterpret_cast<const float4 *>(kg + (size_t)key * kv_row + 4 * col);
                 vx = *reinterpret_cast<const float4 *>(vg + (size_t)key * kv_row + 4 * col);
             }
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(PF32_THREADS) void prefill_f32_kernel(PrefillArgs a
 #pragma unroll
             for (int cc = 0; cc < D; ++cc) dot = fmaf(qv[cc], ksm[kk * D + cc], dot);
             int key = j0 + kk;
-            bool masked = key >= L || (CAUSAL && key > pos);
+            bool masked = key >= Lk || (CAUSAL && key > off + pos);
             s[kk] = masked ? -INFINITY : dot;
             mx = fmaxf(mx, s[kk]);
         }

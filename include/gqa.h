@@ -72,6 +72,26 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *o, int
                        void *hip_stream);
 
 /*
+ * Chunked prefill: the L_q newest positions of each sequence attend to all L_k
+ * keys of that sequence (1 <= L_q <= L_k), i.e. a chunk of new tokens whose
+ * keys and values were appended after L_k - L_q earlier ones ("What is
+ * Grouped-Query Attention", §3.2: append to the cache, then attend).  Run
+ * chunk by chunk this reproduces one full causal prefill exactly, unlike
+ * processing each chunk on its own ("Implementing GQA from scratch in
+ * PyTorch", §4.3).
+ *   q, o : [B, L_q, h_q, d]   (dtype dt)
+ *   k, v : [B, L_k, h_kv, d]  (dtype dt), positions 0 .. L_k - 1
+ *   causal != 0: query row i sits at position L_k - L_q + i and attends to keys
+ *          0 .. L_k - L_q + i (bottom-right alignment); else to all L_k keys.
+ *   Other arguments, limits and errors as gqa_prefill, with L_k in place of L
+ *   for k and v; L_q > L_k returns GQA_ERR_SIZE.  gqa_prefill(..., L, ...) is
+ *   gqa_prefill_chunk(..., L, L, ...).
+ */
+gqa_status gqa_prefill_chunk(const void *q, const void *k, const void *v, void *o, int B,
+                             int L_q, int L_k, int h_q, int h_kv, int d, gqa_dtype dt,
+                             int causal, float scale, void *hip_stream);
+
+/*
  * Decode: one new query position per sequence attends to rows [0, seqlens[b])
  * of a head-major key/value cache ("What is Grouped-Query Attention", §2.2 step
  * 2 for the [batch, g, seq_len, d_head] cache and §3.2 for appending the new

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("gqa_prefill", "gqa_decode", "gqa_decode_workspace_bytes",
+    for n in ("gqa_prefill", "gqa_prefill_chunk", "gqa_decode", "gqa_decode_workspace_bytes",
               "gqa_decode_default_splits", "gqa_status_string"):
         assert n in names
 
@@ -74,6 +74,32 @@ def test_prefill_without_a_gpu_reports_the_device():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert prefill_status() == DEVICE
+
+
+def chunk_status(q=A, k=A, v=A, o=A, B=1, Lq=16, Lk=64, h_q=8, h_kv=2, d=64, dt=1, causal=1,
+                 scale=0.125):
+    return gqa.lib().gqa_prefill_chunk(q, k, v, o, B, Lq, Lk, h_q, h_kv, d, dt, causal, scale,
+                                       None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(v=None), NULLP), (dict(q=MIS), ALIGN),
+    (dict(Lq=0), SIZE), (dict(Lq=65, Lk=64), SIZE), (dict(Lk=-1), SIZE), (dict(B=0), SIZE),
+    (dict(h_q=8, h_kv=3), HEADS), (dict(d=80), HEADDIM), (dict(dt=5), DTYPE),
+    (dict(scale=0.0), SIZE),
+    # the key span bound applies to L_k, not L_q
+    (dict(Lq=16, Lk=1 << 20, h_q=32, h_kv=32, d=128), SIZE),
+])
+def test_prefill_chunk_rejects_bad_arguments(kw, status):
+    assert chunk_status(**kw) == status
+
+
+def test_prefill_chunk_without_a_gpu_reports_the_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert chunk_status() == DEVICE
+    assert chunk_status(Lq=64, Lk=64) == DEVICE  # the square case is valid too
 
 
 def decode_status(q=A, kc=A, vc=A, sl=A, o=A, B=4, h_q=32, h_kv=8, S=1024, d=128, dt=1,

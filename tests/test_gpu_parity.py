@@ -180,6 +180,80 @@ def test_workload_long_context_prefill(dev):
     _sampled_prefill("long_context_prefill_bf16", 96, dev)
 
 
+# ------------------------------------------------ prefill against existing keys
+
+def run_prefill_chunk(q, k, v, causal, scale, dev):
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.full_like(qd, float("nan"))
+    gqa.prefill_chunk(qd, kd, vd, causal=causal, scale=scale, out=out)
+    torch.cuda.synchronize()
+    return out
+
+
+CHUNK_SMALL = [
+    # B, L_q, L_k, h_q, h_kv, d, dtype, causal
+    (1, 1, 200, 8, 2, 128, "bf16", True),      # one new token
+    (2, 70, 300, 8, 4, 64, "bf16", True),      # ragged chunk and keys
+    (1, 64, 128, 8, 1, 64, "bf16", True),      # tile-aligned, MQA
+    (1, 33, 1000, 32, 8, 128, "bf16", False),
+    (1, 129, 129, 16, 2, 128, "bf16", True),   # L_q == L_k
+    (1, 250, 251, 6, 2, 128, "bf16", True),    # G = 3
+    (2, 17, 80, 4, 4, 64, "f32", True),
+    (1, 50, 77, 8, 2, 128, "f32", False),
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_SMALL, ids=lambda c: "B{}_Lq{}_Lk{}_hq{}_hkv{}_d{}_{}_c{}".format(*c))
+def test_prefill_chunk_matches_oracle(case, dev):
+    B, Lq, Lk, h_q, h_kv, d, dt, causal = case
+    seed = 3000 + Lq + Lk + h_q
+    dtype = torch.float32 if dt == "f32" else torch.bfloat16
+    q, k, v = wl.prefill_chunk_inputs(B, Lq, Lk, h_q, h_kv, d, seed, dtype=dtype)
+    say(f"prefill_chunk {case} seed {seed}")
+    out = run_prefill_chunk(q, k, v, causal, 1 / math.sqrt(d), dev)
+    ref = oracle.prefill_cached(f64(q), f64(k), f64(v), causal, 1 / math.sqrt(d))
+    check(f64(out), ref, dt, f"prefill_chunk {case}")
+
+
+def test_prefill_chunk_square_is_prefill(dev):
+    # the same kernel and work map: bit-identical results
+    q, k, v = wl.prefill_inputs(1, 300, 8, 2, 128, 3100)
+    say("prefill_chunk square vs prefill")
+    a = run_prefill(q, k, v, True, 0.09, dev)
+    b = run_prefill_chunk(q, k, v, True, 0.09, dev)
+    assert torch.equal(a, b)
+
+
+def test_chunked_prefill_reproduces_full_prefill(dev):
+    # run one sequence chunk by chunk against the keys so far: every chunk's
+    # rows must match the full causal prefill's rows (oracle) to tolerance
+    B, L, h_q, h_kv, d = 1, 700, 16, 4, 128
+    q, k, v = wl.prefill_inputs(B, L, h_q, h_kv, d, 3200)
+    say("chunked prefill vs full causal prefill")
+    ref = oracle.prefill(f64(q), f64(k), f64(v), causal=True, scale=1 / math.sqrt(d))
+    parts = []
+    for c0, c1 in ((0, 100), (100, 101), (101, 356), (356, 700)):
+        parts.append(run_prefill_chunk(q[:, c0:c1].contiguous(), k[:, :c1].contiguous(),
+                                       v[:, :c1].contiguous(), True, 1 / math.sqrt(d), dev).cpu())
+    check(f64(torch.cat(parts, dim=1)), ref, "bf16", "chunked vs full causal prefill")
+
+
+def test_workload_chunked_prefill(dev):
+    w = wl.WORKLOADS["chunked_prefill_bf16"]
+    q, k, v = wl.workload_inputs(w)
+    say(f"prefill_chunk workload {w.name} ({w.description}) seed {w.seed}")
+    out = run_prefill_chunk(q, k, v, w.causal, w.scale, dev)
+    rows = wl.sample_rows(96, w.B, w.L, w.h_q, w.seed,
+                          include=[(0, 0, 0), (0, w.L - 1, w.h_q - 1)])
+    idx = torch.tensor(rows)
+    q_rows = q[idx[:, 0], idx[:, 1], idx[:, 2]]
+    o_rows = out.cpu()[idx[:, 0], idx[:, 1], idx[:, 2]]
+    ref = oracle.prefill_cached_rows(f64(q_rows), rows, f64(k), f64(v), w.h_q, w.L, w.causal,
+                                     w.scale)
+    check(f64(o_rows), ref, w.dtype, f"{w.name}: {len(rows)} sampled rows")
+    assert not torch.isnan(out).any(), f"{w.name}: output not fully written"
+
+
 # ------------------------------------------------------------------------- decode
 
 def run_decode(seqlens, q, kc, vc, dev, splits=0, out_fill=float("nan")):
