@@ -30,6 +30,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gqa_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libgqa_oracle.so")
+_DEFAULT_LIB = _LIB_PATH
 
 # No -ffast-math and no FP contraction: the C code's operation order is the
 # order that is evaluated.
@@ -52,7 +53,10 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    # the in-tree library is rebuilt when missing or older than its source (a
+    # library named explicitly, such as a test's mutant, is loaded as it is)
+    if _LIB_PATH == _DEFAULT_LIB and (not os.path.exists(_LIB_PATH) or
+                                      os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
         build(force=True)
     lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
@@ -69,6 +73,8 @@ def _load():
                                                    I, I, ctypes.c_double, P]
     lib.gqa_oracle_prefill_cached_rows.restype = I
     lib.gqa_oracle_decode.argtypes = [P, P, P, P, P, I, I, I, I, I]
+    lib.gqa_oracle_decode_append.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I]
+    lib.gqa_oracle_decode_append.restype = I
     lib.gqa_oracle_decode.restype = I
     lib.gqa_oracle_num_threads.argtypes = []
     lib.gqa_oracle_num_threads.restype = I
@@ -186,3 +192,27 @@ def decode(q, k_cache, v_cache, seqlens):
     if rc != 0:
         raise ValueError("oracle decode rejected its arguments (rc=%d)" % rc)
     return o
+
+
+def decode_append(q, k_new, v_new, k_cache, v_cache, seqlens):
+    """Decode with append.  q [B,h_q,d], k_new/v_new [B,h_kv,d], caches [B,h_kv,S,d],
+    seqlens [B] (before the append, each < S).
+
+    Returns (o [B,h_q,d], k_cache', v_cache'): the caches with the new rows
+    written at row seqlens[b] (copies; the inputs are not modified), and the
+    output of attending over rows [0, seqlens[b] + 1).
+    """
+    q, kn, vn = _f64(q), _f64(k_new), _f64(v_new)
+    kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
+    sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+    B, h_q, d = q.shape
+    _, h_kv, S, _ = kc.shape
+    if (kc.shape != (B, h_kv, S, d) or vc.shape != kc.shape or kn.shape != (B, h_kv, d)
+            or vn.shape != kn.shape or sl.shape != (B,)):
+        raise ValueError("decode_append shapes do not match")
+    o = np.empty_like(q)
+    rc = _load().gqa_oracle_decode_append(_ptr(q), _ptr(kn), _ptr(vn), _ptr(kc), _ptr(vc),
+                                          _ptr(sl), _ptr(o), B, h_q, h_kv, S, d)
+    if rc != 0:
+        raise ValueError("oracle decode_append rejected its arguments (rc=%d)" % rc)
+    return o, kc, vc

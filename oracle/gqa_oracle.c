@@ -35,6 +35,11 @@
  *   chunk on its own ("Implementing GQA from scratch in PyTorch", §4.3) does
  *   not.
  *
+ *   Decode with append: the new token's key and value rows are first written
+ *   into cache row seqlens[b] (seqlens[b] < S), then the token attends over
+ *   rows [0, seqlens[b] + 1) -- the order of "What is Grouped-Query
+ *   Attention", §3.2 (append to the cache, then attend).
+ *
  *   Decode: one new query token per sequence attends over the cache rows
  *   [0, seqlens[b]) of a head-major cache [B, h_kv, S, d]
  *   ("What is Grouped-Query Attention", §2.2 step 2 for the cache layout and
@@ -326,4 +331,34 @@ int gqa_oracle_decode(const double *q, const double *k_cache, const double *v_ca
         free(scores);
     }
     return failed ? ORACLE_ERR_NOMEM : 0;
+}
+
+/*
+ * Decode with append: k_new, v_new [B][h_kv][d] are copied into row
+ * seqlens[b] of k_cache, v_cache [B][h_kv][S][d] (modified in place), then
+ * q [B][h_q][d] attends over rows [0, seqlens[b] + 1) with scale 1/sqrt(d).
+ * Requires 0 <= seqlens[b] < S.
+ */
+int gqa_oracle_decode_append(const double *q, const double *k_new, const double *v_new,
+                             double *k_cache, double *v_cache, const int32_t *seqlens,
+                             double *o, int B, int h_q, int h_kv, int S, int d) {
+    if (B <= 0 || S <= 0 || d <= 0) return ORACLE_ERR_ARG;
+    if (check_heads(h_q, h_kv)) return ORACLE_ERR_ARG;
+    for (int b = 0; b < B; ++b)
+        if (seqlens[b] < 0 || seqlens[b] >= S) return ORACLE_ERR_ARG;
+    int32_t *grown = (int32_t *)malloc(sizeof(int32_t) * (size_t)B);
+    if (!grown) return ORACLE_ERR_NOMEM;
+    /* append: the new rows become cache row seqlens[b] */
+    for (int b = 0; b < B; ++b) {
+        for (int g = 0; g < h_kv; ++g) {
+            long row = (((long)b * h_kv + g) * S + seqlens[b]) * d;
+            memcpy(k_cache + row, k_new + ((long)b * h_kv + g) * d, sizeof(double) * (size_t)d);
+            memcpy(v_cache + row, v_new + ((long)b * h_kv + g) * d, sizeof(double) * (size_t)d);
+        }
+        grown[b] = seqlens[b] + 1;
+    }
+    /* then attend over the grown cache */
+    int rc = gqa_oracle_decode(q, k_cache, v_cache, grown, o, B, h_q, h_kv, S, d);
+    free(grown);
+    return rc;
 }

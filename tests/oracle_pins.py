@@ -353,12 +353,72 @@ def pin_chunk_rows_match_full():
     _close(out, np.array([full[b, i, h] for b, i, h in rows]), 0.0, "chunk rows vs full")
 
 
+# ----------------------------------------------------------- decode with append
+
+def pin_append_cross_path():
+    """Appending token n to a cache of n rows and decoding == causal prefill row n,
+    and the grown cache holds rows 0..n exactly."""
+    B, n, h_q, h_kv, d, S = 2, 11, 8, 2, 16, 20
+    q, k, v = (_rand((B, n + 1, h_q, d), 150), _rand((B, n + 1, h_kv, d), 151),
+               _rand((B, n + 1, h_kv, d), 152))
+    full = oracle.prefill(q, k, v, causal=True, scale=1 / math.sqrt(d))
+    kc = np.zeros((B, h_kv, S, d))
+    vc = np.zeros((B, h_kv, S, d))
+    kc[:, :, :n] = k[:, :n].transpose(0, 2, 1, 3)
+    vc[:, :, :n] = v[:, :n].transpose(0, 2, 1, 3)
+    o, kc2, vc2 = oracle.decode_append(q[:, n], k[:, n], v[:, n], kc, vc, [n] * B)
+    _close(o, full[:, n], 1e-12, "append + decode vs causal prefill row n")
+    assert np.array_equal(kc2[:, :, :n + 1], k[:, :n + 1].transpose(0, 2, 1, 3))
+    assert np.array_equal(vc2[:, :, :n + 1], v[:, :n + 1].transpose(0, 2, 1, 3))
+    assert np.array_equal(kc2[:, :, n + 1:], kc[:, :, n + 1:]), "rows past the append changed"
+
+
+def pin_append_to_empty_cache():
+    """With nothing cached the token attends only to itself: o = v_new of its group, exactly."""
+    B, h_q, h_kv, d, S = 3, 6, 2, 8, 5
+    q, kn, vn = _rand((B, h_q, d), 160), _rand((B, h_kv, d), 161), _rand((B, h_kv, d), 162)
+    kc = np.full((B, h_kv, S, d), np.nan)
+    vc = np.full((B, h_kv, S, d), np.nan)
+    o, _, _ = oracle.decode_append(q, kn, vn, kc, vc, [0] * B)
+    G = h_q // h_kv
+    for h in range(h_q):
+        assert np.array_equal(o[:, h], vn[:, h // G]), "empty cache: output must be v_new"
+
+
+def pin_append_brute_and_tail():
+    """Against the brute force over a grown cache built by hand; NaN rows past
+    the appended one never leak in; a length of S is rejected."""
+    B, h_q, h_kv, d, S = 3, 4, 2, 5, 9
+    q, kn, vn = _rand((B, h_q, d), 170), _rand((B, h_kv, d), 171), _rand((B, h_kv, d), 172)
+    kc, vc = _rand((B, h_kv, S, d), 173), _rand((B, h_kv, S, d), 174)
+    lens = [0, 4, 8]
+    kp, vp = kc.copy(), vc.copy()
+    for b, n in enumerate(lens):
+        kp[b, :, n + 1:] = np.nan
+        vp[b, :, n + 1:] = np.nan
+    o, _, _ = oracle.decode_append(q, kn, vn, kp, vp, lens)
+    kg, vg = kc.tolist(), vc.tolist()
+    for b, n in enumerate(lens):
+        for g in range(h_kv):
+            kg[b][g][n] = kn[b, g].tolist()
+            vg[b][g][n] = vn[b, g].tolist()
+    _close(o, brute.decode(q.tolist(), kg, vg, [n + 1 for n in lens]), 1e-12,
+           "append vs brute force over a hand-grown cache")
+    try:
+        oracle.decode_append(q, kn, vn, kc, vc, [S, 0, 0])
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("seqlens[b] == S leaves no row to append into: must be rejected")
+
+
 ALL_PINS = [pin_hand_2x2, pin_head_map, pin_decode_golden, pin_mha_reduction,
             pin_mqa_reduction, pin_gqa_library, pin_rows_sum_to_one, pin_k_zero_mean,
             pin_causal_row0, pin_identical_heads, pin_invariances, pin_cross_path,
             pin_rows_match_full, pin_decode_tail_ignored, pin_argument_errors,
             pin_chunk_golden, pin_chunked_equals_full, pin_chunk_single_query_is_decode,
-            pin_chunk_brute_and_library, pin_chunk_rows_match_full]
+            pin_chunk_brute_and_library, pin_chunk_rows_match_full, pin_append_cross_path,
+            pin_append_to_empty_cache, pin_append_brute_and_tail]
 
 
 def main(argv):

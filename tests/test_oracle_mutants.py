@@ -29,6 +29,7 @@ MUTANTS = {
     "transposed_key_index": ("dot += q[c] * krep[(long)j * d + c];",
                              "dot += q[c] * krep[(long)c * n_vis + j];"),
     "decode_reads_whole_cache": ("int n = seqlens[b];", "int n = S;"),
+    "append_not_attended": ("grown[b] = seqlens[b] + 1;", "grown[b] = seqlens[b];"),
     "decode_scale_wrong": ("const double scale = 1.0 / sqrt((double)d);",
                            "const double scale = 1.0 / (double)d;"),
     "first_head_of_group_only": ("int kvh = kv_head_of(h, h_q, h_kv);\n                int n = seqlens[b];",
