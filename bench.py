@@ -2,7 +2,8 @@
 """Benchmark of the grouped-query attention core on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--decode-workload NAME|none] [--no-cpu-baseline]
+                    [--decode-workload NAME|none] [--append-workload NAME|none]
+                    [--no-cpu-baseline]
 
 Prints ONE JSON line on stdout.  A step is one call of the prefill entry point
 on the selected workload (default: the pages' worked example, B=32, L=1024,
@@ -20,7 +21,11 @@ the 256 MiB last-level cache holds none of the KV cache (a read, not a write:
 evicting with writes would leave dirty lines whose write-back lands inside the
 timed kernel); its throughput is
 KV-cache bytes actually needed (sum of lengths * h_kv * d * 2 tensors * 2 B)
-per second of kernel time, reported under ``decode``.
+per second of kernel time, reported under ``decode``.  The decode that appends
+the new token's key/value rows itself is timed the same way on its own
+workload (the same shape, lengths U{1023..8191} before the append) and
+reported under ``decode_append``; its bytes also count the new rows, read
+once and written once.
 
 ``roofline`` divides the algorithmic work of one launch by the launch's
 average duration measured with HIP events on the launch stream; ``traffic``
@@ -72,7 +77,11 @@ def prefill_flops(w) -> float:
 
 
 def decode_kv_bytes(w, seqlens) -> float:
-    return float(int(seqlens.sum())) * w.h_kv * w.d * 2 * 2
+    """Key/value bytes one decode call must move: every valid cache row of K and
+    V once per key/value head; with append also the new rows read from
+    k_new/v_new and written into the cache."""
+    rows = int(seqlens.sum()) + (2 * w.B if w.path == "decode_append" else 0)
+    return float(rows) * w.h_kv * w.d * 2 * 2
 
 
 def source_digest(files) -> str:
@@ -182,7 +191,12 @@ def bench_decode(w, steps, warmup):
     import gqa_workloads as wl
     import grouped_query_attention_03_amd as gqa
     dev = torch.device("cuda:0")
-    seqlens, q, kc, vc = wl.workload_inputs(w)
+    append = w.path == "decode_append"
+    if append:
+        seqlens, q, kn, vn, kc, vc = wl.workload_inputs(w)
+        kn, vn = kn.to(dev), vn.to(dev)
+    else:
+        seqlens, q, kc, vc = wl.workload_inputs(w)
     kv_bytes = decode_kv_bytes(w, seqlens)
     seqlens, q, kc, vc = seqlens.to(dev), q.to(dev), kc.to(dev), vc.to(dev)
     out = torch.empty_like(q)
@@ -191,7 +205,10 @@ def bench_decode(w, steps, warmup):
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
 
     def step():
-        gqa.decode(q, kc, vc, seqlens, out=out, workspace=ws)
+        if append:  # every call writes the same new rows again
+            gqa.decode_append(q, kn, vn, kc, vc, seqlens, out=out, workspace=ws)
+        else:
+            gqa.decode(q, kc, vc, seqlens, out=out, workspace=ws)
 
     flush.fill_(1)
     flush_words = flush.view(torch.int32)
@@ -208,6 +225,8 @@ def bench_decode(w, steps, warmup):
     avg_ms = sum(ev) / len(ev)
     achieved = kv_bytes / (avg_ms * 1e-3) / 1e9
     traffic = recorded_traffic("decode", w.name)
+    what = "decode split (writing the new rows) + log-sum-exp merge" if append else \
+        "decode split + log-sum-exp merge"
     return {
         "workload": w.name,
         "description": w.description,
@@ -218,7 +237,7 @@ def bench_decode(w, steps, warmup):
         "kv_bytes_per_call": kv_bytes,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernels": "decode split + log-sum-exp merge (one call, timed together)"},
+                     "kernels": what + " (one call, timed together)"},
     }
 
 
@@ -300,6 +319,9 @@ def main(argv=None):
     ap.add_argument("--decode-workload", default="batched_decode_bf16",
                     choices=["none"] + [n for n in wl.WORKLOAD_ORDER
                                         if wl.WORKLOADS[n].path == "decode"])
+    ap.add_argument("--append-workload", default="batched_decode_append_bf16",
+                    choices=["none"] + [n for n in wl.WORKLOAD_ORDER
+                                        if wl.WORKLOADS[n].path == "decode_append"])
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--settle-seconds", type=float, default=0.5,
                     help="untimed runs of the step before the warmup, to reach working clocks")
@@ -358,6 +380,12 @@ def main(argv=None):
         line["decode"] = bench_decode(dw, args.decode_steps, args.warmup)
         log(f"decode: {line['decode']['value']:.1f} GB/s, kernel avg "
             f"{line['decode']['kernel_ms_avg']:.4f} ms")
+    if args.append_workload != "none":
+        aw = wl.WORKLOADS[args.append_workload]
+        log(f"decode with append {aw.name}: {aw.description}; steps {args.decode_steps}")
+        line["decode_append"] = bench_decode(aw, args.decode_steps, args.warmup)
+        log(f"decode with append: {line['decode_append']['value']:.1f} GB/s, kernel avg "
+            f"{line['decode_append']['kernel_ms_avg']:.4f} ms")
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline(w)

@@ -9,7 +9,7 @@ Recipe (one fixed rule for every workload):
 * a CPU ``torch.Generator`` seeded with the workload's seed;
 * draws in float32 with ``torch.randn`` in the order q, k, v (decode: the
   per-sequence lengths first, with ``torch.randint`` over [lo, hi] inclusive,
-  then q, k_cache, v_cache);
+  then q, k_cache, v_cache; decode with append: then also k_new, v_new);
 * a standard deviation other than 1 is applied in float32 before the cast;
 * the cast to bfloat16 is torch's round-to-nearest-even.
 
@@ -36,7 +36,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    path: str  # "prefill", "prefill_chunk" or "decode"
+    path: str  # "prefill", "prefill_chunk", "decode" or "decode_append"
     dtype: str  # "f32" or "bf16"
     B: int
     h_q: int
@@ -47,7 +47,7 @@ class Workload:
     S: int = 0  # decode cache capacity
     causal: bool = False
     std: float = 1.0
-    seqlen_range: tuple = (0, 0)  # decode: inclusive [lo, hi]
+    seqlen_range: tuple = (0, 0)  # decode: inclusive [lo, hi] (decode_append: before the append)
     seed: int = 0
     description: str = field(default="", compare=False)
 
@@ -89,12 +89,19 @@ WORKLOADS = {
         d=128, causal=True, std=1.0 / math.sqrt(2.0), seed=6,
         description="bf16 causal chunked prefill: the last 2048 of 32768 positions, "
                     "B=1 h_q=64 h_kv=8 d=128"),
+    "batched_decode_append_bf16": Workload(
+        "batched_decode_append_bf16", "decode_append", "bf16", B=64, h_q=32, h_kv=8, d=128,
+        S=8192, std=1.0, seqlen_range=(1023, 8191), seed=7,
+        description="bf16 decode with the new token's key/value appended, B=64 h_q=32 h_kv=8 "
+                    "d=128 S=8192 lengths U{1023..8191} before the append"),
 }
 
 # Order in which the workloads are listed everywhere: the five of the core
-# path, then the chunked prefill against existing keys.
+# path, then the chunked prefill against existing keys and the decode that
+# appends the new token's key/value rows itself.
 WORKLOAD_ORDER = ["tiny_prefill_f32", "worked_example_prefill_bf16", "llama2_7b_prefill_bf16",
-                  "batched_decode_bf16", "long_context_prefill_bf16", "chunked_prefill_bf16"]
+                  "batched_decode_bf16", "long_context_prefill_bf16", "chunked_prefill_bf16",
+                  "batched_decode_append_bf16"]
 
 
 def _draw(gen, shape, std, dtype):
@@ -133,12 +140,30 @@ def decode_inputs(B, h_q, h_kv, S, d, seed, seqlen_range, std=1.0, dtype=torch.b
     return seqlens, q, k_cache, v_cache
 
 
+def decode_append_inputs(B, h_q, h_kv, S, d, seed, seqlen_range, std=1.0,
+                         dtype=torch.bfloat16):
+    """decode_inputs' tensors (lengths before the append), then the new token's
+    k_new, v_new [B,1,h_kv,d] drawn from the same generator after them."""
+    lo, hi = seqlen_range
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    seqlens = torch.randint(lo, hi + 1, (B,), generator=gen, dtype=torch.int64).to(torch.int32)
+    q = _draw(gen, (B, 1, h_q, d), std, dtype)
+    k_cache = _draw(gen, (B, h_kv, S, d), std, dtype)
+    v_cache = _draw(gen, (B, h_kv, S, d), std, dtype)
+    k_new = _draw(gen, (B, 1, h_kv, d), std, dtype)
+    v_new = _draw(gen, (B, 1, h_kv, d), std, dtype)
+    return seqlens, q, k_new, v_new, k_cache, v_cache
+
+
 def workload_inputs(w: Workload):
     """Inputs of a named workload, as CPU tensors (see prefill_inputs/decode_inputs)."""
     if w.path == "prefill":
         return prefill_inputs(w.B, w.L, w.h_q, w.h_kv, w.d, w.seed, w.std, w.torch_dtype())
     if w.path == "prefill_chunk":
         return prefill_chunk_inputs(w.B, w.L, w.Lk, w.h_q, w.h_kv, w.d, w.seed, w.std,
+                                    w.torch_dtype())
+    if w.path == "decode_append":
+        return decode_append_inputs(w.B, w.h_q, w.h_kv, w.S, w.d, w.seed, w.seqlen_range, w.std,
                                     w.torch_dtype())
     return decode_inputs(w.B, w.h_q, w.h_kv, w.S, w.d, w.seed, w.seqlen_range, w.std,
                          w.torch_dtype())

@@ -16,6 +16,9 @@ the device is not a gfx950 GPU, the calls raise.
     decode(q, k_cache, v_cache, seqlens, out=None, workspace=None, num_splits=0)
         q [B, 1, h_q, d] bf16, caches [B, h_kv, S, d] bf16, seqlens [B] int32
         -> o [B, 1, h_q, d].
+    decode_append(q, k_new, v_new, k_cache, v_cache, seqlens, ...)
+        writes k_new/v_new [B, 1, h_kv, d] at cache row seqlens[b], then attends
+        over rows [0, seqlens[b] + 1).
 """
 from __future__ import annotations
 
@@ -58,6 +61,9 @@ def lib() -> ctypes.CDLL:
     L.gqa_prefill_chunk.restype = I
     L.gqa_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, ctypes.c_size_t, P]
     L.gqa_decode.restype = I
+    L.gqa_decode_append.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P,
+                                    ctypes.c_size_t, P]
+    L.gqa_decode_append.restype = I
     L.gqa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     L.gqa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.gqa_decode_default_splits.argtypes = []
@@ -185,4 +191,45 @@ def decode(q, k_cache, v_cache, seqlens, *, out=None, workspace=None, num_splits
                           _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_decode")
+    return out
+
+
+def decode_append(q, k_new, v_new, k_cache, v_cache, seqlens, *, out=None, workspace=None,
+                  num_splits: int = 0):
+    """Append the new token's rows at seqlens[b] of the caches (in place), then
+    attend over rows [0, seqlens[b] + 1).  q [B,1,h_q,d], k_new/v_new
+    [B,1,h_kv,d], caches [B,h_kv,S,d] bf16, seqlens [B] int32 (before the
+    append, each < S; not modified) -> o [B,1,h_q,d]."""
+    _check(q, "q", 4)
+    _check(k_new, "k_new", 4)
+    _check(v_new, "v_new", 4)
+    _check(k_cache, "k_cache", 4)
+    _check(v_cache, "v_cache", 4)
+    _check(seqlens, "seqlens", 1)
+    B, one, h_q, d = q.shape
+    if one != 1:
+        raise ValueError("q must be [B, 1, h_q, d]")
+    _, h_kv, S, _ = k_cache.shape
+    if tuple(k_cache.shape) != (B, h_kv, S, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, h_kv, S, d] with q's B and d")
+    if tuple(k_new.shape) != (B, 1, h_kv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [B, 1, h_kv, d]")
+    if seqlens.dtype != torch.int32 or seqlens.shape[0] != B:
+        raise ValueError("seqlens must be int32 [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", 4)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    need = decode_workspace_bytes(B, h_q, h_kv, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().gqa_decode_append(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                 k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
+                                 out.data_ptr(), B, h_q, h_kv, S, d, _dtype_code(q),
+                                 int(num_splits), workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _stream(q))
+    if st != 0:
+        raise GQAError(st, "gqa_decode_append")
     return out

@@ -2,10 +2,12 @@
 //
 // One new query position per sequence attends to cache rows [0, seqlens[b]) of
 // k_cache/v_cache [B, h_kv, S, d] ("What is Grouped-Query Attention", §2.2 step 2
-// for the cache layout, §3.2 for attending over the appended cache).  The pass
-// is bound by reading the cache, so every valid cache byte is read exactly once
-// per key/value head, never once per query head, and the reads are kept
-// streaming without bubbles:
+// for the cache layout, §3.2 for attending over the appended cache).  In the
+// append form the new token's key and value rows are written into cache row
+// seqlens[b] and attended as part of the same pass (rows [0, seqlens[b] + 1)),
+// the order of §3.2.  The pass is bound by reading the cache, so every valid
+// cache byte is read exactly once per key/value head, never once per query
+// head, and the reads are kept streaming without bubbles:
 //
 // decode_split: a persistent, evenly balanced stream per wave.  The valid
 //   32-key blocks of all (sequence, key/value head) segments form one list of
@@ -13,10 +15,10 @@
 //   which may span several segments.  The G query heads of the segment's group
 //   are stacked as the N dimension of v_mfma_f32_16x16x32_bf16 (S^T = K Q^T,
 //   keys on M), so one read of a cache row serves every query head of the
-//   group.  K rows go straight from HBM into MFMA A-operand registers with
-//   16-byte loads; V rows go through the wave's LDS buffer and come back
-//   transposed (ds_read_b64_tr_b16) as the A operand of O^T = V^T P^T.  The
-//   next block's loads are always in flight, also across segment boundaries.
+//   group.  Q, K and V rows move with direct 16-byte loads into a per-wave LDS
+//   ring; K comes back as the MFMA A operand, V transposed
+//   (ds_read_b64_tr_b16) as the A operand of O^T = V^T P^T.  The next block's
+//   loads are always in flight, also across segment boundaries.
 //   For every segment it touches, a wave writes the segment's partial output
 //   (normalised) and its log-sum-exp (base 2, in units of scale*log2(e)) to
 //   slot w + segment of the workspace: the (wave, segment) pairs form a
@@ -24,7 +26,8 @@
 // decode_merge: one wave per (sequence, query head) finds the waves whose
 //   slices cover its segment and combines their partials with weights
 //   2^(lse - max lse): the exact log-sum-exp merge.
-// Rows at or beyond seqlens[b] are never loaded.
+// Rows at or beyond seqlens[b] (seqlens[b] + 1 when appending) are never loaded
+// from the cache.
 #include "gqa_device.h"
 #include "gqa_kernels.h"
 
@@ -68,16 +71,22 @@ __device__ __forceinline__ int vswz(int r) {
 // Direct loads of `n_dma` x 1 KiB into `dst`: load i, lane l fetches row
 // i * ROWS_PER_DMA + l / CPR (clamped to last_row), logical chunk
 // (l % CPR) ^ swz(row), and the hardware stores it at byte 1024 i + 16 l.
-template <int D, bool VSW>
+// With LAST_ELSEWHERE, row last_row (and the clamped rows past it) is taken
+// from the single row at last_src instead: the appended row, which is not in
+// the cache yet.
+template <int D, bool VSW, bool LAST_ELSEWHERE = false>
 __device__ __forceinline__ void dc_dma_rows(const __bf16 *__restrict__ src, size_t row_stride,
-                                            int row0, int last_row, int n_dma, GQA_LDS char *dst) {
+                                            int row0, int last_row, int n_dma, GQA_LDS char *dst,
+                                            const __bf16 *last_src = nullptr) {
     using Lay = DcLayout<D>;
     const int lane = threadIdx.x & 63;
     for (int i = 0; i < n_dma; ++i) {
         const int row = i * Lay::ROWS_PER_DMA + lane / Lay::CPR;
         const int chunk = (lane % Lay::CPR) ^ (VSW ? vswz<D>(row) : kswz<D>(row));
         const int srow = min(row0 + row, last_row);
-        dma16_to_lds(src + (size_t)srow * row_stride + 8 * chunk, dst + i * 1024);
+        const __bf16 *p = src + (size_t)srow * row_stride + 8 * chunk;
+        if (LAST_ELSEWHERE) p = srow == last_row ? last_src + 8 * chunk : p;
+        dma16_to_lds(p, dst + i * 1024);
     }
 }
 
@@ -155,9 +164,10 @@ __device__ __forceinline__ void dc_block(const GQA_LDS char *qt, const GQA_LDS c
 
 // Segment bookkeeping shared by the split and merge passes.  Segments are
 // ordered (sequence b, key/value head, query-head subgroup); segment
-// (b, kv, qs) has nblk(b) = ceil(seqlens[b] / 32) blocks.
-__device__ __forceinline__ int dc_nblk(const int32_t *seqlens, int b) {
-    return (load_const(seqlens, b) + DC_BK - 1) / DC_BK;
+// (b, kv, qs) has nblk(b) = ceil((seqlens[b] + extra) / 32) blocks, extra = 1
+// when the new token's row is appended and attended.
+__device__ __forceinline__ int dc_nblk(const int32_t *seqlens, int b, int extra) {
+    return (load_const(seqlens, b) + extra + DC_BK - 1) / DC_BK;
 }
 
 __device__ __forceinline__ long long dc_slice_start(int w, long long T, int NW) {
@@ -179,14 +189,16 @@ __device__ __forceinline__ long long dc_wave_sum(long long x) {
 
 // Blocks of the whole list (T) and blocks of the sequences before `upto` (P),
 // one sequence per lane, 64 at a time.
-__device__ __forceinline__ void dc_block_totals(const int32_t *seqlens, int B, int segs_per_b,
-                                                int upto, long long &T, long long &P) {
+__device__ __forceinline__ void dc_block_totals(const int32_t *seqlens, int extra, int B,
+                                                int segs_per_b, int upto, long long &T,
+                                                long long &P) {
     const int lane = threadIdx.x & 63;
     long long t = 0, p = 0;
     for (int b0 = 0; b0 < B; b0 += 64) {
         const int bb = b0 + lane;
         if (bb < B) {
-            const long long n = (long long)((seqlens[bb] + DC_BK - 1) / DC_BK) * segs_per_b;
+            const long long n =
+                (long long)((seqlens[bb] + extra + DC_BK - 1) / DC_BK) * segs_per_b;
             t += n;
             if (bb < upto) p += n;
         }
@@ -198,8 +210,9 @@ __device__ __forceinline__ void dc_block_totals(const int32_t *seqlens, int B, i
 // The sequence whose segments hold global block `pos` (0 <= pos < T) and the
 // number of blocks before its first segment: an inclusive scan over 64
 // sequences at a time and a ballot.
-__device__ __forceinline__ void dc_locate(const int32_t *seqlens, int B, int segs_per_b,
-                                          long long pos, int &b_out, long long &cum_out) {
+__device__ __forceinline__ void dc_locate(const int32_t *seqlens, int extra, int B,
+                                          int segs_per_b, long long pos, int &b_out,
+                                          long long &cum_out) {
     const int lane = threadIdx.x & 63;
     long long base = 0;
     b_out = B;
@@ -207,7 +220,7 @@ __device__ __forceinline__ void dc_locate(const int32_t *seqlens, int B, int seg
     for (int b0 = 0; b0 < B; b0 += 64) {
         const int bb = b0 + lane;
         const long long n =
-            bb < B ? (long long)((seqlens[bb] + DC_BK - 1) / DC_BK) * segs_per_b : 0;
+            bb < B ? (long long)((seqlens[bb] + extra + DC_BK - 1) / DC_BK) * segs_per_b : 0;
         long long incl = n;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -238,7 +251,11 @@ constexpr int dc_slots() {
 }
 
 // QD = 1 KiB loads per block for the query tile (ceil(query heads x 2d / 1024)).
-template <int D, int QD>
+// APPEND: the new token's key/value rows (k_new, v_new) are attended as row
+// seqlens[b] and written into that cache row by the wave that owns the
+// segment's last block (query-head subgroup 0 only); no wave reads that cache
+// row, so the write races with nothing.
+template <int D, int QD, bool APPEND>
 __global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs a) {
     using Lay = DcLayout<D>;
     constexpr int DB = D / 16;  // 16-wide blocks of the head dimension
@@ -258,7 +275,7 @@ __global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs 
 
     // total blocks and this wave's slice
     long long T, unused;
-    dc_block_totals(a.seqlens, a.B, segs_per_b, 0, T, unused);
+    dc_block_totals(a.seqlens, a.extra, a.B, segs_per_b, 0, T, unused);
     const long long pos = dc_slice_start(w, T, a.NW);
     const long long end = dc_slice_start(w + 1, T, a.NW);
     if (pos >= end) return;
@@ -270,21 +287,21 @@ __global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs 
     {
         int b0;
         long long cum;
-        dc_locate(a.seqlens, a.B, segs_per_b, pos, b0, cum);
+        dc_locate(a.seqlens, a.extra, a.B, segs_per_b, pos, b0, cum);
         b0 = __builtin_amdgcn_readfirstlane(b0);
-        const long long nb = dc_nblk(a.seqlens, b0);  // > 0: the block at pos lies in b0
+        const long long nb = dc_nblk(a.seqlens, b0, a.extra);  // > 0: the block at pos lies in b0
         cur = Cur{b0, (int)((pos - cum) / nb), (int)((pos - cum) % nb)};
     }
     const float c = a.c;
 
     auto advance = [&](Cur &u) {
-        if (++u.blk == dc_nblk(a.seqlens, u.b)) {
+        if (++u.blk == dc_nblk(a.seqlens, u.b, a.extra)) {
             u.blk = 0;
             if (++u.seg == segs_per_b) {
                 u.seg = 0;
                 do {
                     ++u.b;
-                } while (u.b < a.B && dc_nblk(a.seqlens, u.b) == 0);
+                } while (u.b < a.B && dc_nblk(a.seqlens, u.b, a.extra) == 0);
             }
         }
     };
@@ -294,14 +311,40 @@ __global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs 
     auto issue = [&](const Cur &u, GQA_LDS char *qt, GQA_LDS char *kt, GQA_LDS char *vt) {
         const int kvh = u.seg / a.n_qsub, qs = u.seg % a.n_qsub;
         const size_t slab = ((size_t)u.b * a.h_kv + kvh) * (size_t)a.S * D;
-        const int kend = load_const(a.seqlens, u.b);
+        const int kend = load_const(a.seqlens, u.b) + a.extra;
         const int head0 = kvh * a.G + 16 * qs;
+        const size_t new_row = ((size_t)u.b * a.h_kv + kvh) * D;  // in k_new / v_new
         dc_dma_rows<D, false>(static_cast<const __bf16 *>(a.q) + ((size_t)u.b * a.h_q + head0) * D, D, 0,
                               heads_in(u) - 1, QD, qt);
-        dc_dma_rows<D, false>(static_cast<const __bf16 *>(a.k_cache) + slab, D, DC_BK * u.blk, kend - 1,
-                              Lay::KV_DMA, kt);
-        dc_dma_rows<D, true>(static_cast<const __bf16 *>(a.v_cache) + slab, D, DC_BK * u.blk, kend - 1,
-                             Lay::KV_DMA, vt);
+        dc_dma_rows<D, false, APPEND>(static_cast<const __bf16 *>(a.k_cache) + slab, D, DC_BK * u.blk,
+                                      kend - 1, Lay::KV_DMA, kt,
+                                      static_cast<const __bf16 *>(a.k_new) + new_row);
+        dc_dma_rows<D, true, APPEND>(static_cast<const __bf16 *>(a.v_cache) + slab, D, DC_BK * u.blk,
+                                     kend - 1, Lay::KV_DMA, vt,
+                                     static_cast<const __bf16 *>(a.v_new) + new_row);
+    };
+    // APPEND: copy the new key and value rows into cache row seqlens[b], one
+    // 16-byte chunk per lane, from the block's LDS tiles, which hold them
+    // already (chunk c of tile row r at r * ROW_BYTES + 16 (c ^ swz(r))), so
+    // no global load has to be waited for.
+    // Skipped when seqlens[b] >= S, a broken precondition.
+    auto store_new_rows = [&](const Cur &u, const GQA_LDS char *kt, const GQA_LDS char *vt) {
+        constexpr int CPR = Lay::CPR;
+        const int kvh = u.seg / a.n_qsub;
+        const int row = load_const(a.seqlens, u.b);
+        if (row >= a.S || lane >= 2 * CPR) return;
+        const bool is_v = lane >= CPR;
+        const int ch = is_v ? lane - CPR : lane;
+        const int r = row - DC_BK * u.blk;  // the row's place in the tile
+        const int phys = ch ^ (is_v ? vswz<D>(r) : kswz<D>(r));
+        const u32x4 val = *reinterpret_cast<const GQA_LDS u32x4 *>((is_v ? vt : kt) +
+                                                                  r * Lay::ROW_BYTES + 16 * phys);
+        const size_t off = (((size_t)u.b * a.h_kv + kvh) * a.S + row) * D + 8 * ch;
+        // the pointers pass through readfirstlane so that the per-lane choice
+        // is made between two values, not between two argument addresses
+        // (which would read the arguments with vector loads)
+        const unsigned long long base = is_v ? uniform_addr(a.v_cache) : uniform_addr(a.k_cache);
+        *reinterpret_cast<GQA_GLOBAL u32x4 *>(base + 2 * off) = val;
     };
 
     long long left = end - pos;  // blocks left to compute
@@ -340,10 +383,12 @@ __global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs 
         // DC_SLOTS - 1 slots (issued after them) are still in flight; stores
         // issued in between only make the wait stricter
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DC_SLOTS - 1) * OPS) : "memory");
-        dc_block<D, QD * Lay::ROWS_PER_DMA>(qt, kt, vt, DC_BK * cur.blk, load_const(a.seqlens, cur.b),
-                    qcol < heads_in(cur), c, m_run, l_run, acc);
+        dc_block<D, QD * Lay::ROWS_PER_DMA>(qt, kt, vt, DC_BK * cur.blk,
+                    load_const(a.seqlens, cur.b) + a.extra, qcol < heads_in(cur), c, m_run, l_run, acc);
         --left;
-        if (cur.blk + 1 == dc_nblk(a.seqlens, cur.b) || left == 0) close_segment(cur);
+        const bool last_block = cur.blk + 1 == dc_nblk(a.seqlens, cur.b, a.extra);
+        if (APPEND && last_block && cur.seg % a.n_qsub == 0) store_new_rows(cur, kt, vt);
+        if (last_block || left == 0) close_segment(cur);
         advance(cur);
     };
     // the load cursor stops at the slice's last block; later issues repeat it
@@ -379,14 +424,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     const int kvh = h / a.G, hg = h % a.G, qs = hg / 16, qcol = hg % 16;
     const int segs_per_b = a.h_kv * a.n_qsub;
     __bf16 *op = static_cast<__bf16 *>(a.o) + (size_t)wid * D + PER * lane;
-    const int nb = dc_nblk(a.seqlens, b);
+    const int nb = dc_nblk(a.seqlens, b, a.extra);
     if (nb == 0) {
 #pragma unroll
         for (int e = 0; e < PER; ++e) op[e] = (__bf16)0.f;
         return;
     }
     long long T, P;
-    dc_block_totals(a.seqlens, a.B, segs_per_b, b, T, P);
+    dc_block_totals(a.seqlens, a.extra, a.B, segs_per_b, b, T, P);
     const int seg_in_b = kvh * a.n_qsub + qs;
     P += (long long)seg_in_b * nb;  // first block of this segment
     const long long seg_global = (long long)b * segs_per_b + seg_in_b;
@@ -455,8 +500,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 
 template <int D, int QD>
 void launch_split(const DecodeArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_split_kernel<D, QD>), dim3((a.NW + DC_WAVES - 1) / DC_WAVES),
-                       dim3(DC_THREADS), 0, stream, a);
+    const dim3 grid((a.NW + DC_WAVES - 1) / DC_WAVES), block(DC_THREADS);
+    if (a.extra) hipLaunchKernelGGL((decode_split_kernel<D, QD, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_split_kernel<D, QD, false>), grid, block, 0, stream, a);
 }
 
 int launch_decode_bf16(const DecodeArgs &a, int d, hipStream_t stream) {

@@ -143,14 +143,23 @@ size_t gqa_decode_workspace_bytes(int B, int h_q, int h_kv, int d, int num_split
     return round_up_256(slots * 16 * d * sizeof(float)) + round_up_256(slots * 16 * sizeof(float));
 }
 
-gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
-                      const int32_t *seqlens, void *o, int B, int h_q, int h_kv, int S, int d,
-                      gqa_dtype dt, int num_splits, void *workspace, size_t workspace_bytes,
-                      void *hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by both decode entry points; k_new/v_new non-null selects the append
+// form (the new rows are written at seqlens[b] and attended as well).
+gqa_status decode_impl(const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                       const void *v_cache, const int32_t *seqlens, void *o, int B, int h_q,
+                       int h_kv, int S, int d, gqa_dtype dt, int num_splits, void *workspace,
+                       size_t workspace_bytes, void *hip_stream) {
+    const bool append = k_new != nullptr || v_new != nullptr;
     if (!q || !k_cache || !v_cache || !seqlens || !o) return GQA_ERR_NULL_POINTER;
+    if (append && (!k_new || !v_new)) return GQA_ERR_NULL_POINTER;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
         (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
         return GQA_ERR_ALIGNMENT;
+    if (append && (!aligned16(k_new) || !aligned16(v_new))) return GQA_ERR_ALIGNMENT;
     if (B <= 0 || h_q <= 0 || h_kv <= 0 || S <= 0) return GQA_ERR_SIZE;
     if (h_q % h_kv != 0) return GQA_ERR_HEADS;
     if (d != 64 && d != 128) return GQA_ERR_HEAD_DIM;
@@ -164,6 +173,9 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
     a.q = q;
     a.k_cache = k_cache;
     a.v_cache = v_cache;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.extra = append ? 1 : 0;
     a.seqlens = seqlens;
     a.o = o;
     a.B = B;
@@ -183,6 +195,27 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
     if (st != GQA_OK) return st;
     int rc = gqa::launch_decode_bf16(a, d, static_cast<hipStream_t>(hip_stream));
     return rc == 0 ? GQA_OK : GQA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *seqlens, void *o, int B, int h_q, int h_kv, int S, int d,
+                      gqa_dtype dt, int num_splits, void *workspace, size_t workspace_bytes,
+                      void *hip_stream) {
+    return decode_impl(q, nullptr, nullptr, k_cache, v_cache, seqlens, o, B, h_q, h_kv, S, d, dt,
+                       num_splits, workspace, workspace_bytes, hip_stream);
+}
+
+gqa_status gqa_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                             void *v_cache, const int32_t *seqlens, void *o, int B, int h_q,
+                             int h_kv, int S, int d, gqa_dtype dt, int num_splits,
+                             void *workspace, size_t workspace_bytes, void *hip_stream) {
+    if (!k_new || !v_new) return GQA_ERR_NULL_POINTER;
+    return decode_impl(q, k_new, v_new, k_cache, v_cache, seqlens, o, B, h_q, h_kv, S, d, dt,
+                       num_splits, workspace, workspace_bytes, hip_stream);
 }
 
 }  // extern "C"

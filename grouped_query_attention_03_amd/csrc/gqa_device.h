@@ -65,6 +65,18 @@ __device__ __forceinline__ int load_const(const int32_t *p, int i) {
         reinterpret_cast<uintptr_t>(p))[i];
 }
 
+#define GQA_GLOBAL __attribute__((address_space(1)))
+
+// A wave-uniform global address as a scalar value.  readfirstlane returns a
+// signed 32-bit int: each half goes through unsigned before it is widened, or
+// a low word with bit 31 set would be sign-extended into the high word.
+__device__ __forceinline__ unsigned long long uniform_addr(const void *p) {
+    const unsigned long long a = (unsigned long long)(uintptr_t)p;
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)a);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+    return ((unsigned long long)hi << 32) | (unsigned long long)lo;
+}
+
 // Index of this wave in its work-group, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 

@@ -27,6 +27,8 @@ constexpr int kDecodeWaves = 4;
 
 struct DecodeArgs {
     const void *q, *k_cache, *v_cache;
+    const void *k_new, *v_new;  // [B, h_kv, d] rows appended at seqlens[b] (append form), else null
+    int extra;                  // rows attended = seqlens[b] + extra (1 for the append form)
     const int32_t *seqlens;
     void *o;
     float *opart;  // [NW + segments][16][d] per-slot partial outputs (normalised)

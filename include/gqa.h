@@ -119,6 +119,31 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
                       gqa_dtype dt, int num_splits, void *workspace, size_t workspace_bytes,
                       void *hip_stream);
 
+/*
+ * Decode with append: the new token's key and value rows are written into the
+ * cache, then the token attends over the grown cache ("What is Grouped-Query
+ * Attention", §3.2: append, then attend), in one call.
+ *   q, o             : [B, 1, h_q, d]  bf16
+ *   k_new, v_new     : [B, 1, h_kv, d] bf16 (the new token's key and value rows)
+ *   k_cache, v_cache : [B, h_kv, S, d] bf16; row seqlens[b] of every key/value
+ *                      head is overwritten with k_new / v_new, no other byte of
+ *                      the caches is written
+ *   seqlens          : [B] int32 on the device, the lengths BEFORE the append,
+ *                      each in [0, S - 1]; the token attends over rows
+ *                      [0, seqlens[b] + 1).  The caller advances seqlens.
+ *                      Not checked on the device: for seqlens[b] >= S nothing is
+ *                      written for that sequence (and values above S read past
+ *                      its cache rows, as in gqa_decode).
+ *   Other arguments, the workspace and errors as gqa_decode; the workspace size
+ *   is gqa_decode_workspace_bytes of the same sizes.  The new rows are read
+ *   from k_new / v_new for the attention, so no part of the call depends on
+ *   the order of the cache write.
+ */
+gqa_status gqa_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                             void *v_cache, const int32_t *seqlens, void *o, int B, int h_q,
+                             int h_kv, int S, int d, gqa_dtype dt, int num_splits,
+                             void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* Bytes of decode workspace needed for these sizes and num_splits (0 =
  * default); returns 0 when an argument is invalid. */
 size_t gqa_decode_workspace_bytes(int B, int h_q, int h_kv, int d, int num_splits);

@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("gqa_prefill", "gqa_prefill_chunk", "gqa_decode", "gqa_decode_workspace_bytes",
+    for n in ("gqa_prefill", "gqa_prefill_chunk", "gqa_decode", "gqa_decode_append",
+              "gqa_decode_workspace_bytes",
               "gqa_decode_default_splits", "gqa_status_string"):
         assert n in names
 
@@ -128,6 +129,34 @@ def test_decode_without_a_gpu_reports_the_device():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert decode_status(sl=A + 4) == DEVICE  # int32 alignment is enough for seqlens
+
+
+def append_status(q=A, kn=A, vn=A, kc=A, vc=A, sl=A, o=A, B=4, h_q=32, h_kv=8, S=1024, d=128,
+                  dt=1, splits=0, ws=A, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = (gqa.decode_workspace_bytes(B, h_q, h_kv, d, splits)
+                    if d in (64, 128) and h_q % h_kv == 0 else 1 << 30)
+    return gqa.lib().gqa_decode_append(q, kn, vn, kc, vc, sl, o, B, h_q, h_kv, S, d, dt, splits,
+                                       ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kn=None), NULLP), (dict(vn=None), NULLP), (dict(kn=None, vn=None), NULLP),
+    (dict(q=None), NULLP), (dict(vc=None), NULLP), (dict(sl=None), NULLP),
+    (dict(kn=MIS), ALIGN), (dict(vn=A + 4), ALIGN), (dict(kc=MIS), ALIGN),
+    (dict(S=0), SIZE), (dict(B=0), SIZE), (dict(h_q=32, h_kv=5), HEADS), (dict(d=80), HEADDIM),
+    (dict(dt=0), DTYPE), (dict(splits=-1), SIZE),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE),
+])
+def test_decode_append_rejects_bad_arguments(kw, status):
+    assert append_status(**kw) == status
+
+
+def test_decode_append_without_a_gpu_reports_the_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert append_status(sl=A + 4) == DEVICE
 
 
 @pytest.mark.parametrize("B,h_q,h_kv,d,splits", [(64, 32, 8, 128, 0), (3, 8, 4, 64, 64),

@@ -358,3 +358,145 @@ def test_decode_equals_last_row_of_causal_prefill(dev):
     seqlens = torch.full((B,), L, dtype=torch.int32)
     do = run_decode(seqlens, q[:, L - 1:L].contiguous(), kc, vc, dev).cpu()
     check(f64(do), f64(po[:, L - 1:L]), "bf16", "decode vs prefill row L-1")
+
+
+# -------------------------------------------------------------- decode with append
+
+def run_decode_append(seqlens, q, kn, vn, kc, vc, dev, splits=0):
+    """Returns (o, k_cache after, v_cache after) on the CPU; the inputs are not modified."""
+    qd, knd, vnd, sd = q.to(dev), kn.to(dev), vn.to(dev), seqlens.to(dev)
+    kcd, vcd = kc.to(dev).clone(), vc.to(dev).clone()
+    out = torch.full_like(qd, float("nan"))
+    gqa.decode_append(qd, knd, vnd, kcd, vcd, sd, out=out, num_splits=splits)
+    torch.cuda.synchronize()
+    return out.cpu(), kcd.cpu(), vcd.cpu()
+
+
+def append_ref(seqlens, q, kn, vn, kc, vc):
+    return oracle.decode_append(f64(q[:, 0]), f64(kn[:, 0]), f64(vn[:, 0]), f64(kc), f64(vc),
+                                seqlens.numpy())
+
+
+def check_cache_exact(got, ref, what):
+    g = f64(got)
+    assert g.shape == ref.shape, f"{what}: shape {g.shape} vs {ref.shape}"
+    assert np.array_equal(g, ref, equal_nan=True), (
+        f"{what}: {int((~((g == ref) | (np.isnan(g) & np.isnan(ref)))).sum())} elements differ")
+
+
+APPEND_SMALL = [
+    # B, h_q, h_kv, S, d, lengths before the append
+    (6, 32, 8, 1100, 128, [0, 1, 511, 512, 31, 1099]),  # empty cache, block edges, last free row
+    (3, 8, 8, 700, 64, [699, 63, 64]),                  # G = 1
+    (2, 32, 1, 300, 128, [299, 16]),                    # G = 32: two query-head subgroups
+    (2, 16, 2, 1000, 64, [998, 0]),                     # G = 8
+    (4, 12, 4, 96, 128, [95, 94, 32, 31]),              # G = 3
+]
+
+
+@pytest.mark.parametrize("case", APPEND_SMALL, ids=lambda c: "B{}_hq{}_hkv{}_S{}_d{}".format(*c[:5]))
+def test_decode_append_matches_oracle(case, dev):
+    B, h_q, h_kv, S, d, lens = case
+    seed = 3000 + S + h_q
+    _, q, kn, vn, kc, vc = wl.decode_append_inputs(B, h_q, h_kv, S, d, seed, (0, S - 1))
+    seqlens = torch.tensor(lens, dtype=torch.int32)
+    # poison the row the append overwrites and every row after it: the cache
+    # copy of the new row must not be read, nor any row beyond it
+    for b, n in enumerate(lens):
+        kc[b, :, n:] = float("nan")
+        vc[b, :, n:] = float("nan")
+    say(f"decode_append {case} seed {seed}")
+    o_ref, kc_ref, vc_ref = append_ref(seqlens, q, kn, vn, kc, vc)
+    for splits in (0, 1, 7, 1000):
+        out, kc_out, vc_out = run_decode_append(seqlens, q, kn, vn, kc, vc, dev, splits)
+        check(f64(out[:, 0]), o_ref, "bf16", f"decode_append {case} splits {splits}")
+        check_cache_exact(kc_out, kc_ref, f"k_cache after append, splits {splits}")
+        check_cache_exact(vc_out, vc_ref, f"v_cache after append, splits {splits}")
+
+
+def test_decode_append_equals_decode_of_the_grown_cache(dev):
+    # the fused form reads the new rows from k_new/v_new and the plain decode
+    # from the cache; the values, blocks and slices are the same, so the
+    # results are bit-identical
+    B, h_q, h_kv, S, d = 5, 32, 8, 2000, 128
+    seqlens, q, kn, vn, kc, vc = wl.decode_append_inputs(B, h_q, h_kv, S, d, 51, (0, S - 1))
+    seqlens[0] = 0
+    seqlens[1] = S - 1
+    say("decode_append vs decode of the grown cache")
+    out, kc_out, vc_out = run_decode_append(seqlens, q, kn, vn, kc, vc, dev)
+    grown = run_decode(seqlens + 1, q, kc_out, vc_out, dev).cpu()
+    assert torch.equal(out, grown)
+
+
+def test_decode_append_is_deterministic_and_idempotent(dev):
+    seqlens, q, kn, vn, kc, vc = wl.decode_append_inputs(4, 16, 4, 900, 64, 52, (0, 899))
+    say("decode_append determinism")
+    dq, dkn, dvn, ds = q.to(dev), kn.to(dev), vn.to(dev), seqlens.to(dev)
+    kcd, vcd = kc.to(dev), vc.to(dev)
+    o1 = gqa.decode_append(dq, dkn, dvn, kcd, vcd, ds)
+    k1, v1 = kcd.clone(), vcd.clone()
+    o2 = gqa.decode_append(dq, dkn, dvn, kcd, vcd, ds)  # the same rows written again
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(k1, kcd) and torch.equal(v1, vcd)
+
+
+def test_workload_batched_decode_append(dev):
+    w = wl.WORKLOADS["batched_decode_append_bf16"]
+    seqlens, q, kn, vn, kc, vc = wl.workload_inputs(w)
+    say(f"decode_append workload {w.name} ({w.description})")
+    sd = seqlens.to(dev)
+    kcd, vcd = kc.to(dev), vc.to(dev)
+    out = torch.empty_like(q, device=dev)
+    gqa.decode_append(q.to(dev), kn.to(dev), vn.to(dev), kcd, vcd, sd, out=out)
+    torch.cuda.synchronize()
+    out = out.cpu()
+    # the caches at full size: row seqlens[b] of every head now holds the new
+    # row and no other element changed (a property that holds at any size)
+    b_idx = torch.arange(w.B, device=dev)
+    for name, got, before, new in (("k", kcd, kc, kn), ("v", vcd, vc, vn)):
+        exp = before.to(dev)
+        exp[b_idx, :, sd.long()] = new.to(dev)[:, 0]
+        assert torch.equal(got.view(torch.int16), exp.view(torch.int16)), f"{name}_cache"
+        del exp
+    # the output and the whole cache slabs of sampled sequences against the oracle
+    order = torch.argsort(seqlens).tolist()
+    picks = torch.randperm(w.B, generator=torch.Generator().manual_seed(w.seed))[:6].tolist()
+    bsel = sorted({order[0], order[-1], *picks})
+    bi = torch.tensor(bsel)
+    o_ref, kc_ref, vc_ref = append_ref(seqlens[bi], q[bi], kn[bi], vn[bi], kc[bi], vc[bi])
+    check(f64(out[bi, 0]), o_ref, "bf16", f"{w.name}: sequences {bsel}")
+    check_cache_exact(kcd[bi.to(dev)].cpu(), kc_ref, "k_cache slabs of the sampled sequences")
+    check_cache_exact(vcd[bi.to(dev)].cpu(), vc_ref, "v_cache slabs of the sampled sequences")
+
+
+def _at_address_with_bit31_set(t, dev):
+    """A device copy of t placed where bit 31 of the address's low word is set
+    (a 2 GiB + size buffer always holds such a 256-byte-aligned place)."""
+    n = t.numel() * t.element_size()
+    buf = torch.empty((1 << 31) + n + 256, dtype=torch.uint8, device=dev)
+    base = buf.data_ptr()
+    x = base if base & (1 << 31) else (base & ~0xFFFFFFFF) | (1 << 31)
+    x = (x + 255) // 256 * 256
+    assert x & (1 << 31) and x + n <= base + buf.numel()
+    view = buf[x - base:x - base + n].view(t.dtype).view(t.shape)
+    view.copy_(t)
+    return buf, view
+
+
+def test_decode_append_cache_addresses_with_bit31_set(dev):
+    # regression: the new rows' store address was once built from a signed
+    # 32-bit low word, which corrupted caches placed at such addresses
+    B, h_q, h_kv, S, d = 3, 8, 8, 700, 64
+    seqlens, q, kn, vn, kc, vc = wl.decode_append_inputs(B, h_q, h_kv, S, d, 53, (0, S - 1))
+    seqlens[0] = S - 1
+    say("decode_append with caches at addresses whose bit 31 is set")
+    o_ref, kc_ref, vc_ref = append_ref(seqlens, q, kn, vn, kc, vc)
+    kbuf, kcd = _at_address_with_bit31_set(kc, dev)
+    vbuf, vcd = _at_address_with_bit31_set(vc, dev)
+    out = gqa.decode_append(q.to(dev), kn.to(dev), vn.to(dev), kcd, vcd, seqlens.to(dev))
+    torch.cuda.synchronize()
+    check(f64(out[:, 0]), o_ref, "bf16", "decode_append output")
+    check_cache_exact(kcd.cpu(), kc_ref, "k_cache after append")
+    check_cache_exact(vcd.cpu(), vc_ref, "v_cache after append")
+    del kbuf, vbuf
