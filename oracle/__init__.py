@@ -17,7 +17,9 @@ Two independent implementations live here:
 All functions take and return float64 numpy arrays in the layouts of the
 library's entry points: prefill q, o [B, L, h_q, d] and k, v [B, L, h_kv, d];
 decode q, o [B, h_q, d] (the one new position per sequence), caches
-[B, h_kv, S, d] and seqlens [B].
+[B, h_kv, S, d] (token-major form [B, S, h_kv, d]; paged form
+[num_pages, h_kv, page_size, d] with a block table [B, max_blocks]) and
+seqlens [B].
 """
 from __future__ import annotations
 
@@ -76,6 +78,10 @@ def _load():
     lib.gqa_oracle_decode_append.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I]
     lib.gqa_oracle_decode_append.restype = I
     lib.gqa_oracle_decode.restype = I
+    lib.gqa_oracle_decode_token_major.argtypes = [P, P, P, P, P, I, I, I, I, I]
+    lib.gqa_oracle_decode_token_major.restype = I
+    lib.gqa_oracle_decode_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I]
+    lib.gqa_oracle_decode_paged.restype = I
     lib.gqa_oracle_num_threads.argtypes = []
     lib.gqa_oracle_num_threads.restype = I
     _lib = lib
@@ -191,6 +197,46 @@ def decode(q, k_cache, v_cache, seqlens):
                                    h_kv, S, d)
     if rc != 0:
         raise ValueError("oracle decode rejected its arguments (rc=%d)" % rc)
+    return o
+
+
+def decode_token_major(q, k_cache, v_cache, seqlens):
+    """Decode over a token-major cache.  q [B,h_q,d], caches [B,S,h_kv,d], seqlens [B]."""
+    q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
+    sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+    B, h_q, d = q.shape
+    _, S, h_kv, _ = kc.shape
+    if kc.shape != (B, S, h_kv, d) or vc.shape != kc.shape or sl.shape != (B,):
+        raise ValueError("decode_token_major shapes do not match")
+    o = np.empty_like(q)
+    rc = _load().gqa_oracle_decode_token_major(_ptr(q), _ptr(kc), _ptr(vc), _ptr(sl), _ptr(o),
+                                               B, h_q, h_kv, S, d)
+    if rc != 0:
+        raise ValueError("oracle decode_token_major rejected its arguments (rc=%d)" % rc)
+    return o
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seqlens):
+    """Decode over a paged cache with group-aligned pages.
+
+    q [B,h_q,d]; k_pages, v_pages [num_pages, h_kv, page_size, d]; block_table
+    [B, max_blocks] (block i of sequence b holds its positions
+    [i*page_size, (i+1)*page_size)); seqlens [B].
+    """
+    q, kp, vp = _f64(q), _f64(k_pages), _f64(v_pages)
+    bt = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
+    sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+    B, h_q, d = q.shape
+    num_pages, h_kv, page_size, _ = kp.shape
+    if (kp.shape != (num_pages, h_kv, page_size, d) or vp.shape != kp.shape or bt.ndim != 2
+            or bt.shape[0] != B or sl.shape != (B,)):
+        raise ValueError("decode_paged shapes do not match")
+    o = np.empty_like(q)
+    rc = _load().gqa_oracle_decode_paged(_ptr(q), _ptr(kp), _ptr(vp), _ptr(bt), _ptr(sl),
+                                         _ptr(o), B, h_q, h_kv, page_size, bt.shape[1],
+                                         num_pages, d)
+    if rc != 0:
+        raise ValueError("oracle decode_paged rejected its arguments (rc=%d)" % rc)
     return o
 
 

@@ -47,6 +47,17 @@
  *   1/sqrt(d).  A sequence with seqlens[b] == 0 has no visible key; its output
  *   is defined as zero.
  *
+ *   Decode over other cache layouts (the same attention, rows found elsewhere):
+ *   - token-major [B, S, h_kv, d], the kv_cache of "Attention in Qwen,
+ *     DeepSeek and LLaMA3", §2.2 (shape [bs, max_len, n_kv_heads, head_dim]);
+ *   - paged with group-aligned pages, the same page, §4.3: the cache is a
+ *     pool of physical blocks [num_pages][h_kv][page_size][d], each block
+ *     holding page_size consecutive positions of one sequence with one
+ *     contiguous page per group (key/value head), and block_table[b][i] names
+ *     the block that holds positions [i * page_size, (i + 1) * page_size) of
+ *     sequence b.  Logical row j of (b, g) is block_table[b][j / page_size],
+ *     group g, row j % page_size.
+ *
  * Every entry point returns 0 on success and a negative number for a bad
  * argument (it never aborts).  Arrays are dense, row-major, caller-owned.
  */
@@ -296,15 +307,17 @@ int gqa_oracle_prefill_cached(const double *q, const double *k, const double *v,
  * k_cache, v_cache [B][h_kv][S][d]; seqlens [B] with 0 <= seqlens[b] <= S.
  * scale = 1/sqrt(d).
  */
-int gqa_oracle_decode(const double *q, const double *k_cache, const double *v_cache,
-                      const int32_t *seqlens, double *o, int B, int h_q, int h_kv, int S,
-                      int d) {
+/*
+ * Decode over a cache whose element (b, j, g, c) sits at b*sb + j*sj + g*sh + c.
+ */
+static int decode_strided(const double *q, const double *k_cache, const double *v_cache,
+                          const int32_t *seqlens, double *o, int B, int h_q, int h_kv, int S,
+                          int d, long sb, long sj, long sh) {
     if (B <= 0 || S <= 0 || d <= 0) return ORACLE_ERR_ARG;
     if (check_heads(h_q, h_kv)) return ORACLE_ERR_ARG;
     for (int b = 0; b < B; ++b)
         if (seqlens[b] < 0 || seqlens[b] > S) return ORACLE_ERR_ARG;
     const double scale = 1.0 / sqrt((double)d);
-    const long sj = d, sh = (long)S * d, sb = (long)h_kv * sh;
     int failed = 0;
 #pragma omp parallel
     {
@@ -331,6 +344,68 @@ int gqa_oracle_decode(const double *q, const double *k_cache, const double *v_ca
         free(scores);
     }
     return failed ? ORACLE_ERR_NOMEM : 0;
+}
+
+/* Decode over a head-major cache [B][h_kv][S][d]. */
+int gqa_oracle_decode(const double *q, const double *k_cache, const double *v_cache,
+                      const int32_t *seqlens, double *o, int B, int h_q, int h_kv, int S,
+                      int d) {
+    const long sj = d, sh = (long)S * d, sb = (long)h_kv * sh;
+    return decode_strided(q, k_cache, v_cache, seqlens, o, B, h_q, h_kv, S, d, sb, sj, sh);
+}
+
+/* Decode over a token-major cache [B][S][h_kv][d]. */
+int gqa_oracle_decode_token_major(const double *q, const double *k_cache,
+                                  const double *v_cache, const int32_t *seqlens, double *o,
+                                  int B, int h_q, int h_kv, int S, int d) {
+    const long sh = d, sj = (long)h_kv * d, sb = (long)S * sj;
+    return decode_strided(q, k_cache, v_cache, seqlens, o, B, h_q, h_kv, S, d, sb, sj, sh);
+}
+
+/*
+ * Decode over a paged cache: k_pages, v_pages [num_pages][h_kv][page_size][d],
+ * block_table [B][max_blocks].  The logical cache of every sequence is first
+ * gathered row by row into a head-major [B][h_kv][S][d] copy,
+ * S = max_blocks * page_size, then decoded.  seqlens[b] <= S, and every block
+ * that holds a position below seqlens[b] must name a page in [0, num_pages).
+ */
+int gqa_oracle_decode_paged(const double *q, const double *k_pages, const double *v_pages,
+                            const int32_t *block_table, const int32_t *seqlens, double *o,
+                            int B, int h_q, int h_kv, int page_size, int max_blocks,
+                            int num_pages, int d) {
+    if (B <= 0 || page_size <= 0 || max_blocks <= 0 || num_pages <= 0 || d <= 0)
+        return ORACLE_ERR_ARG;
+    if (check_heads(h_q, h_kv)) return ORACLE_ERR_ARG;
+    const long S = (long)max_blocks * page_size;
+    if (S > 0x7fffffff) return ORACLE_ERR_ARG;
+    for (int b = 0; b < B; ++b) {
+        if (seqlens[b] < 0 || seqlens[b] > S) return ORACLE_ERR_ARG;
+        for (int i = 0; i * (long)page_size < seqlens[b]; ++i) {
+            int page = block_table[(long)b * max_blocks + i];
+            if (page < 0 || page >= num_pages) return ORACLE_ERR_ARG;
+        }
+    }
+    size_t n = (size_t)B * h_kv * S * d;
+    double *kc = (double *)calloc(n, sizeof(double));
+    double *vc = (double *)calloc(n, sizeof(double));
+    if (!kc || !vc) {
+        free(kc);
+        free(vc);
+        return ORACLE_ERR_NOMEM;
+    }
+    for (int b = 0; b < B; ++b)
+        for (int g = 0; g < h_kv; ++g)
+            for (int j = 0; j < seqlens[b]; ++j) {
+                long page = block_table[(long)b * max_blocks + j / page_size];
+                long src = ((page * h_kv + g) * page_size + j % page_size) * d;
+                long dst = (((long)b * h_kv + g) * S + j) * d;
+                memcpy(kc + dst, k_pages + src, sizeof(double) * (size_t)d);
+                memcpy(vc + dst, v_pages + src, sizeof(double) * (size_t)d);
+            }
+    int rc = gqa_oracle_decode(q, kc, vc, seqlens, o, B, h_q, h_kv, (int)S, d);
+    free(kc);
+    free(vc);
+    return rc;
 }
 
 /*

@@ -412,13 +412,96 @@ def pin_append_brute_and_tail():
         raise AssertionError("seqlens[b] == S leaves no row to append into: must be rejected")
 
 
+def pin_token_major_brute():
+    """Token-major cache [B, S, h_kv, d] against the brute force over the same
+    rows read out by index, and against the head-major entry on the transposed
+    copy; NaN rows past a length never leak in."""
+    B, h_q, h_kv, d, S = 3, 6, 2, 5, 7
+    q = _rand((B, h_q, d), 180)
+    kt, vt = _rand((B, S, h_kv, d), 181), _rand((B, S, h_kv, d), 182)
+    lens = [0, 3, 7]
+    for b, n in enumerate(lens):
+        kt[b, n:] = np.nan
+        vt[b, n:] = np.nan
+    o = oracle.decode_token_major(q, kt, vt, lens)
+    kg = [[[kt[b, j, g].tolist() for j in range(S)] for g in range(h_kv)] for b in range(B)]
+    vg = [[[vt[b, j, g].tolist() for j in range(S)] for g in range(h_kv)] for b in range(B)]
+    _close(o, brute.decode(q.tolist(), kg, vg, lens), 1e-12, "token-major vs brute force")
+    o2 = oracle.decode(q, np.ascontiguousarray(kt.transpose(0, 2, 1, 3)),
+                       np.ascontiguousarray(vt.transpose(0, 2, 1, 3)), lens)
+    _close(o, o2, 0.0, "token-major vs head-major on the transposed cache")
+
+
+def _scatter_to_pages(kc, vc, lens, page_size, seed, spare=3):
+    """Scatter head-major caches [B, h_kv, S, d] into a shuffled page pool
+    [num_pages, h_kv, page_size, d]; unused pages and rows past a length are NaN."""
+    B, h_kv, S, d = kc.shape
+    max_blocks = -(-S // page_size)
+    need = [-(-n // page_size) for n in lens]
+    num_pages = sum(need) + spare
+    perm = np.random.default_rng(seed).permutation(num_pages)
+    kp = np.full((num_pages, h_kv, page_size, d), np.nan)
+    vp = np.full_like(kp, np.nan)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    nxt = 0
+    for b, n in enumerate(lens):
+        for i in range(need[b]):
+            page = int(perm[nxt])
+            nxt += 1
+            table[b, i] = page
+            rows = min(page_size, n - i * page_size)
+            kp[page, :, :rows] = kc[b, :, i * page_size:i * page_size + rows]
+            vp[page, :, :rows] = vc[b, :, i * page_size:i * page_size + rows]
+    return kp, vp, table
+
+
+def pin_paged_brute():
+    """Paged cache with group-aligned pages ("Attention in Qwen, DeepSeek and
+    LLaMA3", §4.3) on a shuffled pool: equal to the brute force and to the
+    head-major entry over the logical cache; unused pages and rows past a
+    length (NaN) never leak in; a page index outside the pool is rejected."""
+    B, h_q, h_kv, d, S, P = 4, 8, 2, 6, 20, 4
+    q = _rand((B, h_q, d), 190)
+    kc, vc = _rand((B, h_kv, S, d), 191), _rand((B, h_kv, S, d), 192)
+    lens = [0, 5, 8, 19]
+    kp, vp, table = _scatter_to_pages(kc, vc, lens, P, 193)
+    o = oracle.decode_paged(q, kp, vp, table, lens)
+    _close(o, brute.decode(q.tolist(), kc.tolist(), vc.tolist(), lens), 1e-12,
+           "paged vs brute force over the logical cache")
+    _close(o, oracle.decode(q, kc, vc, lens), 0.0, "paged vs head-major over the logical cache")
+    bad = table.copy()
+    bad[3, 0] = kp.shape[0]
+    try:
+        oracle.decode_paged(q, kp, vp, bad, lens)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a page index outside the pool must be rejected")
+
+
+def pin_paged_shared_prefix():
+    """Two sequences whose tables share their first pages (a shared prefix)
+    give the outputs of two separate caches holding the same rows."""
+    h_q, h_kv, d, P = 4, 1, 3, 2
+    q = _rand((2, h_q, d), 195)
+    pool_k, pool_v = _rand((5, h_kv, P, d), 196), _rand((5, h_kv, P, d), 197)
+    table = np.array([[3, 0, 4], [3, 0, 1]], dtype=np.int32)
+    lens = [5, 6]
+    o = oracle.decode_paged(q, pool_k, pool_v, table, lens)
+    kc = np.stack([np.concatenate([pool_k[p] for p in table[b]], axis=1) for b in range(2)])
+    vc = np.stack([np.concatenate([pool_v[p] for p in table[b]], axis=1) for b in range(2)])
+    _close(o, brute.decode(q.tolist(), kc.tolist(), vc.tolist(), lens), 1e-12,
+           "shared-prefix pages vs brute force")
+
+
 ALL_PINS = [pin_hand_2x2, pin_head_map, pin_decode_golden, pin_mha_reduction,
             pin_mqa_reduction, pin_gqa_library, pin_rows_sum_to_one, pin_k_zero_mean,
             pin_causal_row0, pin_identical_heads, pin_invariances, pin_cross_path,
             pin_rows_match_full, pin_decode_tail_ignored, pin_argument_errors,
             pin_chunk_golden, pin_chunked_equals_full, pin_chunk_single_query_is_decode,
             pin_chunk_brute_and_library, pin_chunk_rows_match_full, pin_append_cross_path,
-            pin_append_to_empty_cache, pin_append_brute_and_tail]
+            pin_append_to_empty_cache, pin_append_brute_and_tail, pin_token_major_brute,
+            pin_paged_brute, pin_paged_shared_prefix]
 
 
 def main(argv):

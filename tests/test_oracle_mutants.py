@@ -32,6 +32,10 @@ MUTANTS = {
     "append_not_attended": ("grown[b] = seqlens[b] + 1;", "grown[b] = seqlens[b];"),
     "decode_scale_wrong": ("const double scale = 1.0 / sqrt((double)d);",
                            "const double scale = 1.0 / (double)d;"),
+    "paged_ignores_table": ("long page = block_table[(long)b * max_blocks + j / page_size];",
+                            "long page = (long)b * max_blocks + j / page_size;"),
+    "token_major_read_head_major": ("const long sh = d, sj = (long)h_kv * d, sb = (long)S * sj;",
+                                    "const long sj = d, sh = (long)S * d, sb = (long)h_kv * sh;"),
     "first_head_of_group_only": ("int kvh = kv_head_of(h, h_q, h_kv);\n                int n = seqlens[b];",
                                  "int kvh = 0;\n                int n = seqlens[b];"),
 }
