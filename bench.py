@@ -3,6 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--decode-workload NAME|none] [--append-workload NAME|none]
+                    [--paged-workload NAME|none]
                     [--no-cpu-baseline]
 
 Prints ONE JSON line on stdout.  A step is one call of the prefill entry point
@@ -25,7 +26,8 @@ per second of kernel time, reported under ``decode``.  The decode that appends
 the new token's key/value rows itself is timed the same way on its own
 workload (the same shape, lengths U{1023..8191} before the append) and
 reported under ``decode_append``; its bytes also count the new rows, read
-once and written once.
+once and written once.  The decode over a paged cache (the batched-decode
+inputs in a shuffled pool of 64-row pages) is reported under ``decode_paged``.
 
 ``roofline`` divides the algorithmic work of one launch by the launch's
 average duration measured with HIP events on the launch stream; ``traffic``
@@ -192,9 +194,13 @@ def bench_decode(w, steps, warmup):
     import grouped_query_attention_03_amd as gqa
     dev = torch.device("cuda:0")
     append = w.path == "decode_append"
+    paged = w.path == "decode_paged"
     if append:
         seqlens, q, kn, vn, kc, vc = wl.workload_inputs(w)
         kn, vn = kn.to(dev), vn.to(dev)
+    elif paged:  # kc, vc are the page pools
+        seqlens, q, kc, vc, table = wl.workload_inputs(w)
+        table = table.to(dev)
     else:
         seqlens, q, kc, vc = wl.workload_inputs(w)
     kv_bytes = decode_kv_bytes(w, seqlens)
@@ -207,6 +213,8 @@ def bench_decode(w, steps, warmup):
     def step():
         if append:  # every call writes the same new rows again
             gqa.decode_append(q, kn, vn, kc, vc, seqlens, out=out, workspace=ws)
+        elif paged:
+            gqa.decode_paged(q, kc, vc, table, seqlens, out=out, workspace=ws)
         else:
             gqa.decode(q, kc, vc, seqlens, out=out, workspace=ws)
 
@@ -225,8 +233,9 @@ def bench_decode(w, steps, warmup):
     avg_ms = sum(ev) / len(ev)
     achieved = kv_bytes / (avg_ms * 1e-3) / 1e9
     traffic = recorded_traffic("decode", w.name)
-    what = "decode split (writing the new rows) + log-sum-exp merge" if append else \
-        "decode split + log-sum-exp merge"
+    what = ("decode split (writing the new rows) + log-sum-exp merge" if append else
+            "decode split over pages + log-sum-exp merge" if paged else
+            "decode split + log-sum-exp merge")
     return {
         "workload": w.name,
         "description": w.description,
@@ -322,6 +331,9 @@ def main(argv=None):
     ap.add_argument("--append-workload", default="batched_decode_append_bf16",
                     choices=["none"] + [n for n in wl.WORKLOAD_ORDER
                                         if wl.WORKLOADS[n].path == "decode_append"])
+    ap.add_argument("--paged-workload", default="batched_decode_paged_bf16",
+                    choices=["none"] + [n for n in wl.WORKLOAD_ORDER
+                                        if wl.WORKLOADS[n].path == "decode_paged"])
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--settle-seconds", type=float, default=0.5,
                     help="untimed runs of the step before the warmup, to reach working clocks")
@@ -386,6 +398,12 @@ def main(argv=None):
         line["decode_append"] = bench_decode(aw, args.decode_steps, args.warmup)
         log(f"decode with append: {line['decode_append']['value']:.1f} GB/s, kernel avg "
             f"{line['decode_append']['kernel_ms_avg']:.4f} ms")
+    if args.paged_workload != "none":
+        pw = wl.WORKLOADS[args.paged_workload]
+        log(f"paged decode {pw.name}: {pw.description}; steps {args.decode_steps}")
+        line["decode_paged"] = bench_decode(pw, args.decode_steps, args.warmup)
+        log(f"paged decode: {line['decode_paged']['value']:.1f} GB/s, kernel avg "
+            f"{line['decode_paged']['kernel_ms_avg']:.4f} ms")
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline(w)

@@ -36,7 +36,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    path: str  # "prefill", "prefill_chunk", "decode" or "decode_append"
+    path: str  # "prefill", "prefill_chunk", "decode", "decode_append" or "decode_paged"
     dtype: str  # "f32" or "bf16"
     B: int
     h_q: int
@@ -49,6 +49,7 @@ class Workload:
     std: float = 1.0
     seqlen_range: tuple = (0, 0)  # decode: inclusive [lo, hi] (decode_append: before the append)
     seed: int = 0
+    page_size: int = 0  # decode_paged: rows per page
     description: str = field(default="", compare=False)
 
     @property
@@ -94,14 +95,19 @@ WORKLOADS = {
         S=8192, std=1.0, seqlen_range=(1023, 8191), seed=7,
         description="bf16 decode with the new token's key/value appended, B=64 h_q=32 h_kv=8 "
                     "d=128 S=8192 lengths U{1023..8191} before the append"),
+    "batched_decode_paged_bf16": Workload(
+        "batched_decode_paged_bf16", "decode_paged", "bf16", B=64, h_q=32, h_kv=8, d=128,
+        S=8192, std=1.0, seqlen_range=(1024, 8192), seed=4, page_size=64,
+        description="bf16 decode over a paged cache: the batched-decode inputs in a shuffled "
+                    "pool of 64-row group-aligned pages"),
 }
 
 # Order in which the workloads are listed everywhere: the five of the core
-# path, then the chunked prefill against existing keys and the decode that
-# appends the new token's key/value rows itself.
+# path, then the chunked prefill against existing keys, the decode that
+# appends the new token's key/value rows itself and the decode over pages.
 WORKLOAD_ORDER = ["tiny_prefill_f32", "worked_example_prefill_bf16", "llama2_7b_prefill_bf16",
                   "batched_decode_bf16", "long_context_prefill_bf16", "chunked_prefill_bf16",
-                  "batched_decode_append_bf16"]
+                  "batched_decode_append_bf16", "batched_decode_paged_bf16"]
 
 
 def _draw(gen, shape, std, dtype):
@@ -155,6 +161,37 @@ def decode_append_inputs(B, h_q, h_kv, S, d, seed, seqlen_range, std=1.0,
     return seqlens, q, k_new, v_new, k_cache, v_cache
 
 
+def to_pages(k_cache, v_cache, seqlens, page_size, seed, spare=0):
+    """Move head-major caches [B, h_kv, S, d] into a pool of group-aligned pages.
+
+    Returns (k_pages, v_pages [num_pages, h_kv, page_size, d], block_table
+    [B, max_blocks] int32).  The pages a sequence needs (ceil(len / page_size))
+    take physical slots in a seeded random order; ``spare`` extra pages are
+    left over.  Rows of a page past the sequence end, spare pages and table
+    entries past a sequence's last block hold zeros (table: -1).  Pure data
+    movement: no arithmetic of the method.
+    """
+    B, h_kv, S, d = k_cache.shape
+    max_blocks = -(-S // page_size)
+    need = [-(-int(n) // page_size) for n in seqlens.tolist()]
+    num_pages = sum(need) + spare
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    perm = torch.randperm(num_pages, generator=gen)
+    k_pages = torch.zeros(num_pages, h_kv, page_size, d, dtype=k_cache.dtype)
+    v_pages = torch.zeros_like(k_pages)
+    table = torch.full((B, max_blocks), -1, dtype=torch.int32)
+    nxt = 0
+    for b, n in enumerate(seqlens.tolist()):
+        for i in range(need[b]):
+            page = int(perm[nxt])
+            nxt += 1
+            table[b, i] = page
+            rows = min(page_size, n - i * page_size)
+            k_pages[page, :, :rows] = k_cache[b, :, i * page_size:i * page_size + rows]
+            v_pages[page, :, :rows] = v_cache[b, :, i * page_size:i * page_size + rows]
+    return k_pages, v_pages, table
+
+
 def workload_inputs(w: Workload):
     """Inputs of a named workload, as CPU tensors (see prefill_inputs/decode_inputs)."""
     if w.path == "prefill":
@@ -162,6 +199,11 @@ def workload_inputs(w: Workload):
     if w.path == "prefill_chunk":
         return prefill_chunk_inputs(w.B, w.L, w.Lk, w.h_q, w.h_kv, w.d, w.seed, w.std,
                                     w.torch_dtype())
+    if w.path == "decode_paged":
+        seqlens, q, kc, vc = decode_inputs(w.B, w.h_q, w.h_kv, w.S, w.d, w.seed, w.seqlen_range,
+                                           w.std, w.torch_dtype())
+        kp, vp, table = to_pages(kc, vc, seqlens, w.page_size, w.seed + 1000)
+        return seqlens, q, kp, vp, table
     if w.path == "decode_append":
         return decode_append_inputs(w.B, w.h_q, w.h_kv, w.S, w.d, w.seed, w.seqlen_range, w.std,
                                     w.torch_dtype())

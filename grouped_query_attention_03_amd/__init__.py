@@ -16,6 +16,11 @@ the device is not a gfx950 GPU, the calls raise.
     decode(q, k_cache, v_cache, seqlens, out=None, workspace=None, num_splits=0)
         q [B, 1, h_q, d] bf16, caches [B, h_kv, S, d] bf16, seqlens [B] int32
         -> o [B, 1, h_q, d].
+    decode_token_major(q, k_cache, v_cache, seqlens, ...)
+        as decode, with caches [B, S, h_kv, d].
+    decode_paged(q, k_pages, v_pages, block_table, seqlens, ...)
+        as decode, over pools [num_pages, h_kv, page_size, d] and a block
+        table [B, max_blocks].
     decode_append(q, k_new, v_new, k_cache, v_cache, seqlens, ...)
         writes k_new/v_new [B, 1, h_kv, d] at cache row seqlens[b], then attends
         over rows [0, seqlens[b] + 1).
@@ -64,6 +69,10 @@ def lib() -> ctypes.CDLL:
     L.gqa_decode_append.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P,
                                     ctypes.c_size_t, P]
     L.gqa_decode_append.restype = I
+    L.gqa_decode_token_major.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, ctypes.c_size_t, P]
+    L.gqa_decode_token_major.restype = I
+    L.gqa_decode_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, ctypes.c_size_t, P]
+    L.gqa_decode_paged.restype = I
     L.gqa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     L.gqa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.gqa_decode_default_splits.argtypes = []
@@ -232,4 +241,68 @@ def decode_append(q, k_new, v_new, k_cache, v_cache, seqlens, *, out=None, works
                                  workspace.numel() * workspace.element_size(), _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_decode_append")
+    return out
+
+
+def _decode_out_ws(q, out, workspace, B, h_q, h_kv, d, num_splits):
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", 4)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    need = decode_workspace_bytes(B, h_q, h_kv, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    return out, workspace
+
+
+def decode_token_major(q, k_cache, v_cache, seqlens, *, out=None, workspace=None,
+                       num_splits: int = 0):
+    """Decode over a token-major cache: q [B,1,h_q,d], caches [B,S,h_kv,d] bf16,
+    seqlens [B] int32 -> o [B,1,h_q,d]."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _check(t, n, 4)
+    _check(seqlens, "seqlens", 1)
+    B, one, h_q, d = q.shape
+    _, S, h_kv, _ = k_cache.shape
+    if one != 1 or tuple(k_cache.shape) != (B, S, h_kv, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("need q [B, 1, h_q, d] and caches [B, S, h_kv, d]")
+    if seqlens.dtype != torch.int32 or seqlens.shape[0] != B:
+        raise ValueError("seqlens must be int32 [B]")
+    out, workspace = _decode_out_ws(q, out, workspace, B, h_q, h_kv, d, num_splits)
+    st = lib().gqa_decode_token_major(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                      seqlens.data_ptr(), out.data_ptr(), B, h_q, h_kv, S, d,
+                                      _dtype_code(q), int(num_splits), workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(), _stream(q))
+    if st != 0:
+        raise GQAError(st, "gqa_decode_token_major")
+    return out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seqlens, *, out=None, workspace=None,
+                 num_splits: int = 0):
+    """Decode over a paged cache with group-aligned pages: q [B,1,h_q,d], pools
+    [num_pages, h_kv, page_size, d] bf16, block_table [B, max_blocks] int32,
+    seqlens [B] int32 -> o [B,1,h_q,d]."""
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
+        _check(t, n, 4)
+    _check(block_table, "block_table", 2)
+    _check(seqlens, "seqlens", 1)
+    B, one, h_q, d = q.shape
+    _, h_kv, page_size, _ = k_pages.shape
+    if one != 1 or k_pages.shape[3] != d or v_pages.shape != k_pages.shape:
+        raise ValueError("need q [B, 1, h_q, d] and pools [num_pages, h_kv, page_size, d]")
+    if block_table.dtype != torch.int32 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_blocks]")
+    if seqlens.dtype != torch.int32 or seqlens.shape[0] != B:
+        raise ValueError("seqlens must be int32 [B]")
+    out, workspace = _decode_out_ws(q, out, workspace, B, h_q, h_kv, d, num_splits)
+    st = lib().gqa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                                block_table.data_ptr(), seqlens.data_ptr(), out.data_ptr(), B,
+                                h_q, h_kv, page_size, block_table.shape[1], d, _dtype_code(q),
+                                int(num_splits), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream(q))
+    if st != 0:
+        raise GQAError(st, "gqa_decode_paged")
     return out

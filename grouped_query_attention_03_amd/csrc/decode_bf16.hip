@@ -251,12 +251,14 @@ constexpr int dc_slots() {
 }
 
 // QD = 1 KiB loads per block for the query tile (ceil(query heads x 2d / 1024)).
-// APPEND: the new token's key/value rows (k_new, v_new) are attended as row
-// seqlens[b] and written into that cache row by the wave that owns the
-// segment's last block (query-head subgroup 0 only); no wave reads that cache
-// row, so the write races with nothing.
-template <int D, int QD, bool APPEND>
+// LAYOUT: where row j of (sequence b, key/value head g) sits (DecodeLayout).
+// APPEND (head-major only): the new token's key/value rows (k_new, v_new) are
+// attended as row seqlens[b] and written into that cache row by the wave that
+// owns the segment's last block (query-head subgroup 0 only); no wave reads
+// that cache row, so the write races with nothing.
+template <int D, int QD, int LAYOUT, bool APPEND>
 __global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs a) {
+    static_assert(!APPEND || LAYOUT == kLayoutHeadMajor, "append writes a head-major cache");
     using Lay = DcLayout<D>;
     constexpr int DB = D / 16;  // 16-wide blocks of the head dimension
     constexpr int OPS = QD + 2 * Lay::KV_DMA;  // memory instructions issued per block
@@ -310,17 +312,32 @@ __global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs 
     // clamped to its last head), K rows, V rows (clamped to the last valid key)
     auto issue = [&](const Cur &u, GQA_LDS char *qt, GQA_LDS char *kt, GQA_LDS char *vt) {
         const int kvh = u.seg / a.n_qsub, qs = u.seg % a.n_qsub;
-        const size_t slab = ((size_t)u.b * a.h_kv + kvh) * (size_t)a.S * D;
         const int kend = load_const(a.seqlens, u.b) + a.extra;
         const int head0 = kvh * a.G + 16 * qs;
+        const int key0 = DC_BK * u.blk;
+        // rows key0 .. key0 + 31 of (b, kvh): base, row stride and the block's
+        // rows as seen by dc_dma_rows (first row, last valid row)
+        size_t base, stride = D;
+        int row0 = key0, last = kend - 1;
+        if (LAYOUT == kLayoutHeadMajor) {
+            base = ((size_t)u.b * a.h_kv + kvh) * (size_t)a.S * D;
+        } else if (LAYOUT == kLayoutTokenMajor) {
+            base = (size_t)u.b * a.S * a.h_kv * D + (size_t)kvh * D;
+            stride = (size_t)a.h_kv * D;
+        } else {  // paged: the block lies inside one page (page_size is a multiple of 32)
+            const int page = load_const(a.block_table, u.b * a.max_blocks + key0 / a.page_size);
+            base = (((size_t)page * a.h_kv + kvh) * a.page_size + key0 % a.page_size) * D;
+            row0 = 0;
+            last = kend - 1 - key0;
+        }
         const size_t new_row = ((size_t)u.b * a.h_kv + kvh) * D;  // in k_new / v_new
         dc_dma_rows<D, false>(static_cast<const __bf16 *>(a.q) + ((size_t)u.b * a.h_q + head0) * D, D, 0,
                               heads_in(u) - 1, QD, qt);
-        dc_dma_rows<D, false, APPEND>(static_cast<const __bf16 *>(a.k_cache) + slab, D, DC_BK * u.blk,
-                                      kend - 1, Lay::KV_DMA, kt,
+        dc_dma_rows<D, false, APPEND>(static_cast<const __bf16 *>(a.k_cache) + base, stride, row0,
+                                      last, Lay::KV_DMA, kt,
                                       static_cast<const __bf16 *>(a.k_new) + new_row);
-        dc_dma_rows<D, true, APPEND>(static_cast<const __bf16 *>(a.v_cache) + slab, D, DC_BK * u.blk,
-                                     kend - 1, Lay::KV_DMA, vt,
+        dc_dma_rows<D, true, APPEND>(static_cast<const __bf16 *>(a.v_cache) + base, stride, row0,
+                                     last, Lay::KV_DMA, vt,
                                      static_cast<const __bf16 *>(a.v_new) + new_row);
     };
     // APPEND: copy the new key and value rows into cache row seqlens[b], one
@@ -501,8 +518,18 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 template <int D, int QD>
 void launch_split(const DecodeArgs &a, hipStream_t stream) {
     const dim3 grid((a.NW + DC_WAVES - 1) / DC_WAVES), block(DC_THREADS);
-    if (a.extra) hipLaunchKernelGGL((decode_split_kernel<D, QD, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((decode_split_kernel<D, QD, false>), grid, block, 0, stream, a);
+    if (a.layout == kLayoutTokenMajor)
+        hipLaunchKernelGGL((decode_split_kernel<D, QD, kLayoutTokenMajor, false>), grid, block, 0,
+                           stream, a);
+    else if (a.layout == kLayoutPaged)
+        hipLaunchKernelGGL((decode_split_kernel<D, QD, kLayoutPaged, false>), grid, block, 0,
+                           stream, a);
+    else if (a.extra)
+        hipLaunchKernelGGL((decode_split_kernel<D, QD, kLayoutHeadMajor, true>), grid, block, 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<D, QD, kLayoutHeadMajor, false>), grid, block, 0,
+                           stream, a);
 }
 
 int launch_decode_bf16(const DecodeArgs &a, int d, hipStream_t stream) {

@@ -149,12 +149,24 @@ namespace {
 
 // Shared by both decode entry points; k_new/v_new non-null selects the append
 // form (the new rows are written at seqlens[b] and attended as well).
+// Paged caches pass layout kLayoutPaged, the block table and its shape, and
+// S = 0 (the logical capacity is max_blocks * page_size).
 gqa_status decode_impl(const void *q, const void *k_new, const void *v_new, const void *k_cache,
                        const void *v_cache, const int32_t *seqlens, void *o, int B, int h_q,
                        int h_kv, int S, int d, gqa_dtype dt, int num_splits, void *workspace,
-                       size_t workspace_bytes, void *hip_stream) {
+                       size_t workspace_bytes, void *hip_stream, int layout = gqa::kLayoutHeadMajor,
+                       const int32_t *block_table = nullptr, int page_size = 0,
+                       int max_blocks = 0) {
     const bool append = k_new != nullptr || v_new != nullptr;
     if (!q || !k_cache || !v_cache || !seqlens || !o) return GQA_ERR_NULL_POINTER;
+    if (layout == gqa::kLayoutPaged) {
+        if (!block_table) return GQA_ERR_NULL_POINTER;
+        if ((reinterpret_cast<uintptr_t>(block_table) & 3u) != 0) return GQA_ERR_ALIGNMENT;
+        if (page_size <= 0 || page_size % 32 != 0 || max_blocks <= 0) return GQA_ERR_SIZE;
+        if ((int64_t)max_blocks * page_size > 0x7fffffff) return GQA_ERR_SIZE;
+        if ((int64_t)B * max_blocks > 0x7fffffff) return GQA_ERR_SIZE;
+        S = max_blocks * page_size;
+    }
     if (append && (!k_new || !v_new)) return GQA_ERR_NULL_POINTER;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
         (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
@@ -190,6 +202,10 @@ gqa_status decode_impl(const void *q, const void *k_new, const void *v_new, cons
     a.lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
                                       round_up_256(slots * 16 * d * sizeof(float)));
     a.c = (float)(1.4426950408889634 / sqrt((double)d));
+    a.layout = layout;
+    a.block_table = block_table;
+    a.page_size = page_size;
+    a.max_blocks = max_blocks;
 
     gqa_status st = check_device();
     if (st != GQA_OK) return st;
@@ -207,6 +223,24 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
                       void *hip_stream) {
     return decode_impl(q, nullptr, nullptr, k_cache, v_cache, seqlens, o, B, h_q, h_kv, S, d, dt,
                        num_splits, workspace, workspace_bytes, hip_stream);
+}
+
+gqa_status gqa_decode_token_major(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *seqlens, void *o, int B, int h_q, int h_kv, int S,
+                                  int d, gqa_dtype dt, int num_splits, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream) {
+    return decode_impl(q, nullptr, nullptr, k_cache, v_cache, seqlens, o, B, h_q, h_kv, S, d, dt,
+                       num_splits, workspace, workspace_bytes, hip_stream, gqa::kLayoutTokenMajor);
+}
+
+gqa_status gqa_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                            const int32_t *block_table, const int32_t *seqlens, void *o, int B,
+                            int h_q, int h_kv, int page_size, int max_blocks, int d, gqa_dtype dt,
+                            int num_splits, void *workspace, size_t workspace_bytes,
+                            void *hip_stream) {
+    return decode_impl(q, nullptr, nullptr, k_pages, v_pages, seqlens, o, B, h_q, h_kv, 0, d, dt,
+                       num_splits, workspace, workspace_bytes, hip_stream, gqa::kLayoutPaged,
+                       block_table, page_size, max_blocks);
 }
 
 gqa_status gqa_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache,

@@ -25,6 +25,13 @@ struct PrefillArgs {
 // resident (its LDS ring fills the CU), 256 CUs x kDecodeWaves waves run at once.
 constexpr int kDecodeWaves = 4;
 
+// Where row j of (sequence b, key/value head g) of a decode cache sits.
+enum DecodeLayout {
+    kLayoutHeadMajor = 0,   // [B][h_kv][S][d]
+    kLayoutTokenMajor = 1,  // [B][S][h_kv][d]
+    kLayoutPaged = 2        // pool [pages][h_kv][page_size][d], block_table[b][j / page_size]
+};
+
 struct DecodeArgs {
     const void *q, *k_cache, *v_cache;
     const void *k_new, *v_new;  // [B, h_kv, d] rows appended at seqlens[b] (append form), else null
@@ -37,6 +44,9 @@ struct DecodeArgs {
     int NW;        // waves in the split pass (number of slices of the block list)
     int n_qsub;    // query-head subgroups of at most 16 heads per key/value head
     float c;       // log2(e) / sqrt(d)
+    int layout;    // DecodeLayout of k_cache / v_cache
+    const int32_t *block_table;  // paged: [B][max_blocks] page of each block of page_size rows
+    int page_size, max_blocks;   // paged: page_size a multiple of 32
 };
 
 int launch_prefill_bf16(const PrefillArgs &a, int d, bool causal, hipStream_t stream);

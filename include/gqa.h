@@ -120,6 +120,47 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
                       void *hip_stream);
 
 /*
+ * Decode over a token-major cache: as gqa_decode, with the cache laid out
+ * [B, S, h_kv, d] (the kv_cache shape of "Attention in Qwen, DeepSeek and
+ * LLaMA3", §2.2, and the layout prefill takes its k and v in, so a prefill's
+ * keys and values can be attended by later tokens without a transpose).
+ *   k_cache, v_cache : [B, S, h_kv, d] bf16; rows of one key/value head are
+ *                      h_kv * d elements apart.
+ *   Everything else, the workspace and errors as gqa_decode.
+ */
+gqa_status gqa_decode_token_major(const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *seqlens, void *o, int B, int h_q, int h_kv, int S,
+                                  int d, gqa_dtype dt, int num_splits, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream);
+
+/*
+ * Decode over a paged cache with group-aligned pages ("Attention in Qwen,
+ * DeepSeek and LLaMA3", §4.3: one page per group, so the rows of one
+ * key/value head inside a page are contiguous).
+ *   k_pages, v_pages : [num_pages, h_kv, page_size, d] bf16: physical block p
+ *                      holds page_size consecutive positions of one sequence,
+ *                      one contiguous page per key/value head.
+ *   block_table      : [B, max_blocks] int32 on the device; block_table[b][i]
+ *                      is the physical block holding positions
+ *                      [i * page_size, (i + 1) * page_size) of sequence b.
+ *                      Entries for blocks at or beyond ceil(seqlens[b] /
+ *                      page_size) are never read; the others must name blocks
+ *                      of the pool (not checked on the device).  Blocks may be
+ *                      shared between sequences (a common prefix).
+ *   seqlens          : [B] int32 on the device, each in [0, max_blocks * page_size].
+ *   page_size        : a positive multiple of 32; max_blocks > 0;
+ *                      max_blocks * page_size and B * max_blocks below 2^31,
+ *                      else GQA_ERR_SIZE.
+ *   Everything else, the workspace and errors as gqa_decode; a NULL or
+ *   misaligned (4-byte) block_table gives GQA_ERR_NULL_POINTER / GQA_ERR_ALIGNMENT.
+ */
+gqa_status gqa_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                            const int32_t *block_table, const int32_t *seqlens, void *o, int B,
+                            int h_q, int h_kv, int page_size, int max_blocks, int d, gqa_dtype dt,
+                            int num_splits, void *workspace, size_t workspace_bytes,
+                            void *hip_stream);
+
+/*
  * Decode with append: the new token's key and value rows are written into the
  * cache, then the token attends over the grown cache ("What is Grouped-Query
  * Attention", §3.2: append, then attend), in one call.

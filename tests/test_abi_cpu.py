@@ -29,6 +29,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("gqa_prefill", "gqa_prefill_chunk", "gqa_decode", "gqa_decode_append",
+              "gqa_decode_token_major", "gqa_decode_paged",
               "gqa_decode_workspace_bytes",
               "gqa_decode_default_splits", "gqa_status_string"):
         assert n in names
@@ -157,6 +158,53 @@ def test_decode_append_without_a_gpu_reports_the_device():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert append_status(sl=A + 4) == DEVICE
+
+
+def token_major_status(q=A, kc=A, vc=A, sl=A, o=A, B=4, h_q=32, h_kv=8, S=1024, d=128, dt=1,
+                       splits=0, ws=A, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = (gqa.decode_workspace_bytes(B, h_q, h_kv, d, splits)
+                    if d in (64, 128) and h_q % h_kv == 0 else 1 << 30)
+    return gqa.lib().gqa_decode_token_major(q, kc, vc, sl, o, B, h_q, h_kv, S, d, dt, splits, ws,
+                                            ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sl=None), NULLP), (dict(kc=None), NULLP), (dict(vc=MIS), ALIGN),
+    (dict(S=0), SIZE), (dict(h_q=32, h_kv=5), HEADS), (dict(d=80), HEADDIM), (dict(dt=0), DTYPE),
+    (dict(ws=None), WORKSPACE),
+])
+def test_decode_token_major_rejects_bad_arguments(kw, status):
+    assert token_major_status(**kw) == status
+
+
+def paged_status(q=A, kp=A, vp=A, bt=A, sl=A, o=A, B=4, h_q=32, h_kv=8, P=64, mb=16, d=128,
+                 dt=1, splits=0, ws=A, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = (gqa.decode_workspace_bytes(B, h_q, h_kv, d, splits)
+                    if d in (64, 128) and h_q % h_kv == 0 else 1 << 30)
+    return gqa.lib().gqa_decode_paged(q, kp, vp, bt, sl, o, B, h_q, h_kv, P, mb, d, dt, splits,
+                                      ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bt=None), NULLP), (dict(kp=None), NULLP), (dict(sl=None), NULLP),
+    (dict(bt=A + 2), ALIGN), (dict(vp=MIS), ALIGN),
+    (dict(P=0), SIZE), (dict(P=48), SIZE), (dict(P=-32), SIZE), (dict(P=16), SIZE),
+    (dict(mb=0), SIZE), (dict(P=1 << 16, mb=1 << 15), SIZE), (dict(B=1 << 20, mb=1 << 12), SIZE),
+    (dict(B=0), SIZE), (dict(h_q=32, h_kv=5), HEADS), (dict(d=80), HEADDIM), (dict(dt=0), DTYPE),
+    (dict(ws_bytes=100), WORKSPACE),
+])
+def test_decode_paged_rejects_bad_arguments(kw, status):
+    assert paged_status(**kw) == status
+
+
+def test_decode_layouts_without_a_gpu_report_the_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert token_major_status(sl=A + 4) == DEVICE
+    assert paged_status(bt=A + 4, sl=A + 8, P=32, mb=1) == DEVICE
 
 
 @pytest.mark.parametrize("B,h_q,h_kv,d,splits", [(64, 32, 8, 128, 0), (3, 8, 4, 64, 64),

@@ -500,3 +500,134 @@ def test_decode_append_cache_addresses_with_bit31_set(dev):
     check_cache_exact(kcd.cpu(), kc_ref, "k_cache after append")
     check_cache_exact(vcd.cpu(), vc_ref, "v_cache after append")
     del kbuf, vbuf
+
+
+# ----------------------------------------------------- decode over other layouts
+
+TOKEN_MAJOR = [
+    # B, h_q, h_kv, S, d, lengths
+    (4, 32, 8, 700, 128, [0, 1, 333, 700]),
+    (3, 8, 8, 300, 64, [300, 64, 65]),     # G = 1
+    (2, 32, 1, 200, 128, [200, 17]),       # G = 32
+    (3, 12, 4, 96, 64, [96, 95, 31]),      # G = 3
+]
+
+
+@pytest.mark.parametrize("case", TOKEN_MAJOR, ids=lambda c: "B{}_hq{}_hkv{}_S{}_d{}".format(*c[:5]))
+def test_decode_token_major_matches_oracle(case, dev):
+    B, h_q, h_kv, S, d, lens = case
+    seed = 4000 + S + h_q
+    _, q, kc, vc = wl.decode_inputs(B, h_q, h_kv, S, d, seed, (1, S))
+    seqlens = torch.tensor(lens, dtype=torch.int32)
+    kt = kc.transpose(1, 2).contiguous()  # [B, S, h_kv, d]
+    vt = vc.transpose(1, 2).contiguous()
+    for b, n in enumerate(lens):
+        kt[b, n:] = float("nan")
+        vt[b, n:] = float("nan")
+    say(f"decode token-major {case} seed {seed}")
+    ref = oracle.decode_token_major(f64(q[:, 0]), f64(kt), f64(vt), seqlens.numpy())
+    qd, ktd, vtd, sd = q.to(dev), kt.to(dev), vt.to(dev), seqlens.to(dev)
+    for splits in (0, 5, 999):
+        out = gqa.decode_token_major(qd, ktd, vtd, sd, num_splits=splits)
+        torch.cuda.synchronize()
+        check(f64(out.cpu()[:, 0]), ref, "bf16", f"token-major {case} splits {splits}")
+    # the same blocks and arithmetic as the head-major entry on the transposed cache
+    hm = run_decode(seqlens, q, kt.transpose(1, 2).contiguous(), vt.transpose(1, 2).contiguous(),
+                    dev).cpu()
+    assert torch.equal(gqa.decode_token_major(qd, ktd, vtd, sd).cpu(), hm)
+
+
+def test_decode_token_major_over_prefill_keys(dev):
+    # prefill's k/v [B, L, h_kv, d] are a token-major cache as they stand: the
+    # last position's decode equals the causal prefill's last row
+    B, L, h_q, h_kv, d = 2, 777, 32, 8, 128
+    q, k, v = wl.prefill_inputs(B, L, h_q, h_kv, d, 43, 1.0, torch.bfloat16)
+    say("token-major decode over prefill keys vs causal prefill last row")
+    po = run_prefill(q, k, v, True, 1 / math.sqrt(d), dev).cpu()
+    seqlens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    do = gqa.decode_token_major(q[:, L - 1:L].contiguous().to(dev), k.to(dev), v.to(dev), seqlens)
+    torch.cuda.synchronize()
+    check(f64(do.cpu()), f64(po[:, L - 1:L]), "bf16", "token-major decode vs prefill row L-1")
+
+
+PAGED = [
+    # B, h_q, h_kv, S, d, page_size, lengths
+    (5, 32, 8, 600, 128, 64, [0, 1, 64, 65, 600]),
+    (3, 8, 8, 300, 64, 32, [300, 31, 33]),        # G = 1, smallest pages
+    (2, 32, 1, 512, 128, 256, [512, 257]),        # G = 32, large pages
+    (4, 12, 4, 200, 64, 96, [200, 96, 95, 1]),    # G = 3, pages of 3 blocks
+]
+
+
+@pytest.mark.parametrize("case", PAGED, ids=lambda c: "B{}_hq{}_hkv{}_S{}_d{}_P{}".format(*c[:6]))
+def test_decode_paged_matches_oracle(case, dev):
+    B, h_q, h_kv, S, d, P, lens = case
+    seed = 5000 + S + h_q + P
+    _, q, kc, vc = wl.decode_inputs(B, h_q, h_kv, S, d, seed, (1, S))
+    seqlens = torch.tensor(lens, dtype=torch.int32)
+    kp, vp, table = wl.to_pages(kc, vc, seqlens, P, seed, spare=3)
+    # rows past each length, spare pages: poisoned, never read
+    used = set(int(x) for x in table.flatten().tolist() if x >= 0)
+    for page in range(kp.shape[0]):
+        if page not in used:
+            kp[page] = float("nan")
+            vp[page] = float("nan")
+    for b, n in enumerate(lens):
+        if n % P:
+            last = int(table[b, (n - 1) // P])
+            kp[last, :, n % P:] = float("nan")
+            vp[last, :, n % P:] = float("nan")
+    say(f"decode paged {case} seed {seed} pages {kp.shape[0]}")
+    ref = oracle.decode_paged(f64(q[:, 0]), f64(kp), f64(vp), table.numpy(), seqlens.numpy())
+    qd, kpd, vpd, td, sd = q.to(dev), kp.to(dev), vp.to(dev), table.to(dev), seqlens.to(dev)
+    for splits in (0, 3, 1000):
+        out = gqa.decode_paged(qd, kpd, vpd, td, sd, num_splits=splits)
+        torch.cuda.synchronize()
+        check(f64(out.cpu()[:, 0]), ref, "bf16", f"paged {case} splits {splits}")
+    # bit-identical to the head-major entry over the logical cache
+    hm = run_decode(seqlens, q, kc, vc, dev).cpu()
+    assert torch.equal(gqa.decode_paged(qd, kpd, vpd, td, sd).cpu(), hm)
+
+
+def test_decode_paged_shared_prefix(dev):
+    # two sequences whose tables start with the same pages
+    h_q, h_kv, d, P = 16, 2, 128, 32
+    g = torch.Generator().manual_seed(61)
+    pool_k = torch.randn(6, h_kv, P, d, generator=g).to(torch.bfloat16)
+    pool_v = torch.randn(6, h_kv, P, d, generator=g).to(torch.bfloat16)
+    q = torch.randn(2, 1, h_q, d, generator=g).to(torch.bfloat16)
+    table = torch.tensor([[4, 0, 5, -1], [4, 0, 2, 3]], dtype=torch.int32)
+    lens = torch.tensor([80, 127], dtype=torch.int32)
+    say("decode paged shared prefix")
+    ref = oracle.decode_paged(f64(q[:, 0]), f64(pool_k), f64(pool_v), table.numpy(), lens.numpy())
+    out = gqa.decode_paged(q.to(dev), pool_k.to(dev), pool_v.to(dev), table.to(dev), lens.to(dev))
+    torch.cuda.synchronize()
+    check(f64(out.cpu()[:, 0]), ref, "bf16", "paged shared prefix")
+
+
+def test_workload_batched_decode_paged(dev):
+    w = wl.WORKLOADS["batched_decode_paged_bf16"]
+    seqlens, q, kp, vp, table = wl.workload_inputs(w)
+    say(f"decode workload {w.name} ({w.description}) pages {kp.shape[0]}")
+    out = gqa.decode_paged(q.to(dev), kp.to(dev), vp.to(dev), table.to(dev), seqlens.to(dev))
+    torch.cuda.synchronize()
+    out = out.cpu()
+    # the same inputs as batched_decode_bf16, so the contiguous decode gives the same bits
+    dw = wl.WORKLOADS["batched_decode_bf16"]
+    s2, q2, kc, vc = wl.workload_inputs(dw)
+    assert torch.equal(s2, seqlens) and torch.equal(q2, q)
+    assert torch.equal(out, run_decode(s2, q2, kc, vc, dev).cpu())
+    order = torch.argsort(seqlens).tolist()
+    picks = torch.randperm(w.B, generator=torch.Generator().manual_seed(w.seed))[:4].tolist()
+    bsel = sorted({order[0], order[-1], *picks})
+    bi = torch.tensor(bsel)
+    # the oracle gets only the pages the sampled sequences use, renumbered
+    sub = table[bi]
+    used = sorted(set(int(x) for x in sub.flatten().tolist() if x >= 0))
+    remap = {p: i for i, p in enumerate(used)}
+    sub = torch.tensor([[remap.get(int(x), -1) for x in row] for row in sub.tolist()],
+                       dtype=torch.int32)
+    idx = torch.tensor(used)
+    ref = oracle.decode_paged(f64(q[bi, 0]), f64(kp[idx]), f64(vp[idx]), sub.numpy(),
+                              seqlens[bi].numpy())
+    check(f64(out[bi, 0]), ref, "bf16", f"{w.name}: sequences {bsel}")
