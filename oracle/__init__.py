@@ -82,6 +82,11 @@ def _load():
     lib.gqa_oracle_decode_token_major.restype = I
     lib.gqa_oracle_decode_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I]
     lib.gqa_oracle_decode_paged.restype = I
+    lib.gqa_oracle_rope.argtypes = [P, P, P, P, I, I, I, I]
+    lib.gqa_oracle_rope.restype = I
+    lib.gqa_oracle_prefill_rope.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I,
+                                            ctypes.c_double]
+    lib.gqa_oracle_prefill_rope.restype = I
     lib.gqa_oracle_num_threads.argtypes = []
     lib.gqa_oracle_num_threads.restype = I
     _lib = lib
@@ -198,6 +203,37 @@ def decode(q, k_cache, v_cache, seqlens):
     if rc != 0:
         raise ValueError("oracle decode rejected its arguments (rc=%d)" % rc)
     return o
+
+
+def rope(x, cos, sin):
+    """Rotary embedding of x [B, L, H, d] with tables cos, sin [L, d/2] (see the C source)."""
+    x, ct, st = _f64(x), _f64(cos), _f64(sin)
+    B, L, H, d = x.shape
+    if d % 2 or ct.shape != (L, d // 2) or st.shape != ct.shape:
+        raise ValueError("rope shapes do not match")
+    out = np.empty_like(x)
+    rc = _load().gqa_oracle_rope(_ptr(x), _ptr(ct), _ptr(st), _ptr(out), B, L, H, d)
+    if rc != 0:
+        raise ValueError("oracle rope rejected its arguments (rc=%d)" % rc)
+    return out
+
+
+def prefill_rope(q, k, v, cos, sin, causal, scale):
+    """Prefill with q and k rotated first.  Returns (o [B,L,h_q,d], k_rot [B,L,h_kv,d])."""
+    q, k, v, ct, st = _f64(q), _f64(k), _f64(v), _f64(cos), _f64(sin)
+    B, L, h_q, d = q.shape
+    h_kv = k.shape[2]
+    if (k.shape != (B, L, h_kv, d) or v.shape != k.shape or ct.shape != (L, d // 2)
+            or st.shape != ct.shape):
+        raise ValueError("prefill_rope shapes do not match")
+    o = np.empty_like(q)
+    k_rot = np.empty_like(k)
+    rc = _load().gqa_oracle_prefill_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(ct), _ptr(st), _ptr(o),
+                                         _ptr(k_rot), B, L, h_q, h_kv, d, int(bool(causal)),
+                                         float(scale))
+    if rc != 0:
+        raise ValueError("oracle prefill_rope rejected its arguments (rc=%d)" % rc)
+    return o, k_rot
 
 
 def decode_token_major(q, k_cache, v_cache, seqlens):

@@ -93,3 +93,22 @@ def decode(q, k_cache, v_cache, seqlens):
             row.append(out)
         o.append(row)
     return o
+
+
+def rope(x, cos, sin):
+    """x [B][L][H][d], cos/sin [L][d/2] -> rotated copy: for pair i at position p,
+    out[i] = x[2i] cos - x[2i+1] sin and out[d/2 + i] = x[2i] sin + x[2i+1] cos
+    ("Attention in Qwen, DeepSeek and LLaMA3", §1)."""
+    out = []
+    for xb in x:
+        ob = []
+        for p, xp in enumerate(xb):
+            op = []
+            for vec in xp:
+                half = len(vec) // 2
+                first = [vec[2 * i] * cos[p][i] - vec[2 * i + 1] * sin[p][i] for i in range(half)]
+                second = [vec[2 * i] * sin[p][i] + vec[2 * i + 1] * cos[p][i] for i in range(half)]
+                op.append(first + second)
+            ob.append(op)
+        out.append(ob)
+    return out

@@ -58,6 +58,17 @@
  *     sequence b.  Logical row j of (b, g) is block_table[b][j / page_size],
  *     group g, row j % page_size.
  *
+ *   Rotary position embedding before the scores ("Attention in Qwen,
+ *   DeepSeek and LLaMA3", §1, apply_rotary_pos_emb; the model-family table
+ *   of "Modern LLM architecture (1)", §1 lists RoPE for every GQA family).
+ *   For a vector x of even length d at position p, with tables cos, sin
+ *   [L][d/2] indexed by position:
+ *     out[i]       = x[2i] cos[p][i] - x[2i+1] sin[p][i]
+ *     out[d/2 + i] = x[2i] sin[p][i] + x[2i+1] cos[p][i]      (0 <= i < d/2)
+ *   -- the even/odd pairs rotated, the two results concatenated along the
+ *   last axis as the page writes it.  q and k are rotated, v is not; then the
+ *   attention above.
+ *
  * Every entry point returns 0 on success and a negative number for a bad
  * argument (it never aborts).  Arrays are dense, row-major, caller-owned.
  */
@@ -289,6 +300,48 @@ int gqa_oracle_prefill(const double *q, const double *k, const double *v, double
                        int L, int h_q, int h_kv, int d, int causal, double scale,
                        double *probs) {
     return prefill_general(q, k, v, o, B, L, L, h_q, h_kv, d, causal, scale, probs);
+}
+
+/*
+ * Rotary embedding of x [B][L][H][d] (d even) with cos, sin [L][d/2] into out
+ * (same shape; out must not alias x).
+ */
+int gqa_oracle_rope(const double *x, const double *cos_t, const double *sin_t, double *out,
+                    int B, int L, int H, int d) {
+    if (B <= 0 || L <= 0 || H <= 0 || d <= 0 || d % 2 != 0) return ORACLE_ERR_ARG;
+    const int half = d / 2;
+    for (int b = 0; b < B; ++b)
+        for (int p = 0; p < L; ++p)
+            for (int h = 0; h < H; ++h) {
+                const double *xv = x + (((int64_t)b * L + p) * H + h) * d;
+                double *ov = out + (((int64_t)b * L + p) * H + h) * d;
+                for (int i = 0; i < half; ++i) {
+                    double c = cos_t[(int64_t)p * half + i], sn = sin_t[(int64_t)p * half + i];
+                    double x0 = xv[2 * i], x1 = xv[2 * i + 1];
+                    ov[i] = x0 * c - x1 * sn;
+                    ov[half + i] = x0 * sn + x1 * c;
+                }
+            }
+    return 0;
+}
+
+/*
+ * Prefill with rotary embedding: q, k rotated (gqa_oracle_rope), then the full
+ * prefill; k_rot [B][L][h_kv][d] receives the rotated keys.
+ */
+int gqa_oracle_prefill_rope(const double *q, const double *k, const double *v,
+                            const double *cos_t, const double *sin_t, double *o, double *k_rot,
+                            int B, int L, int h_q, int h_kv, int d, int causal, double scale) {
+    if (B <= 0 || L <= 0 || d <= 0 || d % 2 != 0) return ORACLE_ERR_ARG;
+    if (check_heads(h_q, h_kv)) return ORACLE_ERR_ARG;
+    double *q_rot = (double *)malloc(sizeof(double) * (size_t)B * L * h_q * d);
+    if (!q_rot) return ORACLE_ERR_NOMEM;
+    int rc = gqa_oracle_rope(q, cos_t, sin_t, q_rot, B, L, h_q, d);
+    if (rc == 0) rc = gqa_oracle_rope(k, cos_t, sin_t, k_rot, B, L, h_kv, d);
+    if (rc == 0) rc = prefill_general(q_rot, k_rot, v, o, B, L, L, h_q, h_kv, d, causal, scale,
+                                      NULL);
+    free(q_rot);
+    return rc;
 }
 
 /*

@@ -494,6 +494,77 @@ def pin_paged_shared_prefix():
            "shared-prefix pages vs brute force")
 
 
+def _rope_tables(L, d, offset=0, base=10000.0):
+    """cos, sin [L, d/2] for angles (p + offset) * base^(-2i/d) (test-side inputs)."""
+    pos = np.arange(L, dtype=np.float64)[:, None] + offset
+    freq = base ** (-2.0 * np.arange(d // 2, dtype=np.float64) / d)
+    ang = pos * freq[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def pin_rope_golden():
+    """Hand-derived rotations and a 2-position prefill (tests/golden/rope_by_hand.json)."""
+    g = _golden("rope_by_hand.json")
+    x = np.array(g["x"])
+    cv, sv = np.array(g["cos_vec"]), np.array(g["sin_vec"])
+    both = np.concatenate([x, x], axis=1)  # the vector at positions 0 and 1
+    r = oracle.rope(both, cv, sv)
+    _close(r[0, 1, 0], g["expected_vector_p1"], 1e-15, "rope of the vector at position 1")
+    _close(r[0, 0, 0], g["expected_vector_p0"], 0.0, "rope with cos 1, sin 0")
+    o, k_rot = oracle.prefill_rope(np.array(g["q"]), np.array(g["k"]), np.array(g["v"]),
+                                   np.array(g["cos_attn"]), np.array(g["sin_attn"]), True, 1.0)
+    _close(o, g["expected_o"], 1e-15, "rope prefill output")
+    _close(k_rot, g["expected_k_rot"], 1e-15, "rotated keys")
+
+
+def pin_rope_identity_tables():
+    """cos = 1, sin = 0 turns the rotation into the fixed permutation evens-then-odds:
+    the rotated keys are that permutation of k exactly, and the attention equals
+    the plain prefill (a common permutation of q and k leaves every dot product)."""
+    B, L, h_q, h_kv, d = 2, 9, 6, 3, 8
+    q, k, v = _rand((B, L, h_q, d), 200), _rand((B, L, h_kv, d), 201), _rand((B, L, h_kv, d), 202)
+    ones, zeros = np.ones((L, d // 2)), np.zeros((L, d // 2))
+    perm = list(range(0, d, 2)) + list(range(1, d, 2))
+    for causal in (False, True):
+        o, k_rot = oracle.prefill_rope(q, k, v, ones, zeros, causal, 0.4)
+        _close(k_rot, k[..., perm], 0.0, "identity tables: rotated keys = permuted keys")
+        _close(o, oracle.prefill(q, k, v, causal=causal, scale=0.4), 1e-13,
+               "identity tables: attention unchanged")
+
+
+def pin_rope_relative_position():
+    """With tables from angles theta_i * p, shifting every position by the same
+    offset leaves the attention output unchanged (scores depend on m - n only),
+    while the rotated keys do change; each pair keeps its norm."""
+    B, L, h_q, h_kv, d = 1, 12, 4, 2, 16
+    q, k, v = _rand((B, L, h_q, d), 210), _rand((B, L, h_kv, d), 211), _rand((B, L, h_kv, d), 212)
+    c0, s0 = _rope_tables(L, d)
+    c1, s1 = _rope_tables(L, d, offset=37)
+    for causal in (False, True):
+        o0, kr0 = oracle.prefill_rope(q, k, v, c0, s0, causal, 0.25)
+        o1, kr1 = oracle.prefill_rope(q, k, v, c1, s1, causal, 0.25)
+        _close(o0, o1, 1e-12, "rope: a common position shift leaves the attention")
+        assert float(np.max(np.abs(kr0 - kr1))) > 1e-3, "the shift must move the rotated keys"
+    half = d // 2
+    n_in = k[..., 0::2] ** 2 + k[..., 1::2] ** 2
+    n_out = kr0[..., :half] ** 2 + kr0[..., half:] ** 2
+    _close(n_in, n_out, 1e-12, "rope keeps the norm of every pair")
+
+
+def pin_rope_brute():
+    """Against the pure-Python rotation followed by the brute-force prefill."""
+    B, L, h_q, h_kv, d = 2, 5, 4, 2, 6
+    q, k, v = _rand((B, L, h_q, d), 220), _rand((B, L, h_kv, d), 221), _rand((B, L, h_kv, d), 222)
+    c, sn = _rope_tables(L, d, offset=3, base=100.0)
+    for causal in (False, True):
+        o, k_rot = oracle.prefill_rope(q, k, v, c, sn, causal, 0.5)
+        qb = brute.rope(q.tolist(), c.tolist(), sn.tolist())
+        kb = brute.rope(k.tolist(), c.tolist(), sn.tolist())
+        ob, _ = brute.prefill(qb, kb, v.tolist(), causal, 0.5)
+        _close(k_rot, kb, 1e-15, "rotated keys vs brute force")
+        _close(o, ob, 1e-12, "rope prefill vs brute force")
+
+
 ALL_PINS = [pin_hand_2x2, pin_head_map, pin_decode_golden, pin_mha_reduction,
             pin_mqa_reduction, pin_gqa_library, pin_rows_sum_to_one, pin_k_zero_mean,
             pin_causal_row0, pin_identical_heads, pin_invariances, pin_cross_path,
@@ -501,7 +572,8 @@ ALL_PINS = [pin_hand_2x2, pin_head_map, pin_decode_golden, pin_mha_reduction,
             pin_chunk_golden, pin_chunked_equals_full, pin_chunk_single_query_is_decode,
             pin_chunk_brute_and_library, pin_chunk_rows_match_full, pin_append_cross_path,
             pin_append_to_empty_cache, pin_append_brute_and_tail, pin_token_major_brute,
-            pin_paged_brute, pin_paged_shared_prefix]
+            pin_paged_brute, pin_paged_shared_prefix, pin_rope_golden,
+            pin_rope_identity_tables, pin_rope_relative_position, pin_rope_brute]
 
 
 def main(argv):

@@ -36,6 +36,11 @@ MUTANTS = {
                             "long page = (long)b * max_blocks + j / page_size;"),
     "token_major_read_head_major": ("const long sh = d, sj = (long)h_kv * d, sb = (long)S * sj;",
                                     "const long sj = d, sh = (long)S * d, sb = (long)h_kv * sh;"),
+    "rope_sin_sign": ("ov[i] = x0 * c - x1 * sn;", "ov[i] = x0 * c + x1 * sn;"),
+    "rope_rotate_half_pairs": ("double x0 = xv[2 * i], x1 = xv[2 * i + 1];",
+                               "double x0 = xv[i], x1 = xv[half + i];"),
+    "rope_keys_not_rotated": ("if (rc == 0) rc = gqa_oracle_rope(k, cos_t, sin_t, k_rot, B, L, h_kv, d);",
+                              "if (rc == 0) memcpy(k_rot, k, sizeof(double) * (size_t)B * L * h_kv * d);"),
     "first_head_of_group_only": ("int kvh = kv_head_of(h, h_q, h_kv);\n                int n = seqlens[b];",
                                  "int kvh = 0;\n                int n = seqlens[b];"),
 }
