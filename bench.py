@@ -165,13 +165,22 @@ def bench_prefill(w, steps, warmup, settle_s=0.0):
     import gqa_workloads as wl
     import grouped_query_attention_03_amd as gqa
     dev = torch.device("cuda:0")
-    q, k, v = (t.to(dev) for t in wl.workload_inputs(w))
+    ins = [t.to(dev) for t in wl.workload_inputs(w)]
+    q, k, v = ins[:3]
     out = torch.empty_like(q)
 
-    call = gqa.prefill_chunk if w.path == "prefill_chunk" else gqa.prefill
+    if w.path == "prefill_rope":  # two kernels: the key rotation, then the prefill
+        cos, sin = ins[3:]
+        k_rot = torch.empty_like(k)
 
-    def step():
-        call(q, k, v, causal=w.causal, scale=w.scale, out=out)
+        def step():
+            gqa.prefill_rope(q, k, v, cos, sin, causal=w.causal, scale=w.scale, out=out,
+                             k_rot=k_rot)
+    else:
+        call = gqa.prefill_chunk if w.path == "prefill_chunk" else gqa.prefill
+
+        def step():
+            call(q, k, v, causal=w.causal, scale=w.scale, out=out)
 
     settle_clocks(step, settle_s)
     for _ in range(warmup):
@@ -259,15 +268,19 @@ def cpu_baseline(w, budget_s=12.0):
     """
     import gqa_workloads as wl
     import oracle
-    q, k, v = wl.workload_inputs(w)
-    qd, kd, vd = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    ins = wl.workload_inputs(w)
+    qd, kd, vd = (t.double().numpy() for t in ins[:3])
 
     if w.path == "prefill_chunk":
         return _cpu_baseline_chunk(w, qd, kd, vd, budget_s)
 
     def run(nb):
         t0 = time.perf_counter()
-        oracle.prefill(qd[:nb], kd[:nb], vd[:nb], causal=w.causal, scale=w.scale)
+        if w.path == "prefill_rope":
+            oracle.prefill_rope(qd[:nb], kd[:nb], vd[:nb], ins[3].double().numpy(),
+                                ins[4].double().numpy(), causal=w.causal, scale=w.scale)
+        else:
+            oracle.prefill(qd[:nb], kd[:nb], vd[:nb], causal=w.causal, scale=w.scale)
         return time.perf_counter() - t0
 
     t1 = run(1)
@@ -324,7 +337,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="worked_example_prefill_bf16",
                     choices=[n for n in wl.WORKLOAD_ORDER
-                             if wl.WORKLOADS[n].path in ("prefill", "prefill_chunk")])
+                             if wl.WORKLOADS[n].path in ("prefill", "prefill_chunk",
+                                                         "prefill_rope")])
     ap.add_argument("--decode-workload", default="batched_decode_bf16",
                     choices=["none"] + [n for n in wl.WORKLOAD_ORDER
                                         if wl.WORKLOADS[n].path == "decode"])

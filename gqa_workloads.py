@@ -36,7 +36,8 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    path: str  # "prefill", "prefill_chunk", "decode", "decode_append" or "decode_paged"
+    # "prefill", "prefill_chunk", "prefill_rope", "decode", "decode_append" or "decode_paged"
+    path: str
     dtype: str  # "f32" or "bf16"
     B: int
     h_q: int
@@ -95,6 +96,11 @@ WORKLOADS = {
         S=8192, std=1.0, seqlen_range=(1023, 8191), seed=7,
         description="bf16 decode with the new token's key/value appended, B=64 h_q=32 h_kv=8 "
                     "d=128 S=8192 lengths U{1023..8191} before the append"),
+    "llama2_7b_prefill_rope_bf16": Workload(
+        "llama2_7b_prefill_rope_bf16", "prefill_rope", "bf16", B=1, L=4096, h_q=32, h_kv=8,
+        d=128, causal=True, std=1.0 / math.sqrt(2.0), seed=3,
+        description="bf16 causal prefill with rotary embedding (tables for base 10000), "
+                    "B=1 L=4096 h_q=32 h_kv=8 d=128"),
     "batched_decode_paged_bf16": Workload(
         "batched_decode_paged_bf16", "decode_paged", "bf16", B=64, h_q=32, h_kv=8, d=128,
         S=8192, std=1.0, seqlen_range=(1024, 8192), seed=4, page_size=64,
@@ -107,7 +113,8 @@ WORKLOADS = {
 # appends the new token's key/value rows itself and the decode over pages.
 WORKLOAD_ORDER = ["tiny_prefill_f32", "worked_example_prefill_bf16", "llama2_7b_prefill_bf16",
                   "batched_decode_bf16", "long_context_prefill_bf16", "chunked_prefill_bf16",
-                  "batched_decode_append_bf16", "batched_decode_paged_bf16"]
+                  "batched_decode_append_bf16", "batched_decode_paged_bf16",
+                  "llama2_7b_prefill_rope_bf16"]
 
 
 def _draw(gen, shape, std, dtype):
@@ -161,6 +168,16 @@ def decode_append_inputs(B, h_q, h_kv, S, d, seed, seqlen_range, std=1.0,
     return seqlens, q, k_new, v_new, k_cache, v_cache
 
 
+def rope_tables(L, d, base=10000.0):
+    """cos, sin [L, d/2] float32 for the angles p * base^(-2i/d) (position p,
+    pair i), evaluated in float64 and rounded to float32: the input tables of a
+    rotary embedding, as a model would pass them."""
+    pos = torch.arange(L, dtype=torch.float64)[:, None]
+    freq = base ** (-2.0 * torch.arange(d // 2, dtype=torch.float64) / d)
+    ang = pos * freq[None, :]
+    return torch.cos(ang).to(torch.float32), torch.sin(ang).to(torch.float32)
+
+
 def to_pages(k_cache, v_cache, seqlens, page_size, seed, spare=0):
     """Move head-major caches [B, h_kv, S, d] into a pool of group-aligned pages.
 
@@ -199,6 +216,10 @@ def workload_inputs(w: Workload):
     if w.path == "prefill_chunk":
         return prefill_chunk_inputs(w.B, w.L, w.Lk, w.h_q, w.h_kv, w.d, w.seed, w.std,
                                     w.torch_dtype())
+    if w.path == "prefill_rope":
+        q, k, v = prefill_inputs(w.B, w.L, w.h_q, w.h_kv, w.d, w.seed, w.std, w.torch_dtype())
+        cos, sin = rope_tables(w.L, w.d)
+        return q, k, v, cos, sin
     if w.path == "decode_paged":
         seqlens, q, kc, vc = decode_inputs(w.B, w.h_q, w.h_kv, w.S, w.d, w.seed, w.seqlen_range,
                                            w.std, w.torch_dtype())

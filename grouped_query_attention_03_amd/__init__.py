@@ -16,6 +16,9 @@ the device is not a gfx950 GPU, the calls raise.
     decode(q, k_cache, v_cache, seqlens, out=None, workspace=None, num_splits=0)
         q [B, 1, h_q, d] bf16, caches [B, h_kv, S, d] bf16, seqlens [B] int32
         -> o [B, 1, h_q, d].
+    prefill_rope(q, k, v, cos, sin, causal=..., scale=None, out=None, k_rot=None)
+        q and k rotated (tables cos, sin [L, d/2]), then prefill; returns
+        (o, k_rot).
     decode_token_major(q, k_cache, v_cache, seqlens, ...)
         as decode, with caches [B, S, h_kv, d].
     decode_paged(q, k_pages, v_pages, block_table, seqlens, ...)
@@ -73,6 +76,8 @@ def lib() -> ctypes.CDLL:
     L.gqa_decode_token_major.restype = I
     L.gqa_decode_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, ctypes.c_size_t, P]
     L.gqa_decode_paged.restype = I
+    L.gqa_prefill_rope.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
+    L.gqa_prefill_rope.restype = I
     L.gqa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     L.gqa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.gqa_decode_default_splits.argtypes = []
@@ -306,3 +311,34 @@ def decode_paged(q, k_pages, v_pages, block_table, seqlens, *, out=None, workspa
     if st != 0:
         raise GQAError(st, "gqa_decode_paged")
     return out
+
+
+def prefill_rope(q, k, v, cos, sin, *, causal: bool, scale=None, out=None, k_rot=None):
+    """Prefill with q and k rotated first (bf16).  q [B,L,h_q,d], k/v
+    [B,L,h_kv,d], cos/sin [L, d/2] fp32.  Returns (o [B,L,h_q,d], k_rot
+    [B,L,h_kv,d]: the rotated keys)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, 4)
+    _check(cos, "cos", 2)
+    _check(sin, "sin", 2)
+    B, L, h_q, d = q.shape
+    h_kv = k.shape[2]
+    if tuple(k.shape) != (B, L, h_kv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, L, h_kv, d] with q's B, L and d")
+    if (cos.dtype != torch.float32 or sin.dtype != torch.float32
+            or tuple(cos.shape) != (L, d // 2) or sin.shape != cos.shape):
+        raise ValueError("cos and sin must be float32 [L, d/2]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if k_rot is None:
+        k_rot = torch.empty_like(k)
+    _check(out, "out", 4)
+    _check(k_rot, "k_rot", 4)
+    st = lib().gqa_prefill_rope(q.data_ptr(), k.data_ptr(), v.data_ptr(), cos.data_ptr(),
+                                sin.data_ptr(), out.data_ptr(), k_rot.data_ptr(), B, L, h_q, h_kv,
+                                d, _dtype_code(q), int(bool(causal)), float(scale), _stream(q))
+    if st != 0:
+        raise GQAError(st, "gqa_prefill_rope")
+    return out, k_rot

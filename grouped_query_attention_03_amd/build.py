@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libgqa_hip.so")
-SOURCES = ["gqa_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode_bf16.hip"]
+SOURCES = ["gqa_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode_bf16.hip",
+           "rope_bf16.hip"]
 # Per-source additions.  The bf16 prefill kernel never orders NaNs (masked and
 # stale scores are replaced by -inf with a select before any max), so it runs
 # with the IEEE mode bit off: max/min then need no canonicalising copies.

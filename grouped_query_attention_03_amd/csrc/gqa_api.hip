@@ -71,10 +71,21 @@ namespace {
 
 // Shared by both prefill entry points: Lq query positions per sequence attend
 // to Lk >= Lq keys, query row i sitting at position Lk - Lq + i.
+// The rotary form passes tables cos, sin [Lk][d/2] and the k_rot output: the
+// keys are rotated into k_rot first and the prefill reads them from there.
 gqa_status prefill_impl(const void *q, const void *k, const void *v, void *o, int B, int Lq,
                         int Lk, int h_q, int h_kv, int d, gqa_dtype dt, int causal, float scale,
-                        void *hip_stream) {
+                        void *hip_stream, const float *rope_cos = nullptr,
+                        const float *rope_sin = nullptr, void *k_rot = nullptr,
+                        bool rope = false) {
     if (!q || !k || !v || !o) return GQA_ERR_NULL_POINTER;
+    if (rope) {
+        if (!rope_cos || !rope_sin || !k_rot) return GQA_ERR_NULL_POINTER;
+        if (!aligned16(rope_cos) || !aligned16(rope_sin) || !aligned16(k_rot))
+            return GQA_ERR_ALIGNMENT;
+        if (dt != GQA_BF16) return GQA_ERR_DTYPE;
+        if (k_rot == k) return GQA_ERR_SIZE;  // rotated in place would race
+    }
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GQA_ERR_ALIGNMENT;
     if (B <= 0 || Lq <= 0 || Lk < Lq || h_q <= 0 || h_kv <= 0) return GQA_ERR_SIZE;
     if (h_q % h_kv != 0) return GQA_ERR_HEADS;
@@ -105,11 +116,25 @@ gqa_status prefill_impl(const void *q, const void *k, const void *v, void *o, in
     a.n_units = B * h_kv * a.nsub;
     a.n_qtiles = (Lq + a.BM - 1) / a.BM;
     a.c = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
+    a.rope_cos = rope ? rope_cos : nullptr;
+    a.rope_sin = rope ? rope_sin : nullptr;
     if ((int64_t)a.n_units * a.n_qtiles > 0x7fffffff) return GQA_ERR_SIZE;
 
     gqa_status st = check_device();
     if (st != GQA_OK) return st;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (rope) {
+        gqa::RopeArgs r;
+        r.x = k;
+        r.out = k_rot;
+        r.cos = rope_cos;
+        r.sin = rope_sin;
+        r.rows = (long long)B * Lk * h_kv;
+        r.L = Lk;
+        r.h = h_kv;
+        if (gqa::launch_rope_k_bf16(r, d, stream) != 0) return GQA_ERR_LAUNCH;
+        a.k = k_rot;
+    }
     int rc = dt == GQA_BF16 ? gqa::launch_prefill_bf16(a, d, causal != 0, stream)
                             : gqa::launch_prefill_f32(a, d, causal != 0, stream);
     return rc == 0 ? GQA_OK : GQA_ERR_LAUNCH;
@@ -129,6 +154,14 @@ gqa_status gqa_prefill_chunk(const void *q, const void *k, const void *v, void *
                              int L_q, int L_k, int h_q, int h_kv, int d, gqa_dtype dt,
                              int causal, float scale, void *hip_stream) {
     return prefill_impl(q, k, v, o, B, L_q, L_k, h_q, h_kv, d, dt, causal, scale, hip_stream);
+}
+
+gqa_status gqa_prefill_rope(const void *q, const void *k, const void *v, const float *cos_table,
+                            const float *sin_table, void *o, void *k_rot, int B, int L, int h_q,
+                            int h_kv, int d, gqa_dtype dt, int causal, float scale,
+                            void *hip_stream) {
+    return prefill_impl(q, k, v, o, B, L, L, h_q, h_kv, d, dt, causal, scale, hip_stream,
+                        cos_table, sin_table, k_rot, true);
 }
 
 int gqa_decode_default_splits(void) { return kDefaultSplits; }

@@ -19,6 +19,19 @@ struct PrefillArgs {
     int n_units;   // B * h_kv * nsub
     int n_qtiles;  // ceil(L / BM)
     float c;       // scale * log2(e)
+    // rotary tables cos, sin [positions][d/2] fp32 (row p for position p);
+    // non-null only in the rotary form, where q is rotated as it is loaded
+    const float *rope_cos, *rope_sin;
+};
+
+// Rotary embedding of key rows x [rows][d] (rows in [B][L][h][...] order) into
+// out, tables cos, sin [L][d/2].
+struct RopeArgs {
+    const void *x;
+    void *out;
+    const float *cos, *sin;
+    long long rows;  // B * L * h
+    int L, h;
 };
 
 // Waves per work-group of the decode split pass; with one work-group per CU
@@ -50,6 +63,7 @@ struct DecodeArgs {
 };
 
 int launch_prefill_bf16(const PrefillArgs &a, int d, bool causal, hipStream_t stream);
+int launch_rope_k_bf16(const RopeArgs &a, int d, hipStream_t stream);
 int launch_prefill_f32(const PrefillArgs &a, int d, bool causal, hipStream_t stream);
 int launch_decode_bf16(const DecodeArgs &a, int d, hipStream_t stream);
 

@@ -97,7 +97,8 @@ __device__ __forceinline__ void block_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-template <int D, bool CAUSAL>
+// ROPE: q is rotated as it is loaded (the keys arrive rotated already).
+template <int D, bool CAUSAL, bool ROPE>
 __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs a) {
     using Lay = PfLay<D>;
     constexpr int KSTEPS = Lay::KSTEPS, DB = Lay::DB, DPW = Lay::DMA_PER_WAVE;
@@ -167,15 +168,42 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
     {
         const int pos = pos0 + (lane & 31);
         if (pos < L) {
-            const __bf16 *qp = static_cast<const __bf16 *>(a.q) +
-                               (((size_t)b * L + pos) * a.h_q + head) * D + 8 * (lane >> 5);
+            const __bf16 *qrow = static_cast<const __bf16 *>(a.q) +
+                                 (((size_t)b * L + pos) * a.h_q + head) * D;
+            const __bf16 *qp = qrow + 8 * (lane >> 5);
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
                 // fold scale * log2(e) into Q once (rounded to bf16): S^T then
                 // comes out of the MFMA already in log2 units
-                const bf16x8 raw = __builtin_bit_cast(bf16x8, load16(qp + 16 * ks));
+                if (!ROPE) {
+                    const bf16x8 raw = __builtin_bit_cast(bf16x8, load16(qp + 16 * ks));
 #pragma unroll
-                for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)raw[e] * a.c);
+                    for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)raw[e] * a.c);
+                } else {
+                    // rotated columns c0 .. c0 + 7: pairs i0 .. i0 + 7 of the row,
+                    // first half x0 cos - x1 sin, second half x0 sin + x1 cos
+                    // (position off + pos; whether c0 is in the first half is
+                    // fixed per k-step since d/2 is a multiple of 16)
+                    const int c0 = 16 * ks + 8 * (lane >> 5);
+                    const bool first = 16 * ks < D / 2;
+                    const int i0 = first ? c0 : c0 - D / 2;
+                    const bf16x8 xa = __builtin_bit_cast(bf16x8, load16(qrow + 2 * i0));
+                    const bf16x8 xb = __builtin_bit_cast(bf16x8, load16(qrow + 2 * i0 + 8));
+                    const size_t t0 = (size_t)(off + pos) * (D / 2) + i0;
+                    const float4 ca = *reinterpret_cast<const float4 *>(a.rope_cos + t0);
+                    const float4 cb = *reinterpret_cast<const float4 *>(a.rope_cos + t0 + 4);
+                    const float4 sa = *reinterpret_cast<const float4 *>(a.rope_sin + t0);
+                    const float4 sb = *reinterpret_cast<const float4 *>(a.rope_sin + t0 + 4);
+                    const float cc[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
+                    const float ss[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float x0 = (float)(e < 4 ? xa[2 * e] : xb[2 * e - 8]);
+                        const float x1 = (float)(e < 4 ? xa[2 * e + 1] : xb[2 * e - 7]);
+                        const float r = first ? x0 * cc[e] - x1 * ss[e] : x0 * ss[e] + x1 * cc[e];
+                        qf[ks][e] = (__bf16)(r * a.c);
+                    }
+                }
             }
         } else {
 #pragma unroll
@@ -350,13 +378,27 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
 
 int launch_prefill_bf16(const PrefillArgs &a, int d, bool causal, hipStream_t stream) {
     dim3 grid(a.n_units * a.n_qtiles), block(PF_THREADS);
+    const bool rope = a.rope_cos != nullptr;
+#define GQA_PF_LAUNCH(D_, C_, R_) \
+    hipLaunchKernelGGL((prefill_bf16_kernel<D_, C_, R_>), grid, block, 0, stream, a)
     if (d == 128) {
-        if (causal) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, stream, a);
+        if (causal) {
+            if (rope) GQA_PF_LAUNCH(128, true, true);
+            else GQA_PF_LAUNCH(128, true, false);
+        } else {
+            if (rope) GQA_PF_LAUNCH(128, false, true);
+            else GQA_PF_LAUNCH(128, false, false);
+        }
     } else {
-        if (causal) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, stream, a);
+        if (causal) {
+            if (rope) GQA_PF_LAUNCH(64, true, true);
+            else GQA_PF_LAUNCH(64, true, false);
+        } else {
+            if (rope) GQA_PF_LAUNCH(64, false, true);
+            else GQA_PF_LAUNCH(64, false, false);
+        }
     }
+#undef GQA_PF_LAUNCH
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -92,6 +92,32 @@ gqa_status gqa_prefill_chunk(const void *q, const void *k, const void *v, void *
                              int causal, float scale, void *hip_stream);
 
 /*
+ * Prefill with rotary position embedding: q and k are rotated, then the
+ * prefill above runs on the rotated q, k and the unrotated v ("Attention in
+ * Qwen, DeepSeek and LLaMA3", §1, apply_rotary_pos_emb).  For a row x at
+ * position p and pair i (0 <= i < d/2):
+ *   x'[i]       = x[2i] cos[p][i] - x[2i+1] sin[p][i]
+ *   x'[d/2 + i] = x[2i] sin[p][i] + x[2i+1] cos[p][i]
+ * (the even/odd pairs rotated, the two halves concatenated as the page writes
+ * them).
+ *   q, k, v, o, B, L, h_q, h_kv, d, causal, scale: as gqa_prefill; dt must be
+ *          GQA_BF16 (else GQA_ERR_DTYPE).
+ *   cos_table, sin_table : [L, d/2] fp32 device arrays, row p for position p,
+ *          16-byte aligned.  Any values: the call does not assume
+ *          cos^2 + sin^2 = 1.
+ *   k_rot : [B, L, h_kv, d] bf16 output, the rotated keys (what a cache holds);
+ *          the attention reads the keys from here.  It must not overlap k
+ *          (k_rot == k returns GQA_ERR_SIZE).
+ * The keys are rotated by one small kernel (fp32 arithmetic, one rounding to
+ * bf16); q is rotated in fp32 as the prefill kernel loads it, then scaled and
+ * rounded to bf16 once, as in gqa_prefill.  Two kernels run on `hip_stream`.
+ */
+gqa_status gqa_prefill_rope(const void *q, const void *k, const void *v, const float *cos_table,
+                            const float *sin_table, void *o, void *k_rot, int B, int L, int h_q,
+                            int h_kv, int d, gqa_dtype dt, int causal, float scale,
+                            void *hip_stream);
+
+/*
  * Decode: one new query position per sequence attends to rows [0, seqlens[b])
  * of a head-major key/value cache ("What is Grouped-Query Attention", §2.2 step
  * 2 for the [batch, g, seq_len, d_head] cache and §3.2 for appending the new

@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("gqa_prefill", "gqa_prefill_chunk", "gqa_decode", "gqa_decode_append",
-              "gqa_decode_token_major", "gqa_decode_paged",
+              "gqa_decode_token_major", "gqa_decode_paged", "gqa_prefill_rope",
               "gqa_decode_workspace_bytes",
               "gqa_decode_default_splits", "gqa_status_string"):
         assert n in names
@@ -102,6 +102,29 @@ def test_prefill_chunk_without_a_gpu_reports_the_device():
         pytest.skip("a GPU is present")
     assert chunk_status() == DEVICE
     assert chunk_status(Lq=64, Lk=64) == DEVICE  # the square case is valid too
+
+
+def rope_status(q=A, k=A, v=A, c=A, s=A, o=A, kr=A + 0x100, B=1, L=16, h_q=8, h_kv=2, d=64,
+                dt=1, causal=1, scale=0.125):
+    return gqa.lib().gqa_prefill_rope(q, k, v, c, s, o, kr, B, L, h_q, h_kv, d, dt, causal,
+                                      ctypes.c_float(scale), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(c=None), NULLP), (dict(s=None), NULLP), (dict(kr=None), NULLP), (dict(q=None), NULLP),
+    (dict(c=A + 4), ALIGN), (dict(s=MIS), ALIGN), (dict(kr=MIS), ALIGN),
+    (dict(dt=0), DTYPE), (dict(kr=A), SIZE),  # k_rot == k: rotating in place would race
+    (dict(L=0), SIZE), (dict(h_q=8, h_kv=3), HEADS), (dict(d=96), HEADDIM), (dict(scale=0.0), SIZE),
+])
+def test_prefill_rope_rejects_bad_arguments(kw, status):
+    assert rope_status(**kw) == status
+
+
+def test_prefill_rope_without_a_gpu_reports_the_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert rope_status() == DEVICE
 
 
 def decode_status(q=A, kc=A, vc=A, sl=A, o=A, B=4, h_q=32, h_kv=8, S=1024, d=128, dt=1,

@@ -631,3 +631,80 @@ def test_workload_batched_decode_paged(dev):
     ref = oracle.decode_paged(f64(q[bi, 0]), f64(kp[idx]), f64(vp[idx]), sub.numpy(),
                               seqlens[bi].numpy())
     check(f64(out[bi, 0]), ref, "bf16", f"{w.name}: sequences {bsel}")
+
+
+# ------------------------------------------------------ prefill with rotary embedding
+
+def check_rotated_keys(got, ref, what):
+    """bf16 keys rotated in fp32 and rounded once: within one bf16 rounding of
+    the fp64 rotation (half an ulp of the result, plus the fp32 arithmetic)."""
+    g, r = f64(got), np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape and np.isfinite(g).all(), what
+    bound = np.abs(r) * 2.0 ** -8 + 1e-6
+    bad = int((np.abs(g - r) > bound).sum())
+    say(f"  {what}: max-abs {float(np.abs(g - r).max()):.3e}, {bad} beyond one bf16 rounding")
+    assert bad == 0, f"{what}: {bad} elements beyond one bf16 rounding of the oracle"
+
+
+ROPE_SMALL = [
+    # B, L, h_q, h_kv, d, causal
+    (2, 200, 8, 2, 128, True),
+    (1, 333, 8, 8, 64, False),   # G = 1, ragged tail
+    (2, 130, 32, 4, 128, False),
+    (1, 77, 6, 3, 64, True),     # G = 2, one partial tile
+]
+
+
+@pytest.mark.parametrize("case", ROPE_SMALL, ids=lambda c: "B{}_L{}_hq{}_hkv{}_d{}_c{}".format(*c))
+def test_prefill_rope_matches_oracle(case, dev):
+    B, L, h_q, h_kv, d, causal = case
+    seed = 6000 + L + h_q
+    q, k, v = wl.prefill_inputs(B, L, h_q, h_kv, d, seed, 1.0 / math.sqrt(2.0), torch.bfloat16)
+    cos, sin = wl.rope_tables(L, d)
+    scale = 1 / math.sqrt(d)
+    say(f"prefill rope {case} seed {seed}")
+    out, k_rot = gqa.prefill_rope(q.to(dev), k.to(dev), v.to(dev), cos.to(dev), sin.to(dev),
+                                  causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, kr_ref = oracle.prefill_rope(f64(q), f64(k), f64(v), f64(cos), f64(sin), causal,
+                                        scale)
+    check(f64(out.cpu()), o_ref, "bf16", f"rope prefill {case}")
+    check_rotated_keys(k_rot.cpu(), kr_ref, f"rotated keys {case}")
+
+
+def test_prefill_rope_identity_tables_is_permuted_prefill(dev):
+    # cos = 1, sin = 0: the rotation is the evens-then-odds permutation, exact in
+    # fp32, so the rotary call gives the plain prefill of permuted q and k bit for bit
+    B, L, h_q, h_kv, d = 2, 300, 16, 4, 128
+    q, k, v = wl.prefill_inputs(B, L, h_q, h_kv, d, 71, 1.0, torch.bfloat16)
+    ones = torch.ones(L, d // 2, dtype=torch.float32)
+    zeros = torch.zeros(L, d // 2, dtype=torch.float32)
+    perm = list(range(0, d, 2)) + list(range(1, d, 2))
+    say("rope identity tables vs permuted plain prefill")
+    for causal in (True, False):
+        out, k_rot = gqa.prefill_rope(q.to(dev), k.to(dev), v.to(dev), ones.to(dev), zeros.to(dev),
+                                      causal=causal, scale=0.1)
+        plain = run_prefill(q[..., perm].contiguous(), k[..., perm].contiguous(), v, causal, 0.1,
+                            dev)
+        assert torch.equal(k_rot.cpu(), k[..., perm])
+        assert torch.equal(out.cpu(), plain.cpu())
+
+
+def test_workload_llama2_prefill_rope(dev):
+    w = wl.WORKLOADS["llama2_7b_prefill_rope_bf16"]
+    q, k, v, cos, sin = wl.workload_inputs(w)
+    say(f"prefill workload {w.name} ({w.description}) seed {w.seed}")
+    out, k_rot = gqa.prefill_rope(q.to(dev), k.to(dev), v.to(dev), cos.to(dev), sin.to(dev),
+                                  causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    out, k_rot = out.cpu(), k_rot.cpu()
+    kr_ref = oracle.rope(f64(k), f64(cos), f64(sin))
+    check_rotated_keys(k_rot, kr_ref, f"{w.name}: all rotated keys")
+    q_rot = oracle.rope(f64(q), f64(cos), f64(sin))
+    rows = wl.sample_rows(256, w.B, w.L, w.h_q, w.seed,
+                          include=[(0, 0, 0), (0, w.L - 1, w.h_q - 1)])
+    idx = np.asarray(rows)
+    ref = oracle.prefill_rows(q_rot[idx[:, 0], idx[:, 1], idx[:, 2]], rows, kr_ref, f64(v), w.h_q,
+                              causal=w.causal, scale=w.scale)
+    ti = torch.tensor(rows)
+    check(f64(out[ti[:, 0], ti[:, 1], ti[:, 2]]), ref, "bf16", f"{w.name}: {len(rows)} sampled rows")
