@@ -82,6 +82,11 @@ def _load():
     lib.gqa_oracle_decode_token_major.restype = I
     lib.gqa_oracle_decode_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I]
     lib.gqa_oracle_decode_paged.restype = I
+    lib.gqa_oracle_prefill_varlen.argtypes = [P, P, P, P, P, I, I, I, I, I, I, ctypes.c_double]
+    lib.gqa_oracle_prefill_varlen.restype = I
+    lib.gqa_oracle_prefill_varlen_rows.argtypes = [P, P, ctypes.c_int64, P, P, P, I, I, I, I, I,
+                                                   I, ctypes.c_double, P]
+    lib.gqa_oracle_prefill_varlen_rows.restype = I
     lib.gqa_oracle_rope.argtypes = [P, P, P, P, I, I, I, I]
     lib.gqa_oracle_rope.restype = I
     lib.gqa_oracle_prefill_rope.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I,
@@ -203,6 +208,42 @@ def decode(q, k_cache, v_cache, seqlens):
     if rc != 0:
         raise ValueError("oracle decode rejected its arguments (rc=%d)" % rc)
     return o
+
+
+def prefill_varlen(q, k, v, kv_lens, causal: bool, scale: float):
+    """Padded variable-length prefill: q [B,L,h_q,d], k/v [B,L,h_kv,d], kv_lens [B];
+    key j of sequence b is visible iff j < kv_lens[b] (and j <= i when causal)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    kl = np.ascontiguousarray(np.asarray(kv_lens, dtype=np.int32))
+    B, L, h_q, d = q.shape
+    h_kv = k.shape[2]
+    if k.shape != (B, L, h_kv, d) or v.shape != k.shape or kl.shape != (B,):
+        raise ValueError("prefill_varlen shapes do not match")
+    o = np.empty_like(q)
+    rc = _load().gqa_oracle_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(kl), _ptr(o), B, L,
+                                           h_q, h_kv, d, int(bool(causal)), float(scale))
+    if rc != 0:
+        raise ValueError("oracle prefill_varlen rejected its arguments (rc=%d)" % rc)
+    return o
+
+
+def prefill_varlen_rows(q_rows, rows_bih, k, v, kv_lens, h_q: int, causal: bool, scale: float):
+    """Selected rows (b, i, h) of the padded variable-length prefill.  Returns [n, d]."""
+    q_rows = _f64(q_rows)
+    rows = np.ascontiguousarray(np.asarray(rows_bih, dtype=np.int64).reshape(-1, 3))
+    k, v = _f64(k), _f64(v)
+    kl = np.ascontiguousarray(np.asarray(kv_lens, dtype=np.int32))
+    B, L, h_kv, d = k.shape
+    n = rows.shape[0]
+    if q_rows.shape != (n, d) or kl.shape != (B,):
+        raise ValueError("prefill_varlen_rows shapes do not match")
+    out = np.empty((n, d))
+    rc = _load().gqa_oracle_prefill_varlen_rows(_ptr(q_rows), _ptr(rows), n, _ptr(k), _ptr(v),
+                                                _ptr(kl), B, L, h_q, h_kv, d, int(bool(causal)),
+                                                float(scale), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle prefill_varlen_rows rejected its arguments (rc=%d)" % rc)
+    return out
 
 
 def rope(x, cos, sin):

@@ -58,6 +58,13 @@
  *     sequence b.  Logical row j of (b, g) is block_table[b][j / page_size],
  *     group g, row j % page_size.
  *
+ *   Variable-length sequences in a padded batch: the page's forward pass takes
+ *   an attention mask applied as masked_fill(mask == 0, -inf) "to handle
+ *   variable-length sequences" ("Implementing GQA from scratch in PyTorch",
+ *   §3.3).  Read as a key-padding mask given by lengths: key j of sequence b
+ *   is visible iff j < kv_lens[b] (and j <= i when causal).  Every query row
+ *   is computed, padded ones included; a row with no visible key is zero.
+ *
  *   Rotary position embedding before the scores ("Attention in Qwen,
  *   DeepSeek and LLaMA3", §1, apply_rotary_pos_emb; the model-family table
  *   of "Modern LLM architecture (1)", §1 lists RoPE for every GQA family).
@@ -159,6 +166,7 @@ static int check_heads(int h_q, int h_kv) {
  *   k, v    [B][L_k][h_kv][d]
  *   out     [n_rows][d]
  *   probs   NULL, or [n_rows][L_k]: the softmax row (zeros beyond the visible keys)
+ *   kv_lens NULL, or [B]: only keys j < kv_lens[b] are visible (0 <= kv_lens[b] <= L_k)
  * Query row i sits at position L_k - L_q + i (1 <= L_q <= L_k).  Rows are
  * processed in groups that share (b, h) so the repeated slab of their head is
  * built once per group; rows must be sorted by (b, h) for that to help, but
@@ -167,9 +175,12 @@ static int check_heads(int h_q, int h_kv) {
 static int prefill_rows_general(const double *q_rows, const int64_t *row_bih, int64_t n_rows,
                                 const double *k, const double *v, int B, int Lq, int Lk,
                                 int h_q, int h_kv, int d, int causal, double scale,
-                                double *out, double *probs) {
+                                double *out, double *probs, const int32_t *kv_lens) {
     if (B <= 0 || Lq <= 0 || Lk < Lq || d <= 0 || n_rows < 0) return ORACLE_ERR_ARG;
     if (check_heads(h_q, h_kv)) return ORACLE_ERR_ARG;
+    if (kv_lens)
+        for (int b = 0; b < B; ++b)
+            if (kv_lens[b] < 0 || kv_lens[b] > Lk) return ORACLE_ERR_ARG;
     for (int64_t r = 0; r < n_rows; ++r) {
         int64_t b = row_bih[3 * r], i = row_bih[3 * r + 1], h = row_bih[3 * r + 2];
         if (b < 0 || b >= B || i < 0 || i >= Lq || h < 0 || h >= h_q) return ORACLE_ERR_ARG;
@@ -209,6 +220,7 @@ static int prefill_rows_general(const double *q_rows, const int64_t *row_bih, in
                 for (int64_t r = r0; r < r1; ++r) {
                     int i = (int)row_bih[3 * r + 1];
                     int n_vis = causal ? first + i + 1 : Lk;
+                    if (kv_lens && kv_lens[b] < n_vis) n_vis = kv_lens[b]; /* key padding */
                     double *prow = NULL;
                     if (probs) {
                         prow = probs + r * (int64_t)Lk;
@@ -233,7 +245,7 @@ int gqa_oracle_prefill_rows(const double *q_rows, const int64_t *row_bih, int64_
                             int h_kv, int d, int causal, double scale, double *out,
                             double *probs) {
     return prefill_rows_general(q_rows, row_bih, n_rows, k, v, B, L, L, h_q, h_kv, d, causal,
-                                scale, out, probs);
+                                scale, out, probs, NULL);
 }
 
 /* Rows of a prefill against L_k keys, L_q new positions (see prefill_rows_general). */
@@ -242,7 +254,7 @@ int gqa_oracle_prefill_cached_rows(const double *q_rows, const int64_t *row_bih,
                                    int Lq, int Lk, int h_q, int h_kv, int d, int causal,
                                    double scale, double *out) {
     return prefill_rows_general(q_rows, row_bih, n_rows, k, v, B, Lq, Lk, h_q, h_kv, d, causal,
-                                scale, out, NULL);
+                                scale, out, NULL, NULL);
 }
 
 /*
@@ -252,7 +264,7 @@ int gqa_oracle_prefill_cached_rows(const double *q_rows, const int64_t *row_bih,
  */
 static int prefill_general(const double *q, const double *k, const double *v, double *o, int B,
                            int Lq, int Lk, int h_q, int h_kv, int d, int causal, double scale,
-                           double *probs) {
+                           double *probs, const int32_t *kv_lens) {
     if (B <= 0 || Lq <= 0 || Lk < Lq || d <= 0) return ORACLE_ERR_ARG;
     if (check_heads(h_q, h_kv)) return ORACLE_ERR_ARG;
     int64_t n = (int64_t)B * h_q * Lq;
@@ -277,7 +289,7 @@ static int prefill_general(const double *q, const double *k, const double *v, do
                        sizeof(double) * (size_t)d);
             }
     int rc = prefill_rows_general(qr, bih, n, k, v, B, Lq, Lk, h_q, h_kv, d, causal, scale,
-                                  orow, probs);
+                                  orow, probs, kv_lens);
     if (rc == 0) {
         r = 0;
         for (int b = 0; b < B; ++b)
@@ -299,7 +311,29 @@ static int prefill_general(const double *q, const double *k, const double *v, do
 int gqa_oracle_prefill(const double *q, const double *k, const double *v, double *o, int B,
                        int L, int h_q, int h_kv, int d, int causal, double scale,
                        double *probs) {
-    return prefill_general(q, k, v, o, B, L, L, h_q, h_kv, d, causal, scale, probs);
+    return prefill_general(q, k, v, o, B, L, L, h_q, h_kv, d, causal, scale, probs, NULL);
+}
+
+/*
+ * Prefill of a padded batch of variable-length sequences: q, o [B][L][h_q][d],
+ * k, v [B][L][h_kv][d], kv_lens [B] in [0, L]; key j of sequence b is visible
+ * iff j < kv_lens[b] (and j <= i when causal).
+ */
+int gqa_oracle_prefill_varlen(const double *q, const double *k, const double *v,
+                              const int32_t *kv_lens, double *o, int B, int L, int h_q, int h_kv,
+                              int d, int causal, double scale) {
+    if (!kv_lens) return ORACLE_ERR_ARG;
+    return prefill_general(q, k, v, o, B, L, L, h_q, h_kv, d, causal, scale, NULL, kv_lens);
+}
+
+/* Selected rows of the padded variable-length prefill (see prefill_rows_general). */
+int gqa_oracle_prefill_varlen_rows(const double *q_rows, const int64_t *row_bih, int64_t n_rows,
+                                   const double *k, const double *v, const int32_t *kv_lens,
+                                   int B, int L, int h_q, int h_kv, int d, int causal,
+                                   double scale, double *out) {
+    if (!kv_lens) return ORACLE_ERR_ARG;
+    return prefill_rows_general(q_rows, row_bih, n_rows, k, v, B, L, L, h_q, h_kv, d, causal,
+                                scale, out, NULL, kv_lens);
 }
 
 /*
@@ -339,7 +373,7 @@ int gqa_oracle_prefill_rope(const double *q, const double *k, const double *v,
     int rc = gqa_oracle_rope(q, cos_t, sin_t, q_rot, B, L, h_q, d);
     if (rc == 0) rc = gqa_oracle_rope(k, cos_t, sin_t, k_rot, B, L, h_kv, d);
     if (rc == 0) rc = prefill_general(q_rot, k_rot, v, o, B, L, L, h_q, h_kv, d, causal, scale,
-                                      NULL);
+                                      NULL, NULL);
     free(q_rot);
     return rc;
 }
@@ -352,7 +386,7 @@ int gqa_oracle_prefill_rope(const double *q, const double *k, const double *v,
 int gqa_oracle_prefill_cached(const double *q, const double *k, const double *v, double *o,
                               int B, int Lq, int Lk, int h_q, int h_kv, int d, int causal,
                               double scale, double *probs) {
-    return prefill_general(q, k, v, o, B, Lq, Lk, h_q, h_kv, d, causal, scale, probs);
+    return prefill_general(q, k, v, o, B, Lq, Lk, h_q, h_kv, d, causal, scale, probs, NULL);
 }
 
 /*

@@ -565,6 +565,60 @@ def pin_rope_brute():
         _close(o, ob, 1e-12, "rope prefill vs brute force")
 
 
+def pin_varlen_equals_truncated():
+    """A padded batch with lengths: each valid row equals the prefill of its
+    sequence cut to its length; padding (NaN) never leaks in; a padded row
+    sees every valid key (causal: as the last valid row's key set); a length
+    of 0 gives zero rows."""
+    B, L, h_q, h_kv, d = 4, 9, 6, 2, 5
+    q, k, v = _rand((B, L, h_q, d), 230), _rand((B, L, h_kv, d), 231), _rand((B, L, h_kv, d), 232)
+    lens = [9, 4, 1, 0]
+    kp, vp = k.copy(), v.copy()
+    for b, n in enumerate(lens):
+        kp[b, n:] = np.nan
+        vp[b, n:] = np.nan
+    for causal in (False, True):
+        o = oracle.prefill_varlen(q, kp, vp, lens, causal, 0.6)
+        assert np.isfinite(o).all(), "padding leaked into the output"
+        for b, n in enumerate(lens):
+            if n == 0:
+                _close(o[b], np.zeros_like(o[b]), 0.0, "length 0 gives zero rows")
+                continue
+            alone = oracle.prefill(q[b:b + 1, :n], k[b:b + 1, :n], v[b:b + 1, :n], causal=causal,
+                                   scale=0.6)
+            _close(o[b:b + 1, :n], alone, 1e-13, f"seq {b}: valid rows vs the cut sequence")
+            # a padded row attends to all n valid keys (brute force, by hand)
+            for i in range(n, L):
+                for h in range(h_q):
+                    g = h // (h_q // h_kv)
+                    want, _ = brute._softmax_average(q[b, i, h].tolist(),
+                                                     [k[b, j, g].tolist() for j in range(n)],
+                                                     [v[b, j, g].tolist() for j in range(n)], 0.6)
+                    _close(o[b, i, h], want, 1e-12, f"seq {b} padded row {i} head {h}")
+
+
+def pin_varlen_library():
+    """Against torch's fp64 SDPA with an explicit boolean mask (key padding, and
+    causal), on sequences of nonzero length."""
+    B, L, h_q, h_kv, d = 3, 11, 4, 4, 7
+    q, k, v = _rand((B, L, h_q, d), 240), _rand((B, L, h_kv, d), 241), _rand((B, L, h_kv, d), 242)
+    lens = [11, 6, 1]
+    for causal in (False, True):
+        o = oracle.prefill_varlen(q, k, v, lens, causal, 0.3)
+        keep = torch.zeros(B, 1, L, L, dtype=torch.bool)
+        for b, n in enumerate(lens):
+            keep[b, :, :, :n] = True
+        if causal:
+            keep &= torch.ones(L, L, dtype=torch.bool).tril()
+        tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3) for x in (q, k, v))
+        ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=keep, scale=0.3)
+        _close(o, ref.permute(0, 2, 1, 3).numpy(), 1e-12, f"varlen vs masked SDPA causal={causal}")
+        rows = [(1, 0, 0), (1, 5, 3), (1, 10, 2), (2, 7, 1), (0, 10, 3)]
+        qr = np.array([q[b, i, h] for (b, i, h) in rows])
+        _close(oracle.prefill_varlen_rows(qr, rows, k, v, lens, h_q, causal, 0.3),
+               np.array([o[b, i, h] for (b, i, h) in rows]), 0.0, "varlen rows vs full")
+
+
 ALL_PINS = [pin_hand_2x2, pin_head_map, pin_decode_golden, pin_mha_reduction,
             pin_mqa_reduction, pin_gqa_library, pin_rows_sum_to_one, pin_k_zero_mean,
             pin_causal_row0, pin_identical_heads, pin_invariances, pin_cross_path,
@@ -573,7 +627,8 @@ ALL_PINS = [pin_hand_2x2, pin_head_map, pin_decode_golden, pin_mha_reduction,
             pin_chunk_brute_and_library, pin_chunk_rows_match_full, pin_append_cross_path,
             pin_append_to_empty_cache, pin_append_brute_and_tail, pin_token_major_brute,
             pin_paged_brute, pin_paged_shared_prefix, pin_rope_golden,
-            pin_rope_identity_tables, pin_rope_relative_position, pin_rope_brute]
+            pin_rope_identity_tables, pin_rope_relative_position, pin_rope_brute,
+            pin_varlen_equals_truncated, pin_varlen_library]
 
 
 def main(argv):

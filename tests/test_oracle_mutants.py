@@ -41,6 +41,8 @@ MUTANTS = {
                                "double x0 = xv[i], x1 = xv[half + i];"),
     "rope_keys_not_rotated": ("if (rc == 0) rc = gqa_oracle_rope(k, cos_t, sin_t, k_rot, B, L, h_kv, d);",
                               "if (rc == 0) memcpy(k_rot, k, sizeof(double) * (size_t)B * L * h_kv * d);"),
+    "varlen_lengths_ignored": ("if (kv_lens && kv_lens[b] < n_vis) n_vis = kv_lens[b]; /* key padding */",
+                               "/* key padding dropped */"),
     "first_head_of_group_only": ("int kvh = kv_head_of(h, h_q, h_kv);\n                int n = seqlens[b];",
                                  "int kvh = 0;\n                int n = seqlens[b];"),
 }
