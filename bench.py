@@ -73,7 +73,18 @@ def visible_pairs(Lq: int, Lk: int, causal: bool) -> int:
     return Lq * (first + 1) + Lq * (Lq - 1) // 2
 
 
-def prefill_flops(w) -> float:
+def varlen_pairs(L: int, n: int, causal: bool) -> int:
+    """(query, key) pairs of one padded sequence with n valid keys: every one of
+    the L rows sees keys j < n (and j <= i when causal)."""
+    if not causal:
+        return L * n
+    return n * (n + 1) // 2 + (L - n) * n
+
+
+def prefill_flops(w, kv_lens=None) -> float:
+    if w.path == "prefill_varlen":
+        pairs = sum(varlen_pairs(w.L, int(n), w.causal) for n in kv_lens)
+        return 4.0 * w.h_q * w.d * pairs
     Lk = w.Lk if w.path == "prefill_chunk" else w.L
     return 4.0 * w.B * w.h_q * w.d * visible_pairs(w.L, Lk, w.causal)
 
@@ -169,7 +180,13 @@ def bench_prefill(w, steps, warmup, settle_s=0.0):
     q, k, v = ins[:3]
     out = torch.empty_like(q)
 
-    if w.path == "prefill_rope":  # two kernels: the key rotation, then the prefill
+    kv_lens = None
+    if w.path == "prefill_varlen":
+        kv_lens = ins[3]
+
+        def step():
+            gqa.prefill_varlen(q, k, v, kv_lens, causal=w.causal, scale=w.scale, out=out)
+    elif w.path == "prefill_rope":  # two kernels: the key rotation, then the prefill
         cos, sin = ins[3:]
         k_rot = torch.empty_like(k)
 
@@ -186,7 +203,7 @@ def bench_prefill(w, steps, warmup, settle_s=0.0):
     for _ in range(warmup):
         step()
     wall, ev = time_launches(step, steps)
-    flops = prefill_flops(w)
+    flops = prefill_flops(w, None if kv_lens is None else kv_lens.tolist())
     avg_ms = sum(ev) / len(ev)
     return {
         "value": flops * steps / wall / 1e12,
@@ -279,6 +296,9 @@ def cpu_baseline(w, budget_s=12.0):
         if w.path == "prefill_rope":
             oracle.prefill_rope(qd[:nb], kd[:nb], vd[:nb], ins[3].double().numpy(),
                                 ins[4].double().numpy(), causal=w.causal, scale=w.scale)
+        elif w.path == "prefill_varlen":
+            oracle.prefill_varlen(qd[:nb], kd[:nb], vd[:nb], ins[3][:nb].numpy(), causal=w.causal,
+                                  scale=w.scale)
         else:
             oracle.prefill(qd[:nb], kd[:nb], vd[:nb], causal=w.causal, scale=w.scale)
         return time.perf_counter() - t0
@@ -289,8 +309,11 @@ def cpu_baseline(w, budget_s=12.0):
     while total < budget_s or reps == 0:
         total += run(nb) if (nb > 1 or reps > 0) else t1
         reps += 1
-    per_b = prefill_flops(w) / w.B
-    return {"value": per_b * nb * reps / total / 1e12, "unit": "TFLOP/s",
+    if w.path == "prefill_varlen":
+        work = 4.0 * w.h_q * w.d * sum(varlen_pairs(w.L, int(n), w.causal) for n in ins[3][:nb])
+    else:
+        work = prefill_flops(w) / w.B * nb
+    return {"value": work * reps / total / 1e12, "unit": "TFLOP/s",
             "cores": oracle.num_threads(), "kind": "oracle", "seconds": total,
             "sample": f"{nb} of {w.B} batch elements of {w.name} (all {w.h_q} heads x {w.L} "
                       f"positions each), run {reps} time(s), fp64"}
@@ -338,7 +361,7 @@ def main(argv=None):
     ap.add_argument("--workload", default="worked_example_prefill_bf16",
                     choices=[n for n in wl.WORKLOAD_ORDER
                              if wl.WORKLOADS[n].path in ("prefill", "prefill_chunk",
-                                                         "prefill_rope")])
+                                                         "prefill_rope", "prefill_varlen")])
     ap.add_argument("--decode-workload", default="batched_decode_bf16",
                     choices=["none"] + [n for n in wl.WORKLOAD_ORDER
                                         if wl.WORKLOADS[n].path == "decode"])

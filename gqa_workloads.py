@@ -36,7 +36,8 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    # "prefill", "prefill_chunk", "prefill_rope", "decode", "decode_append" or "decode_paged"
+    # "prefill", "prefill_chunk", "prefill_rope", "prefill_varlen", "decode",
+    # "decode_append" or "decode_paged"
     path: str
     dtype: str  # "f32" or "bf16"
     B: int
@@ -48,7 +49,9 @@ class Workload:
     S: int = 0  # decode cache capacity
     causal: bool = False
     std: float = 1.0
-    seqlen_range: tuple = (0, 0)  # decode: inclusive [lo, hi] (decode_append: before the append)
+    # decode: inclusive [lo, hi] of the lengths (decode_append: before the append);
+    # prefill_varlen: of the valid lengths in the padded batch
+    seqlen_range: tuple = (0, 0)
     seed: int = 0
     page_size: int = 0  # decode_paged: rows per page
     description: str = field(default="", compare=False)
@@ -101,6 +104,11 @@ WORKLOADS = {
         d=128, causal=True, std=1.0 / math.sqrt(2.0), seed=3,
         description="bf16 causal prefill with rotary embedding (tables for base 10000), "
                     "B=1 L=4096 h_q=32 h_kv=8 d=128"),
+    "varlen_prefill_bf16": Workload(
+        "varlen_prefill_bf16", "prefill_varlen", "bf16", B=16, L=2048, h_q=32, h_kv=8, d=128,
+        causal=True, std=1.0 / math.sqrt(2.0), seqlen_range=(128, 2048), seed=8,
+        description="bf16 causal prefill of a padded batch, B=16 L=2048 lengths U{128..2048} "
+                    "h_q=32 h_kv=8 d=128"),
     "batched_decode_paged_bf16": Workload(
         "batched_decode_paged_bf16", "decode_paged", "bf16", B=64, h_q=32, h_kv=8, d=128,
         S=8192, std=1.0, seqlen_range=(1024, 8192), seed=4, page_size=64,
@@ -114,7 +122,7 @@ WORKLOADS = {
 WORKLOAD_ORDER = ["tiny_prefill_f32", "worked_example_prefill_bf16", "llama2_7b_prefill_bf16",
                   "batched_decode_bf16", "long_context_prefill_bf16", "chunked_prefill_bf16",
                   "batched_decode_append_bf16", "batched_decode_paged_bf16",
-                  "llama2_7b_prefill_rope_bf16"]
+                  "llama2_7b_prefill_rope_bf16", "varlen_prefill_bf16"]
 
 
 def _draw(gen, shape, std, dtype):
@@ -216,6 +224,12 @@ def workload_inputs(w: Workload):
     if w.path == "prefill_chunk":
         return prefill_chunk_inputs(w.B, w.L, w.Lk, w.h_q, w.h_kv, w.d, w.seed, w.std,
                                     w.torch_dtype())
+    if w.path == "prefill_varlen":
+        q, k, v = prefill_inputs(w.B, w.L, w.h_q, w.h_kv, w.d, w.seed, w.std, w.torch_dtype())
+        lo, hi = w.seqlen_range
+        gen = torch.Generator(device="cpu").manual_seed(int(w.seed) + 1000)
+        lens = torch.randint(lo, hi + 1, (w.B,), generator=gen, dtype=torch.int64)
+        return q, k, v, lens.to(torch.int32)
     if w.path == "prefill_rope":
         q, k, v = prefill_inputs(w.B, w.L, w.h_q, w.h_kv, w.d, w.seed, w.std, w.torch_dtype())
         cos, sin = rope_tables(w.L, w.d)

@@ -16,6 +16,8 @@ the device is not a gfx950 GPU, the calls raise.
     decode(q, k_cache, v_cache, seqlens, out=None, workspace=None, num_splits=0)
         q [B, 1, h_q, d] bf16, caches [B, h_kv, S, d] bf16, seqlens [B] int32
         -> o [B, 1, h_q, d].
+    prefill_varlen(q, k, v, kv_lens, causal=..., scale=None, out=None)
+        padded batch; key j of sequence b visible iff j < kv_lens[b].
     prefill_rope(q, k, v, cos, sin, causal=..., scale=None, out=None, k_rot=None)
         q and k rotated (tables cos, sin [L, d/2]), then prefill; returns
         (o, k_rot).
@@ -76,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.gqa_decode_token_major.restype = I
     L.gqa_decode_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, ctypes.c_size_t, P]
     L.gqa_decode_paged.restype = I
+    L.gqa_prefill_varlen.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P]
+    L.gqa_prefill_varlen.restype = I
     L.gqa_prefill_rope.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
     L.gqa_prefill_rope.restype = I
     L.gqa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -342,3 +346,28 @@ def prefill_rope(q, k, v, cos, sin, *, causal: bool, scale=None, out=None, k_rot
     if st != 0:
         raise GQAError(st, "gqa_prefill_rope")
     return out, k_rot
+
+
+def prefill_varlen(q, k, v, kv_lens, *, causal: bool, scale=None, out=None):
+    """Padded variable-length prefill: q [B,L,h_q,d], k/v [B,L,h_kv,d], kv_lens
+    [B] int32 (key j of sequence b visible iff j < kv_lens[b]) -> o."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, 4)
+    _check(kv_lens, "kv_lens", 1)
+    B, L, h_q, d = q.shape
+    h_kv = k.shape[2]
+    if tuple(k.shape) != (B, L, h_kv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, L, h_kv, d] with q's B, L and d")
+    if kv_lens.dtype != torch.int32 or kv_lens.shape[0] != B:
+        raise ValueError("kv_lens must be int32 [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", 4)
+    st = lib().gqa_prefill_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  kv_lens.data_ptr(), B, L, h_q, h_kv, d, _dtype_code(q),
+                                  int(bool(causal)), float(scale), _stream(q))
+    if st != 0:
+        raise GQAError(st, "gqa_prefill_varlen")
+    return out

@@ -77,8 +77,13 @@ gqa_status prefill_impl(const void *q, const void *k, const void *v, void *o, in
                         int Lk, int h_q, int h_kv, int d, gqa_dtype dt, int causal, float scale,
                         void *hip_stream, const float *rope_cos = nullptr,
                         const float *rope_sin = nullptr, void *k_rot = nullptr,
-                        bool rope = false) {
+                        bool rope = false, const int32_t *kv_lens = nullptr,
+                        bool varlen = false) {
     if (!q || !k || !v || !o) return GQA_ERR_NULL_POINTER;
+    if (varlen) {
+        if (!kv_lens) return GQA_ERR_NULL_POINTER;
+        if ((reinterpret_cast<uintptr_t>(kv_lens) & 3u) != 0) return GQA_ERR_ALIGNMENT;
+    }
     if (rope) {
         if (!rope_cos || !rope_sin || !k_rot) return GQA_ERR_NULL_POINTER;
         if (!aligned16(rope_cos) || !aligned16(rope_sin) || !aligned16(k_rot))
@@ -118,6 +123,7 @@ gqa_status prefill_impl(const void *q, const void *k, const void *v, void *o, in
     a.c = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
     a.rope_cos = rope ? rope_cos : nullptr;
     a.rope_sin = rope ? rope_sin : nullptr;
+    a.kv_lens = varlen ? kv_lens : nullptr;
     if ((int64_t)a.n_units * a.n_qtiles > 0x7fffffff) return GQA_ERR_SIZE;
 
     gqa_status st = check_device();
@@ -162,6 +168,13 @@ gqa_status gqa_prefill_rope(const void *q, const void *k, const void *v, const f
                             void *hip_stream) {
     return prefill_impl(q, k, v, o, B, L, L, h_q, h_kv, d, dt, causal, scale, hip_stream,
                         cos_table, sin_table, k_rot, true);
+}
+
+gqa_status gqa_prefill_varlen(const void *q, const void *k, const void *v, void *o,
+                              const int32_t *kv_lens, int B, int L, int h_q, int h_kv, int d,
+                              gqa_dtype dt, int causal, float scale, void *hip_stream) {
+    return prefill_impl(q, k, v, o, B, L, L, h_q, h_kv, d, dt, causal, scale, hip_stream, nullptr,
+                        nullptr, nullptr, false, kv_lens, true);
 }
 
 int gqa_decode_default_splits(void) { return kDefaultSplits; }

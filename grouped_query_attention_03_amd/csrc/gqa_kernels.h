@@ -22,6 +22,9 @@ struct PrefillArgs {
     // rotary tables cos, sin [positions][d/2] fp32 (row p for position p);
     // non-null only in the rotary form, where q is rotated as it is loaded
     const float *rope_cos, *rope_sin;
+    // per-sequence key lengths [B] (key j of sequence b visible iff j <
+    // kv_lens[b]), or null: all Lk keys
+    const int32_t *kv_lens;
 };
 
 // Rotary embedding of key rows x [rows][d] (rows in [B][L][h][...] order) into

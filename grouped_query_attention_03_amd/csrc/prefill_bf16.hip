@@ -98,7 +98,8 @@ __device__ __forceinline__ void block_barrier() {
 }
 
 // ROPE: q is rotated as it is loaded (the keys arrive rotated already).
-template <int D, bool CAUSAL, bool ROPE>
+// VARLEN: sequence b has a.kv_lens[b] visible keys (a padded batch).
+template <int D, bool CAUSAL, bool ROPE, bool VARLEN>
 __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs a) {
     using Lay = PfLay<D>;
     constexpr int KSTEPS = Lay::KSTEPS, DB = Lay::DB, DPW = Lay::DMA_PER_WAVE;
@@ -118,7 +119,10 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
     const int bk = unit / a.nsub;
     const int kvh = bk % a.h_kv;
     const int b = bk / a.h_kv;
-    const int L = a.L, Lk = a.Lk, off = a.off;  // query rows, keys, position of row 0
+    const int L = a.L, off = a.off;  // query rows, position of row 0
+    const int Lt = a.Lk;             // key rows per sequence in the tensors
+    // visible keys of this sequence: all, or its length (clamped to [0, Lt])
+    const int Lk = VARLEN ? min(max(load_const(a.kv_lens, b), 0), Lt) : Lt;
     const int PB = 8 / a.GW;  // 32-position blocks per work-group
     const int p0 = qt * a.BM;
 
@@ -141,8 +145,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
     // and then reads zeros or finite data of the same tensor, which the mask
     // discards.
     const u32x4 rsrc = make_buffer_rsrc(
-        static_cast<const __bf16 *>(loads_v ? a.v : a.k) + ((size_t)b * Lk * a.h_kv + kvh) * D,
-        (unsigned)(Lk - 1) * krb + 2 * D);
+        static_cast<const __bf16 *>(loads_v ? a.v : a.k) + ((size_t)b * Lt * a.h_kv + kvh) * D,
+        (!VARLEN || Lk > 0) ? (unsigned)(Lk - 1) * krb + 2 * D : 0u);
     // per-lane byte offset of piece i within its rows; depends on i only via i % NLO
     unsigned loff[NLO];
 #pragma unroll
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     block_barrier();
-    issue_tile(0);
+    if (!VARLEN || ntiles > 0) issue_tile(0);  // a zero-length sequence has no tile
 #pragma unroll
     for (int x = 1; x < PF_DIST; ++x)
         if (x < ntiles) issue_tile(x);
@@ -359,7 +363,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
     const float lt = l_run + other_half(l_run);
     const int pos = pos0 + (lane & 31);
     if (pos < L) {
-        const float inv = 1.f / lt;
+        // no visible key (only a zero-length sequence): a zero row
+        const float inv = (!VARLEN || lt > 0.f) ? 1.f / lt : 0.f;
         __bf16 *op = static_cast<__bf16 *>(a.o) + (((size_t)b * L + pos) * a.h_q + head) * D +
                      4 * (lane >> 5);
 #pragma unroll
@@ -378,25 +383,26 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
 
 int launch_prefill_bf16(const PrefillArgs &a, int d, bool causal, hipStream_t stream) {
     dim3 grid(a.n_units * a.n_qtiles), block(PF_THREADS);
-    const bool rope = a.rope_cos != nullptr;
-#define GQA_PF_LAUNCH(D_, C_, R_) \
-    hipLaunchKernelGGL((prefill_bf16_kernel<D_, C_, R_>), grid, block, 0, stream, a)
+    // forms: plain, rotary (q rotated at load), variable length
+    const int form = a.rope_cos != nullptr ? 1 : a.kv_lens != nullptr ? 2 : 0;
+#define GQA_PF_LAUNCH(D_, C_)                                                                  \
+    do {                                                                                       \
+        if (form == 1)                                                                         \
+            hipLaunchKernelGGL((prefill_bf16_kernel<D_, C_, true, false>), grid, block, 0,     \
+                               stream, a);                                                     \
+        else if (form == 2)                                                                    \
+            hipLaunchKernelGGL((prefill_bf16_kernel<D_, C_, false, true>), grid, block, 0,     \
+                               stream, a);                                                     \
+        else                                                                                   \
+            hipLaunchKernelGGL((prefill_bf16_kernel<D_, C_, false, false>), grid, block, 0,    \
+                               stream, a);                                                     \
+    } while (0)
     if (d == 128) {
-        if (causal) {
-            if (rope) GQA_PF_LAUNCH(128, true, true);
-            else GQA_PF_LAUNCH(128, true, false);
-        } else {
-            if (rope) GQA_PF_LAUNCH(128, false, true);
-            else GQA_PF_LAUNCH(128, false, false);
-        }
+        if (causal) GQA_PF_LAUNCH(128, true);
+        else GQA_PF_LAUNCH(128, false);
     } else {
-        if (causal) {
-            if (rope) GQA_PF_LAUNCH(64, true, true);
-            else GQA_PF_LAUNCH(64, true, false);
-        } else {
-            if (rope) GQA_PF_LAUNCH(64, false, true);
-            else GQA_PF_LAUNCH(64, false, false);
-        }
+        if (causal) GQA_PF_LAUNCH(64, true);
+        else GQA_PF_LAUNCH(64, false);
     }
 #undef GQA_PF_LAUNCH
     return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -31,15 +31,18 @@ __global__ __launch_bounds__(PF32_THREADS) void prefill_f32_kernel(PrefillArgs a
     const int bk = unit / a.nsub;
     const int kvh = bk % a.h_kv;
     const int b = bk / a.h_kv;
-    const int L = a.L, Lk = a.Lk, off = a.off;  // query rows, keys, position of row 0
+    const int L = a.L, off = a.off;  // query rows, position of row 0
+    const int Lt = a.Lk;             // key rows per sequence in the tensors
+    // visible keys of this sequence: all, or its length (clamped to [0, Lt])
+    const int Lk = a.kv_lens ? min(max(load_const(a.kv_lens, b), 0), Lt) : Lt;
     const int p0 = qt * a.BM;
     const int hl = tid / a.BM, pp = tid % a.BM;
     const int pos = p0 + pp;
     const int head = kvh * a.G + sub * a.GW + hl;
 
     const float *qg = static_cast<const float *>(a.q);
-    const float *kg = static_cast<const float *>(a.k) + ((size_t)b * Lk * a.h_kv + kvh) * D;
-    const float *vg = static_cast<const float *>(a.v) + ((size_t)b * Lk * a.h_kv + kvh) * D;
+    const float *kg = static_cast<const float *>(a.k) + ((size_t)b * Lt * a.h_kv + kvh) * D;
+    const float *vg = static_cast<const float *>(a.v) + ((size_t)b * Lt * a.h_kv + kvh) * D;
     const size_t kv_row = (size_t)a.h_kv * D;
 
     float qv[D], ov[D];
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(PF32_THREADS) void prefill_f32_kernel(PrefillArgs a
     }
 
     if (pos < L) {
-        float inv = 1.f / l;
+        float inv = l > 0.f ? 1.f / l : 0.f;  // no visible key: a zero row
         float *op = static_cast<float *>(a.o) + (((size_t)b * L + pos) * a.h_q + head) * D;
 #pragma unroll
         for (int cc = 0; cc < D; cc += 4)

@@ -92,6 +92,24 @@ gqa_status gqa_prefill_chunk(const void *q, const void *k, const void *v, void *
                              int causal, float scale, void *hip_stream);
 
 /*
+ * Prefill of a padded batch of variable-length sequences.  The attention mask
+ * that handles variable-length sequences ("Implementing GQA from scratch in
+ * PyTorch", §3.3: masked_fill(mask == 0, -inf)) given as lengths: key j of
+ * sequence b is visible iff j < kv_lens[b] (and j <= i when causal).
+ *   q, k, v, o, B, L, h_q, h_kv, d, dt, causal, scale: as gqa_prefill (both
+ *          dtypes); positions at or beyond kv_lens[b] are padding.
+ *   kv_lens : [B] int32 on the device, 4-byte aligned; values are clamped to
+ *          [0, L] on the device.  Key/value rows at or beyond kv_lens[b] are
+ *          never read into a result (they may hold anything, NaN included).
+ * Every query row is computed, padded rows included: a padded row attends to
+ * all kv_lens[b] keys.  A row with no visible key (kv_lens[b] == 0) is zero.
+ * With every kv_lens[b] == L the result equals gqa_prefill bit for bit.
+ */
+gqa_status gqa_prefill_varlen(const void *q, const void *k, const void *v, void *o,
+                              const int32_t *kv_lens, int B, int L, int h_q, int h_kv, int d,
+                              gqa_dtype dt, int causal, float scale, void *hip_stream);
+
+/*
  * Prefill with rotary position embedding: q and k are rotated, then the
  * prefill above runs on the rotated q, k and the unrotated v ("Attention in
  * Qwen, DeepSeek and LLaMA3", §1, apply_rotary_pos_emb).  For a row x at

@@ -30,6 +30,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("gqa_prefill", "gqa_prefill_chunk", "gqa_decode", "gqa_decode_append",
               "gqa_decode_token_major", "gqa_decode_paged", "gqa_prefill_rope",
+              "gqa_prefill_varlen",
               "gqa_decode_workspace_bytes",
               "gqa_decode_default_splits", "gqa_status_string"):
         assert n in names
@@ -102,6 +103,29 @@ def test_prefill_chunk_without_a_gpu_reports_the_device():
         pytest.skip("a GPU is present")
     assert chunk_status() == DEVICE
     assert chunk_status(Lq=64, Lk=64) == DEVICE  # the square case is valid too
+
+
+def varlen_status(q=A, k=A, v=A, o=A, kl=A, B=2, L=16, h_q=8, h_kv=2, d=64, dt=1, causal=1,
+                  scale=0.125):
+    return gqa.lib().gqa_prefill_varlen(q, k, v, o, kl, B, L, h_q, h_kv, d, dt, causal,
+                                        ctypes.c_float(scale), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kl=None), NULLP), (dict(v=None), NULLP), (dict(kl=A + 2), ALIGN), (dict(o=MIS), ALIGN),
+    (dict(L=0), SIZE), (dict(B=0), SIZE), (dict(h_q=8, h_kv=3), HEADS), (dict(d=32), HEADDIM),
+    (dict(dt=7), DTYPE), (dict(scale=float("inf")), SIZE),
+])
+def test_prefill_varlen_rejects_bad_arguments(kw, status):
+    assert varlen_status(**kw) == status
+
+
+def test_prefill_varlen_without_a_gpu_reports_the_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert varlen_status(kl=A + 4) == DEVICE
+    assert varlen_status(dt=0) == DEVICE  # fp32 is served too
 
 
 def rope_status(q=A, k=A, v=A, c=A, s=A, o=A, kr=A + 0x100, B=1, L=16, h_q=8, h_kv=2, d=64,

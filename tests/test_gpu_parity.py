@@ -708,3 +708,69 @@ def test_workload_llama2_prefill_rope(dev):
                               causal=w.causal, scale=w.scale)
     ti = torch.tensor(rows)
     check(f64(out[ti[:, 0], ti[:, 1], ti[:, 2]]), ref, "bf16", f"{w.name}: {len(rows)} sampled rows")
+
+
+# ------------------------------------------------ prefill of variable-length sequences
+
+VARLEN_SMALL = [
+    # B, L, h_q, h_kv, d, dtype, causal, lengths
+    (7, 200, 32, 8, 128, "bf16", True, [200, 0, 1, 63, 64, 65, 137]),
+    (4, 333, 8, 8, 64, "bf16", False, [333, 1, 256, 100]),    # G = 1
+    (3, 130, 16, 2, 128, "bf16", False, [0, 130, 64]),         # G = 8
+    (3, 96, 8, 2, 64, "f32", True, [96, 33, 0]),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_SMALL,
+                         ids=lambda c: "B{}_L{}_hq{}_hkv{}_d{}_{}_c{}".format(*c[:7]))
+def test_prefill_varlen_matches_oracle(case, dev):
+    B, L, h_q, h_kv, d, dtype, causal, lens = case
+    seed = 7000 + L + h_q
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q, k, v = wl.prefill_inputs(B, L, h_q, h_kv, d, seed, 1.0, tdt)
+    kv_lens = torch.tensor(lens, dtype=torch.int32)
+    for b, n in enumerate(lens):  # padding keys and values: never read into a result
+        k[b, n:] = float("nan")
+        v[b, n:] = float("nan")
+    scale = 1 / math.sqrt(d)
+    say(f"prefill varlen {case} seed {seed}")
+    out = gqa.prefill_varlen(q.to(dev), k.to(dev), v.to(dev), kv_lens.to(dev), causal=causal,
+                             scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_varlen(f64(q), f64(k), f64(v), lens, causal, scale)
+    check(f64(out.cpu()), ref, dtype, f"varlen {case}")
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert torch.equal(out[b].cpu(), torch.zeros_like(out[b].cpu()))
+
+
+def test_prefill_varlen_full_lengths_is_prefill(dev):
+    B, L, h_q, h_kv, d = 2, 300, 32, 8, 128
+    q, k, v = wl.prefill_inputs(B, L, h_q, h_kv, d, 72, 1.0, torch.bfloat16)
+    kv_lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    say("varlen with every length L vs plain prefill")
+    for causal in (True, False):
+        a = gqa.prefill_varlen(q.to(dev), k.to(dev), v.to(dev), kv_lens, causal=causal, scale=0.09)
+        b = run_prefill(q, k, v, causal, 0.09, dev)
+        assert torch.equal(a.cpu(), b.cpu())
+
+
+def test_workload_varlen_prefill(dev):
+    w = wl.WORKLOADS["varlen_prefill_bf16"]
+    q, k, v, kv_lens = wl.workload_inputs(w)
+    say(f"prefill workload {w.name} ({w.description}) lengths {kv_lens.tolist()}")
+    out = gqa.prefill_varlen(q.to(dev), k.to(dev), v.to(dev), kv_lens.to(dev), causal=w.causal,
+                             scale=w.scale)
+    torch.cuda.synchronize()
+    out = out.cpu()
+    assert not torch.isnan(out).any()
+    # sampled rows, plus the last valid and first padded row of the shortest sequence
+    b0 = int(torch.argmin(kv_lens))
+    n0 = int(kv_lens[b0])
+    rows = wl.sample_rows(192, w.B, w.L, w.h_q, w.seed,
+                          include=[(b0, n0 - 1, 0), (b0, min(n0, w.L - 1), w.h_q - 1),
+                                   (w.B - 1, w.L - 1, 3)])
+    idx = torch.tensor(rows)
+    ref = oracle.prefill_varlen_rows(f64(q[idx[:, 0], idx[:, 1], idx[:, 2]]), rows, f64(k), f64(v),
+                                     kv_lens.numpy(), w.h_q, w.causal, w.scale)
+    check(f64(out[idx[:, 0], idx[:, 1], idx[:, 2]]), ref, "bf16", f"{w.name}: {len(rows)} rows")
