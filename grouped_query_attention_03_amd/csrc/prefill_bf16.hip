@@ -260,12 +260,23 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
             s[kb] = mfma32x32x16(kread(kt, st), qf[ks], ks == 0 ? negm : s[kb]);
         }
     };
+    // At d = 128 the V^T operands of the whole tile are read into registers
+    // right after QK, so their LDS latency passes under the softmax; at d = 64
+    // the extra registers would cost a wave per SIMD, and PV reads them as it goes.
+    constexpr bool V_EARLY = D == 128;
+    bf16x8 vf[V_EARLY ? NSTEP : 1];
+    auto vload = [&](int j) {
+        const char *vt = smem + (j % PF_SLOTS) * Lay::SLOT_BYTES + Lay::TILE_BYTES;
+#pragma unroll
+        for (int st = 0; st < NSTEP; ++st) vf[V_EARLY ? st : 0] = vread(vt, st);
+    };
     auto pv = [&](int j) {  // O^T += V^T P^T for tile j
         const char *vt = smem + (j % PF_SLOTS) * Lay::SLOT_BYTES + Lay::TILE_BYTES;
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) {
             const int kh = st / DB, db = st % DB;
-            acc[db] = mfma32x32x16(vread(vt, st), pb[kh >> 1][kh & 1], acc[db]);
+            acc[db] = mfma32x32x16(V_EARLY ? vf[V_EARLY ? st : 0] : vread(vt, st),
+                                   pb[kh >> 1][kh & 1], acc[db]);
         }
     };
     // Softmax of tile j: mask, running max, P = exp2(S c - m), row sums.
@@ -333,7 +344,9 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     block_barrier();
-    if (!VARLEN || ntiles > 0) issue_tile(0);  // a zero-length sequence has no tile
+    // a zero-length sequence has no tile; its buffer range is empty, so these
+    // loads read zeros without touching memory
+    issue_tile(0);
 #pragma unroll
     for (int x = 1; x < PF_DIST; ++x)
         if (x < ntiles) issue_tile(x);
@@ -348,6 +361,10 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
         if (j + PF_DIST < ntiles) issue_tile(j + PF_DIST);
         if (active(j)) {
             qk(j);
+            if (V_EARLY) {
+                vload(j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             softmax(j);
             pv(j);
         }
