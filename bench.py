@@ -120,17 +120,24 @@ def recorded_traffic(kind: str, workload: str, launches_per_step: int = 1):
     if not os.path.exists(TRAFFIC_SUMMARY):
         return None
     digest = source_digest(KERNEL_SOURCES[kind])
+    total, found = 0.0, False
     for line in open(TRAFFIC_SUMMARY):
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
-        if len(cells) < 5 or cells[0] != kind or cells[1] != workload:
+        if len(cells) < 5:
+            continue
+        # a decode call is the split pass of its workload plus the merge pass
+        # (one row, the mean over the decode workloads)
+        if not ((cells[0] == kind and cells[1] == workload) or
+                (kind == "decode" and cells[0] == "decode_merge")):
             continue
         if cells[2] != digest:
             return None
         try:
-            return float(cells[3]) + float(cells[4])
+            total += float(cells[3]) + float(cells[4])
+            found = True
         except ValueError:
             return None
-    return None
+    return total if found else None
 
 
 def time_launches(fn, steps, before=None):
