@@ -774,3 +774,41 @@ def test_workload_varlen_prefill(dev):
     ref = oracle.prefill_varlen_rows(f64(q[idx[:, 0], idx[:, 1], idx[:, 2]]), rows, f64(k), f64(v),
                                      kv_lens.numpy(), w.h_q, w.causal, w.scale)
     check(f64(out[idx[:, 0], idx[:, 1], idx[:, 2]]), ref, "bf16", f"{w.name}: {len(rows)} rows")
+
+
+# ------------------------------------------------------------------ maximum sizes
+
+def test_decode_largest_split_count(dev):
+    # num_splits at its limit (2^20 slices: most waves get an empty slice and
+    # exit; the workspace is about 4 GiB)
+    B, h_q, h_kv, S, d = 2, 8, 2, 700, 64
+    seqlens, q, kc, vc = wl.decode_inputs(B, h_q, h_kv, S, d, 81, (1, S))
+    say(f"decode num_splits 2^20, workspace {gqa.decode_workspace_bytes(B, h_q, h_kv, d, 1 << 20)}")
+    out = run_decode(seqlens, q, kc, vc, dev, splits=1 << 20).cpu()
+    check(f64(out[:, 0]), decode_ref(seqlens, q, kc, vc), "bf16", "decode num_splits 2^20")
+
+
+@pytest.mark.parametrize("h_q,h_kv", [(64, 1), (128, 2)])
+def test_prefill_wide_group(h_q, h_kv, dev):
+    # G = 64: eight work-groups of 8 heads share each key/value head
+    B, L, d = 1, 300, 128
+    q, k, v = wl.prefill_inputs(B, L, h_q, h_kv, d, 82 + h_q, 1.0, torch.bfloat16)
+    say(f"prefill wide group h_q {h_q} h_kv {h_kv}")
+    for causal in (True, False):
+        out = run_prefill(q, k, v, causal, 1 / math.sqrt(d), dev).cpu()
+        check(f64(out), oracle.prefill(f64(q), f64(k), f64(v), causal=causal, scale=1 / math.sqrt(d)),
+              "bf16", f"prefill G=64 h_q={h_q} causal={causal}")
+
+
+@pytest.mark.parametrize("h_q,h_kv,d", [(64, 1, 128), (128, 2, 64)])
+def test_decode_wide_group(h_q, h_kv, d, dev):
+    # G = 64: four subgroups of 16 query heads per key/value head
+    B, S = 3, 500
+    seqlens, q, kc, vc = wl.decode_inputs(B, h_q, h_kv, S, d, 84 + h_q, (1, S))
+    seqlens[0] = 1
+    seqlens[2] = S
+    say(f"decode wide group h_q {h_q} h_kv {h_kv} d {d}")
+    for splits in (0, 17):
+        out = run_decode(seqlens, q, kc, vc, dev, splits=splits).cpu()
+        check(f64(out[:, 0]), decode_ref(seqlens, q, kc, vc), "bf16",
+              f"decode G=64 h_q={h_q} splits={splits}")
