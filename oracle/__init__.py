@@ -87,6 +87,8 @@ def _load():
     lib.gqa_oracle_prefill_varlen_rows.argtypes = [P, P, ctypes.c_int64, P, P, P, I, I, I, I, I,
                                                    I, ctypes.c_double, P]
     lib.gqa_oracle_prefill_varlen_rows.restype = I
+    lib.gqa_oracle_decode_append_rope.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I]
+    lib.gqa_oracle_decode_append_rope.restype = I
     lib.gqa_oracle_rope.argtypes = [P, P, P, P, I, I, I, I]
     lib.gqa_oracle_rope.restype = I
     lib.gqa_oracle_prefill_rope.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I,
@@ -275,6 +277,29 @@ def prefill_rope(q, k, v, cos, sin, causal, scale):
     if rc != 0:
         raise ValueError("oracle prefill_rope rejected its arguments (rc=%d)" % rc)
     return o, k_rot
+
+
+def decode_append_rope(q, k_new, v_new, k_cache, v_cache, seqlens, cos, sin):
+    """Decode step with rotary embedding: q [B,h_q,d] and k_new [B,h_kv,d]
+    rotated with row seqlens[b] of cos, sin [S, d/2], the rotated key appended
+    at row seqlens[b], then attend.  Returns (o, k_cache', v_cache') (copies)."""
+    q, kn, vn = _f64(q), _f64(k_new), _f64(v_new)
+    kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
+    ct, st = _f64(cos), _f64(sin)
+    sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+    B, h_q, d = q.shape
+    _, h_kv, S, _ = kc.shape
+    if (kc.shape != (B, h_kv, S, d) or vc.shape != kc.shape or kn.shape != (B, h_kv, d)
+            or vn.shape != kn.shape or sl.shape != (B,) or ct.shape != (S, d // 2)
+            or st.shape != ct.shape):
+        raise ValueError("decode_append_rope shapes do not match")
+    o = np.empty_like(q)
+    rc = _load().gqa_oracle_decode_append_rope(_ptr(q), _ptr(kn), _ptr(vn), _ptr(kc), _ptr(vc),
+                                               _ptr(sl), _ptr(ct), _ptr(st), _ptr(o), B, h_q,
+                                               h_kv, S, d)
+    if rc != 0:
+        raise ValueError("oracle decode_append_rope rejected its arguments (rc=%d)" % rc)
+    return o, kc, vc
 
 
 def decode_token_major(q, k_cache, v_cache, seqlens):

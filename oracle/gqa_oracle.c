@@ -58,10 +58,10 @@
  *     sequence b.  Logical row j of (b, g) is block_table[b][j / page_size],
  *     group g, row j % page_size.
  *
- *   Variable-length sequences in a padded batch: the page's forward pass takes
- *   an attention mask applied as masked_fill(mask == 0, -inf) "to handle
- *   variable-length sequences" ("Implementing GQA from scratch in PyTorch",
- *   §3.3).  Read as a key-padding mask given by lengths: key j of sequence b
+ *   Variable-length sequences in a padded batch: the forward pass of
+ *   "Implementing GQA from scratch in PyTorch", §3.3 takes an optional mask,
+ *   applied as masked_fill(mask == 0, -inf), for sequences of different
+ *   lengths.  Read as a key-padding mask given by lengths: key j of sequence b
  *   is visible iff j < kv_lens[b] (and j <= i when causal).  Every query row
  *   is computed, padded ones included; a row with no visible key is zero.
  *
@@ -74,7 +74,9 @@
  *     out[d/2 + i] = x[2i] sin[p][i] + x[2i+1] cos[p][i]      (0 <= i < d/2)
  *   -- the even/odd pairs rotated, the two results concatenated along the
  *   last axis as the page writes it.  q and k are rotated, v is not; then the
- *   attention above.
+ *   attention above.  In a decode step the new token sits at position
+ *   seqlens[b]: its q and k are rotated with row seqlens[b] of the tables,
+ *   the rotated key is appended, then the token attends (decode with append).
  *
  * Every entry point returns 0 on success and a negative number for a bad
  * argument (it never aborts).  Arrays are dense, row-major, caller-owned.
@@ -357,6 +359,58 @@ int gqa_oracle_rope(const double *x, const double *cos_t, const double *sin_t, d
                 }
             }
     return 0;
+}
+
+/* One vector: out = rotation of x (length d) by the table rows c, s (length d/2). */
+static void rope_vec(const double *x, const double *c, const double *s, double *out, int d) {
+    const int half = d / 2;
+    for (int i = 0; i < half; ++i) {
+        out[i] = x[2 * i] * c[i] - x[2 * i + 1] * s[i];
+        out[half + i] = x[2 * i] * s[i] + x[2 * i + 1] * c[i];
+    }
+}
+
+/*
+ * Decode step with rotary embedding: the new token of sequence b sits at
+ * position seqlens[b] (0 <= seqlens[b] < S); q [B][h_q][d] and k_new
+ * [B][h_kv][d] are rotated with row seqlens[b] of cos, sin [S][d/2], the
+ * rotated key and v_new are appended (gqa_oracle_decode_append), then the
+ * token attends.
+ */
+int gqa_oracle_decode_append(const double *q, const double *k_new, const double *v_new,
+                             double *k_cache, double *v_cache, const int32_t *seqlens,
+                             double *o, int B, int h_q, int h_kv, int S, int d);
+
+int gqa_oracle_decode_append_rope(const double *q, const double *k_new, const double *v_new,
+                                  double *k_cache, double *v_cache, const int32_t *seqlens,
+                                  const double *cos_t, const double *sin_t, double *o, int B,
+                                  int h_q, int h_kv, int S, int d) {
+    if (B <= 0 || S <= 0 || d <= 0 || d % 2 != 0) return ORACLE_ERR_ARG;
+    if (check_heads(h_q, h_kv)) return ORACLE_ERR_ARG;
+    for (int b = 0; b < B; ++b)
+        if (seqlens[b] < 0 || seqlens[b] >= S) return ORACLE_ERR_ARG;
+    double *qr = (double *)malloc(sizeof(double) * (size_t)B * h_q * d);
+    double *kr = (double *)malloc(sizeof(double) * (size_t)B * h_kv * d);
+    if (!qr || !kr) {
+        free(qr);
+        free(kr);
+        return ORACLE_ERR_NOMEM;
+    }
+    const int half = d / 2;
+    for (int b = 0; b < B; ++b) {
+        const long p = seqlens[b];
+        for (int h = 0; h < h_q; ++h)
+            rope_vec(q + ((long)b * h_q + h) * d, cos_t + p * half, sin_t + p * half,
+                     qr + ((long)b * h_q + h) * d, d);
+        for (int g = 0; g < h_kv; ++g)
+            rope_vec(k_new + ((long)b * h_kv + g) * d, cos_t + p * half, sin_t + p * half,
+                     kr + ((long)b * h_kv + g) * d, d);
+    }
+    int rc = gqa_oracle_decode_append(qr, kr, v_new, k_cache, v_cache, seqlens, o, B, h_q, h_kv,
+                                      S, d);
+    free(qr);
+    free(kr);
+    return rc;
 }
 
 /*

@@ -619,6 +619,34 @@ def pin_varlen_library():
                np.array([o[b, i, h] for (b, i, h) in rows]), 0.0, "varlen rows vs full")
 
 
+def pin_rope_decode_step():
+    """A decode step with rotary embedding continues a rotary prefill: with the
+    cache holding the prefill's rotated keys of positions 0..n-1, appending
+    token n (rotated at position n) and attending gives the prefill's row n,
+    and the appended cache row is the prefill's rotated key n.  With identity
+    tables it is the plain decode with append of permuted q and k."""
+    B, n, h_q, h_kv, d, S = 2, 9, 6, 2, 8, 12
+    q, k, v = (_rand((B, n + 1, h_q, d), 250), _rand((B, n + 1, h_kv, d), 251),
+               _rand((B, n + 1, h_kv, d), 252))
+    c, sn = _rope_tables(S, d)
+    full, k_rot = oracle.prefill_rope(q, k, v, c[:n + 1], sn[:n + 1], True, 1 / math.sqrt(d))
+    kc = np.full((B, h_kv, S, d), np.nan)
+    vc = np.full((B, h_kv, S, d), np.nan)
+    kc[:, :, :n] = k_rot[:, :n].transpose(0, 2, 1, 3)
+    vc[:, :, :n] = v[:, :n].transpose(0, 2, 1, 3)
+    o, kc2, vc2 = oracle.decode_append_rope(q[:, n], k[:, n], v[:, n], kc, vc, [n] * B, c, sn)
+    _close(o, full[:, n], 1e-12, "rotary decode step vs rotary prefill row n")
+    _close(kc2[:, :, n], k_rot[:, n], 0.0, "appended row = the prefill's rotated key n")
+    _close(vc2[:, :, n], v[:, n], 0.0, "appended value row")
+    ones, zeros = np.ones((S, d // 2)), np.zeros((S, d // 2))
+    perm = list(range(0, d, 2)) + list(range(1, d, 2))
+    o1, k1, _ = oracle.decode_append_rope(q[:, n], k[:, n], v[:, n], kc, vc, [n] * B, ones, zeros)
+    o2, k2, _ = oracle.decode_append(q[:, n][..., perm], k[:, n][..., perm], v[:, n], kc, vc,
+                                     [n] * B)
+    _close(o1, o2, 0.0, "identity tables: plain decode of permuted q, k")
+    _close(k1[:, :, :n + 1], k2[:, :, :n + 1], 0.0, "identity tables: appended permuted key")
+
+
 ALL_PINS = [pin_hand_2x2, pin_head_map, pin_decode_golden, pin_mha_reduction,
             pin_mqa_reduction, pin_gqa_library, pin_rows_sum_to_one, pin_k_zero_mean,
             pin_causal_row0, pin_identical_heads, pin_invariances, pin_cross_path,
@@ -628,7 +656,7 @@ ALL_PINS = [pin_hand_2x2, pin_head_map, pin_decode_golden, pin_mha_reduction,
             pin_append_to_empty_cache, pin_append_brute_and_tail, pin_token_major_brute,
             pin_paged_brute, pin_paged_shared_prefix, pin_rope_golden,
             pin_rope_identity_tables, pin_rope_relative_position, pin_rope_brute,
-            pin_varlen_equals_truncated, pin_varlen_library]
+            pin_varlen_equals_truncated, pin_varlen_library, pin_rope_decode_step]
 
 
 def main(argv):

@@ -43,6 +43,8 @@ MUTANTS = {
                               "if (rc == 0) memcpy(k_rot, k, sizeof(double) * (size_t)B * L * h_kv * d);"),
     "varlen_lengths_ignored": ("if (kv_lens && kv_lens[b] < n_vis) n_vis = kv_lens[b]; /* key padding */",
                                "/* key padding dropped */"),
+    "rope_decode_position_off_by_one": ("const long p = seqlens[b];",
+                                        "const long p = seqlens[b] > 0 ? seqlens[b] - 1 : 0;"),
     "first_head_of_group_only": ("int kvh = kv_head_of(h, h_q, h_kv);\n                int n = seqlens[b];",
                                  "int kvh = 0;\n                int n = seqlens[b];"),
 }
