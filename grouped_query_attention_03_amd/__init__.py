@@ -21,6 +21,8 @@ the device is not a gfx950 GPU, the calls raise.
     prefill_rope(q, k, v, cos, sin, causal=..., scale=None, out=None, k_rot=None)
         q and k rotated (tables cos, sin [L, d/2]), then prefill; returns
         (o, k_rot).
+    decode_append_rope(q, k_new, v_new, k_cache, v_cache, seqlens, cos, sin, ...)
+        decode with append, q and k_new rotated at position seqlens[b] first.
     decode_token_major(q, k_cache, v_cache, seqlens, ...)
         as decode, with caches [B, S, h_kv, d].
     decode_paged(q, k_pages, v_pages, block_table, seqlens, ...)
@@ -82,6 +84,11 @@ def lib() -> ctypes.CDLL:
     L.gqa_prefill_varlen.restype = I
     L.gqa_prefill_rope.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
     L.gqa_prefill_rope.restype = I
+    L.gqa_decode_append_rope.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P,
+                                         ctypes.c_size_t, P]
+    L.gqa_decode_append_rope.restype = I
+    L.gqa_decode_rope_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.gqa_decode_rope_workspace_bytes.restype = ctypes.c_size_t
     L.gqa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     L.gqa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.gqa_decode_default_splits.argtypes = []
@@ -370,4 +377,47 @@ def prefill_varlen(q, k, v, kv_lens, *, causal: bool, scale=None, out=None):
                                   int(bool(causal)), float(scale), _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_prefill_varlen")
+    return out
+
+
+def decode_rope_workspace_bytes(B, h_q, h_kv, d, num_splits=0) -> int:
+    return int(lib().gqa_decode_rope_workspace_bytes(B, h_q, h_kv, d, num_splits))
+
+
+def decode_append_rope(q, k_new, v_new, k_cache, v_cache, seqlens, cos, sin, *, out=None,
+                       workspace=None, num_splits: int = 0):
+    """Decode step with rotary embedding: q [B,1,h_q,d] and k_new [B,1,h_kv,d]
+    rotated at position seqlens[b] (tables cos, sin [S, d/2] fp32), the rotated
+    key and v_new appended at cache row seqlens[b] (in place), then attend over
+    rows [0, seqlens[b] + 1) -> o [B,1,h_q,d]."""
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
+                 (v_cache, "v_cache")):
+        _check(t, n, 4)
+    _check(seqlens, "seqlens", 1)
+    _check(cos, "cos", 2)
+    _check(sin, "sin", 2)
+    B, one, h_q, d = q.shape
+    _, h_kv, S, _ = k_cache.shape
+    if one != 1 or tuple(k_cache.shape) != (B, h_kv, S, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("need q [B, 1, h_q, d] and caches [B, h_kv, S, d]")
+    if tuple(k_new.shape) != (B, 1, h_kv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [B, 1, h_kv, d]")
+    if (cos.dtype != torch.float32 or sin.dtype != torch.float32
+            or tuple(cos.shape) != (S, d // 2) or sin.shape != cos.shape):
+        raise ValueError("cos and sin must be float32 [S, d/2]")
+    if seqlens.dtype != torch.int32 or seqlens.shape[0] != B:
+        raise ValueError("seqlens must be int32 [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", 4)
+    need = decode_rope_workspace_bytes(B, h_q, h_kv, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().gqa_decode_append_rope(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                      k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
+                                      cos.data_ptr(), sin.data_ptr(), out.data_ptr(), B, h_q, h_kv,
+                                      S, d, _dtype_code(q), int(num_splits), workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(), _stream(q))
+    if st != 0:
+        raise GQAError(st, "gqa_decode_append_rope")
     return out

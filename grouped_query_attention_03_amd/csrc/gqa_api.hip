@@ -138,6 +138,7 @@ gqa_status prefill_impl(const void *q, const void *k, const void *v, void *o, in
         r.rows = (long long)B * Lk * h_kv;
         r.L = Lk;
         r.h = h_kv;
+        r.pos = nullptr;
         if (gqa::launch_rope_k_bf16(r, d, stream) != 0) return GQA_ERR_LAUNCH;
         a.k = k_rot;
     }
@@ -287,6 +288,61 @@ gqa_status gqa_decode_paged(const void *q, const void *k_pages, const void *v_pa
     return decode_impl(q, nullptr, nullptr, k_pages, v_pages, seqlens, o, B, h_q, h_kv, 0, d, dt,
                        num_splits, workspace, workspace_bytes, hip_stream, gqa::kLayoutPaged,
                        block_table, page_size, max_blocks);
+}
+
+size_t gqa_decode_rope_workspace_bytes(int B, int h_q, int h_kv, int d, int num_splits) {
+    const size_t base = gqa_decode_workspace_bytes(B, h_q, h_kv, d, num_splits);
+    if (base == 0) return 0;
+    return base + round_up_256((size_t)B * h_q * d * 2) + round_up_256((size_t)B * h_kv * d * 2);
+}
+
+gqa_status gqa_decode_append_rope(const void *q, const void *k_new, const void *v_new,
+                                  void *k_cache, void *v_cache, const int32_t *seqlens,
+                                  const float *cos_table, const float *sin_table, void *o, int B,
+                                  int h_q, int h_kv, int S, int d, gqa_dtype dt, int num_splits,
+                                  void *workspace, size_t workspace_bytes, void *hip_stream) {
+    // everything the decode checks, checked here too: nothing is enqueued
+    // unless the whole call is valid
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !seqlens || !o || !cos_table ||
+        !sin_table)
+        return GQA_ERR_NULL_POINTER;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(o) || !aligned16(cos_table) || !aligned16(sin_table) ||
+        (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
+        return GQA_ERR_ALIGNMENT;
+    if (B <= 0 || h_q <= 0 || h_kv <= 0 || S <= 0) return GQA_ERR_SIZE;
+    if (h_q % h_kv != 0) return GQA_ERR_HEADS;
+    if (d != 64 && d != 128) return GQA_ERR_HEAD_DIM;
+    if (dt != GQA_BF16) return GQA_ERR_DTYPE;
+    if (!splits_valid(num_splits)) return GQA_ERR_SIZE;
+    if ((int64_t)B * h_q > 0x7fffffff / 4) return GQA_ERR_SIZE;
+    const size_t base = gqa_decode_workspace_bytes(B, h_q, h_kv, d, num_splits);
+    const size_t need = gqa_decode_rope_workspace_bytes(B, h_q, h_kv, d, num_splits);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+    gqa_status st = check_device();
+    if (st != GQA_OK) return st;
+
+    // the rotated q and k_new rows go to the workspace after the decode's part
+    char *q_rot = static_cast<char *>(workspace) + base;
+    char *k_rot = q_rot + round_up_256((size_t)B * h_q * d * 2);
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    gqa::RopeArgs r;
+    r.cos = cos_table;
+    r.sin = sin_table;
+    r.L = S;
+    r.pos = seqlens;
+    r.x = q;
+    r.out = q_rot;
+    r.rows = (long long)B * h_q;
+    r.h = h_q;
+    if (gqa::launch_rope_k_bf16(r, d, stream) != 0) return GQA_ERR_LAUNCH;
+    r.x = k_new;
+    r.out = k_rot;
+    r.rows = (long long)B * h_kv;
+    r.h = h_kv;
+    if (gqa::launch_rope_k_bf16(r, d, stream) != 0) return GQA_ERR_LAUNCH;
+    return decode_impl(q_rot, k_rot, v_new, k_cache, v_cache, seqlens, o, B, h_q, h_kv, S, d, dt,
+                       num_splits, workspace, base, hip_stream);
 }
 
 gqa_status gqa_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache,

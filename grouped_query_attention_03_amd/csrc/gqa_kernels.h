@@ -27,14 +27,17 @@ struct PrefillArgs {
     const int32_t *kv_lens;
 };
 
-// Rotary embedding of key rows x [rows][d] (rows in [B][L][h][...] order) into
-// out, tables cos, sin [L][d/2].
+// Rotary embedding of rows x [rows][d] into out, tables cos, sin [L][d/2].
+// Without pos the rows are in [B][L][h] order and row r sits at position
+// (r / h) % L; with pos ([B], one new token per sequence) the rows are in
+// [B][h] order and row r sits at position pos[r / h], clamped to [0, L - 1].
 struct RopeArgs {
     const void *x;
     void *out;
     const float *cos, *sin;
-    long long rows;  // B * L * h
+    long long rows;  // B * L * h, or B * h with pos
     int L, h;
+    const int32_t *pos;
 };
 
 // Waves per work-group of the decode split pass; with one work-group per CU

@@ -10,6 +10,9 @@
 // are rotated once here, not once per query tile, and the rotated rows are
 // what a cache stores; the prefill kernel then reads them like plain keys.
 //
+// In a decode step the rows are the new token's q or k rows, one position per
+// sequence (its length before the append).
+//
 // One thread per (row, 4 pairs): one 16-byte load of the row, 16-byte loads
 // of the 4 cosines and 4 sines, two 8-byte stores (one into each half).
 #include "gqa_device.h"
@@ -26,7 +29,7 @@ __global__ __launch_bounds__(256) void rope_k_kernel(RopeArgs a) {
          t += (long long)gridDim.x * blockDim.x) {
         const long long row = t / QUADS;  // (b, p, g) in [B][L][h_kv] order
         const int quad = (int)(t % QUADS);
-        const int p = (int)((row / a.h) % a.L);
+        const int p = a.pos ? min(max(a.pos[row / a.h], 0), a.L - 1) : (int)((row / a.h) % a.L);
         const __bf16 *xr = static_cast<const __bf16 *>(a.x) + row * D;
         __bf16 *orow = static_cast<__bf16 *>(a.out) + row * D;
         const int i0 = 4 * quad;  // first pair

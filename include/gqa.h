@@ -229,6 +229,32 @@ gqa_status gqa_decode_append(const void *q, const void *k_new, const void *v_new
                              int h_kv, int S, int d, gqa_dtype dt, int num_splits,
                              void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/*
+ * Decode step with rotary position embedding: the new token of sequence b sits
+ * at position seqlens[b]; its query and key rows are rotated with row
+ * seqlens[b] of the tables (the rotation of gqa_prefill_rope, "Attention in
+ * Qwen, DeepSeek and LLaMA3", §1), the rotated key and v_new are appended at
+ * cache row seqlens[b], and the token attends over rows [0, seqlens[b] + 1)
+ * ("What is Grouped-Query Attention", §3.2).  The cache therefore holds rotated
+ * keys, as gqa_prefill_rope's k_rot does.
+ *   q, k_new, v_new, k_cache, v_cache, seqlens, o, sizes: as gqa_decode_append.
+ *   cos_table, sin_table : [S, d/2] fp32 device arrays, 16-byte aligned; a
+ *          position outside [0, S - 1] (a broken precondition) is clamped.
+ *   workspace : at least gqa_decode_rope_workspace_bytes(...) bytes (the
+ *          decode's part, then the rotated q and k_new rows).
+ * Everything is validated before anything is enqueued; errors as
+ * gqa_decode_append.  Four kernels run on `hip_stream`: the rotation of q, of
+ * k_new, then the split and merge passes.
+ */
+gqa_status gqa_decode_append_rope(const void *q, const void *k_new, const void *v_new,
+                                  void *k_cache, void *v_cache, const int32_t *seqlens,
+                                  const float *cos_table, const float *sin_table, void *o, int B,
+                                  int h_q, int h_kv, int S, int d, gqa_dtype dt, int num_splits,
+                                  void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Bytes of workspace gqa_decode_append_rope needs (0 when an argument is invalid). */
+size_t gqa_decode_rope_workspace_bytes(int B, int h_q, int h_kv, int d, int num_splits);
+
 /* Bytes of decode workspace needed for these sizes and num_splits (0 =
  * default); returns 0 when an argument is invalid. */
 size_t gqa_decode_workspace_bytes(int B, int h_q, int h_kv, int d, int num_splits);

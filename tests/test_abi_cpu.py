@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("gqa_prefill", "gqa_prefill_chunk", "gqa_decode", "gqa_decode_append",
               "gqa_decode_token_major", "gqa_decode_paged", "gqa_prefill_rope",
-              "gqa_prefill_varlen",
+              "gqa_prefill_varlen", "gqa_decode_append_rope", "gqa_decode_rope_workspace_bytes",
               "gqa_decode_workspace_bytes",
               "gqa_decode_default_splits", "gqa_status_string"):
         assert n in names
@@ -126,6 +126,42 @@ def test_prefill_varlen_without_a_gpu_reports_the_device():
         pytest.skip("a GPU is present")
     assert varlen_status(kl=A + 4) == DEVICE
     assert varlen_status(dt=0) == DEVICE  # fp32 is served too
+
+
+def append_rope_status(q=A, kn=A, vn=A, kc=A, vc=A, sl=A, c=A, s=A, o=A, B=4, h_q=32, h_kv=8,
+                       S=1024, d=128, dt=1, splits=0, ws=A, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = (gqa.decode_rope_workspace_bytes(B, h_q, h_kv, d, splits)
+                    if d in (64, 128) and h_q % h_kv == 0 else 1 << 30)
+    return gqa.lib().gqa_decode_append_rope(q, kn, vn, kc, vc, sl, c, s, o, B, h_q, h_kv, S, d,
+                                            dt, splits, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(c=None), NULLP), (dict(s=None), NULLP), (dict(kn=None), NULLP), (dict(vc=None), NULLP),
+    (dict(c=A + 8), ALIGN), (dict(kn=MIS), ALIGN), (dict(sl=A + 1), ALIGN),
+    (dict(S=0), SIZE), (dict(h_q=32, h_kv=5), HEADS), (dict(d=80), HEADDIM), (dict(dt=0), DTYPE),
+    (dict(splits=-2), SIZE), (dict(ws=None), WORKSPACE),
+    # the decode's own workspace is not enough: the rotated rows need room too
+    (dict(ws_bytes=gqa.decode_workspace_bytes(4, 32, 8, 128, 0)), WORKSPACE),
+])
+def test_decode_append_rope_rejects_bad_arguments(kw, status):
+    assert append_rope_status(**kw) == status
+
+
+def test_decode_append_rope_without_a_gpu_reports_the_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert append_rope_status(sl=A + 4) == DEVICE
+
+
+def test_rope_workspace_is_the_decode_workspace_plus_the_rotated_rows():
+    B, h_q, h_kv, d = 5, 32, 8, 128
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert gqa.decode_rope_workspace_bytes(B, h_q, h_kv, d, 7) == (
+        gqa.decode_workspace_bytes(B, h_q, h_kv, d, 7) + up(B * h_q * d * 2) + up(B * h_kv * d * 2))
+    assert gqa.decode_rope_workspace_bytes(B, h_q, h_kv, 96, 0) == 0
 
 
 def rope_status(q=A, k=A, v=A, c=A, s=A, o=A, kr=A + 0x100, B=1, L=16, h_q=8, h_kv=2, d=64,

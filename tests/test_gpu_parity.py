@@ -812,3 +812,67 @@ def test_decode_wide_group(h_q, h_kv, d, dev):
         out = run_decode(seqlens, q, kc, vc, dev, splits=splits).cpu()
         check(f64(out[:, 0]), decode_ref(seqlens, q, kc, vc), "bf16",
               f"decode G=64 h_q={h_q} splits={splits}")
+
+
+# ------------------------------------------------ decode step with rotary embedding
+
+APPEND_ROPE = [
+    # B, h_q, h_kv, S, d, lengths before the append
+    (5, 32, 8, 700, 128, [0, 1, 63, 64, 699]),
+    (3, 8, 8, 300, 64, [299, 31, 100]),       # G = 1
+    (2, 32, 1, 200, 128, [150, 7]),           # G = 32
+]
+
+
+@pytest.mark.parametrize("case", APPEND_ROPE, ids=lambda c: "B{}_hq{}_hkv{}_S{}_d{}".format(*c[:5]))
+def test_decode_append_rope_matches_oracle(case, dev):
+    B, h_q, h_kv, S, d, lens = case
+    seed = 8000 + S + h_q
+    _, q, kn, vn, kc, vc = wl.decode_append_inputs(B, h_q, h_kv, S, d, seed, (0, S - 1))
+    seqlens = torch.tensor(lens, dtype=torch.int32)
+    for b, n in enumerate(lens):
+        kc[b, :, n:] = float("nan")
+        vc[b, :, n:] = float("nan")
+    cos, sin = wl.rope_tables(S, d)
+    say(f"decode_append_rope {case} seed {seed}")
+    o_ref, kc_ref, vc_ref = oracle.decode_append_rope(f64(q[:, 0]), f64(kn[:, 0]), f64(vn[:, 0]),
+                                                      f64(kc), f64(vc), seqlens.numpy(), f64(cos),
+                                                      f64(sin))
+    for splits in (0, 9):
+        kcd, vcd = kc.to(dev), vc.to(dev)
+        out = gqa.decode_append_rope(q.to(dev), kn.to(dev), vn.to(dev), kcd, vcd, seqlens.to(dev),
+                                     cos.to(dev), sin.to(dev), num_splits=splits)
+        torch.cuda.synchronize()
+        check(f64(out.cpu()[:, 0]), o_ref, "bf16", f"decode_append_rope {case} splits {splits}")
+        # the appended keys are within one bf16 rounding of the fp64 rotation;
+        # every other element of the caches is exactly the oracle's
+        kg, vg = kcd.cpu(), vcd.cpu()
+        k_expect = kc_ref.copy()
+        for b, n in enumerate(lens):
+            check_rotated_keys(kg[b, :, n], kc_ref[b, :, n], f"appended key of seq {b}")
+            k_expect[b, :, n] = f64(kg[b, :, n])
+        check_cache_exact(kg, k_expect, "k_cache after the rotary append")
+        check_cache_exact(vg, vc_ref, "v_cache after the rotary append")
+
+
+def test_decode_append_rope_continues_rotary_prefill(dev):
+    # the rotary prefill of n positions leaves its rotated keys in the cache;
+    # the decode step of token n then matches the rotary prefill of n + 1
+    # positions at row n, and appends exactly that prefill's rotated key n
+    B, n, h_q, h_kv, d, S = 2, 300, 32, 8, 128, 512
+    q, k, v = wl.prefill_inputs(B, n + 1, h_q, h_kv, d, 91, 1.0 / math.sqrt(2.0), torch.bfloat16)
+    cos, sin = wl.rope_tables(S, d)
+    say("rotary decode step vs rotary prefill")
+    full, k_rot = gqa.prefill_rope(q.to(dev), k.to(dev), v.to(dev), cos[:n + 1].contiguous().to(dev),
+                                   sin[:n + 1].contiguous().to(dev), causal=True)
+    kc = torch.zeros(B, h_kv, S, d, dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    kc[:, :, :n] = k_rot[:, :n].transpose(1, 2)
+    vc[:, :, :n] = v[:, :n].to(dev).transpose(1, 2)
+    seqlens = torch.full((B,), n, dtype=torch.int32, device=dev)
+    out = gqa.decode_append_rope(q[:, n:n + 1].contiguous().to(dev), k[:, n:n + 1].contiguous().to(dev),
+                                 v[:, n:n + 1].contiguous().to(dev), kc, vc, seqlens, cos.to(dev),
+                                 sin.to(dev))
+    torch.cuda.synchronize()
+    check(f64(out.cpu()), f64(full[:, n:n + 1].cpu()), "bf16", "decode step vs prefill row n")
+    assert torch.equal(kc[:, :, n].cpu(), k_rot[:, n].cpu())
