@@ -139,6 +139,10 @@ gqa_status prefill_impl(const void *q, const void *k, const void *v, void *o, in
         r.L = Lk;
         r.h = h_kv;
         r.pos = nullptr;
+        r.x2 = nullptr;
+        r.out2 = nullptr;
+        r.rows2 = 0;
+        r.h2 = 1;
         if (gqa::launch_rope_k_bf16(r, d, stream) != 0) return GQA_ERR_LAUNCH;
         a.k = k_rot;
     }
@@ -331,15 +335,14 @@ gqa_status gqa_decode_append_rope(const void *q, const void *k_new, const void *
     r.sin = sin_table;
     r.L = S;
     r.pos = seqlens;
-    r.x = q;
+    r.x = q;  // q rows, then k_new rows, in one launch
     r.out = q_rot;
     r.rows = (long long)B * h_q;
     r.h = h_q;
-    if (gqa::launch_rope_k_bf16(r, d, stream) != 0) return GQA_ERR_LAUNCH;
-    r.x = k_new;
-    r.out = k_rot;
-    r.rows = (long long)B * h_kv;
-    r.h = h_kv;
+    r.x2 = k_new;
+    r.out2 = k_rot;
+    r.rows2 = (long long)B * h_kv;
+    r.h2 = h_kv;
     if (gqa::launch_rope_k_bf16(r, d, stream) != 0) return GQA_ERR_LAUNCH;
     return decode_impl(q_rot, k_rot, v_new, k_cache, v_cache, seqlens, o, B, h_q, h_kv, S, d, dt,
                        num_splits, workspace, base, hip_stream);

@@ -38,6 +38,12 @@ struct RopeArgs {
     long long rows;  // B * L * h, or B * h with pos
     int L, h;
     const int32_t *pos;
+    // optional second segment of rows, rotated in the same launch (the new
+    // token's k rows after its q rows): x2 -> out2, rows2 rows of h2 heads
+    const void *x2;
+    void *out2;
+    long long rows2;
+    int h2;
 };
 
 // Waves per work-group of the decode split pass; with one work-group per CU

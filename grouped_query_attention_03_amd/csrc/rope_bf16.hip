@@ -24,14 +24,17 @@ namespace {
 template <int D>
 __global__ __launch_bounds__(256) void rope_k_kernel(RopeArgs a) {
     constexpr int QUADS = D / 8;  // 4-pair pieces per row
-    const long long n = (long long)a.rows * QUADS;
+    const long long n1 = (long long)a.rows * QUADS;
+    const long long n = n1 + (long long)a.rows2 * QUADS;
     for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < n;
          t += (long long)gridDim.x * blockDim.x) {
-        const long long row = t / QUADS;  // (b, p, g) in [B][L][h_kv] order
+        const bool second = t >= n1;
+        const long long row = (second ? t - n1 : t) / QUADS;  // [B][L][h] or [B][h] order
         const int quad = (int)(t % QUADS);
-        const int p = a.pos ? min(max(a.pos[row / a.h], 0), a.L - 1) : (int)((row / a.h) % a.L);
-        const __bf16 *xr = static_cast<const __bf16 *>(a.x) + row * D;
-        __bf16 *orow = static_cast<__bf16 *>(a.out) + row * D;
+        const int h = second ? a.h2 : a.h;
+        const int p = a.pos ? min(max(a.pos[row / h], 0), a.L - 1) : (int)((row / h) % a.L);
+        const __bf16 *xr = static_cast<const __bf16 *>(second ? a.x2 : a.x) + row * D;
+        __bf16 *orow = static_cast<__bf16 *>(second ? a.out2 : a.out) + row * D;
         const int i0 = 4 * quad;  // first pair
         const bf16x8 x = __builtin_bit_cast(bf16x8, load16(xr + 2 * i0));
         const float4 c = *reinterpret_cast<const float4 *>(a.cos + (size_t)p * (D / 2) + i0);
@@ -52,7 +55,7 @@ __global__ __launch_bounds__(256) void rope_k_kernel(RopeArgs a) {
 }  // namespace
 
 int launch_rope_k_bf16(const RopeArgs &a, int d, hipStream_t stream) {
-    const long long n = (long long)a.rows * (d / 8);
+    const long long n = ((long long)a.rows + a.rows2) * (d / 8);
     const int blocks = (int)(n / 256 + 1 < 256 * 16 ? n / 256 + 1 : 256 * 16);
     if (d == 128) hipLaunchKernelGGL(rope_k_kernel<128>, dim3(blocks), dim3(256), 0, stream, a);
     else hipLaunchKernelGGL(rope_k_kernel<64>, dim3(blocks), dim3(256), 0, stream, a);

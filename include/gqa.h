@@ -243,8 +243,8 @@ gqa_status gqa_decode_append(const void *q, const void *k_new, const void *v_new
  *   workspace : at least gqa_decode_rope_workspace_bytes(...) bytes (the
  *          decode's part, then the rotated q and k_new rows).
  * Everything is validated before anything is enqueued; errors as
- * gqa_decode_append.  Four kernels run on `hip_stream`: the rotation of q, of
- * k_new, then the split and merge passes.
+ * gqa_decode_append.  Three kernels run on `hip_stream`: the rotation of the
+ * new token's q and k rows (one launch), then the split and merge passes.
  */
 gqa_status gqa_decode_append_rope(const void *q, const void *k_new, const void *v_new,
                                   void *k_cache, void *v_cache, const int32_t *seqlens,
