@@ -876,3 +876,42 @@ def test_decode_append_rope_continues_rotary_prefill(dev):
     torch.cuda.synchronize()
     check(f64(out.cpu()), f64(full[:, n:n + 1].cpu()), "bf16", "decode step vs prefill row n")
     assert torch.equal(kc[:, :, n].cpu(), k_rot[:, n].cpu())
+
+
+# --------------------------------------------------------------- graph capture
+
+def test_graph_capture_replays_match_eager(dev):
+    # the entry points allocate nothing and never synchronise, so a prefill and
+    # a paged decode captured in one HIP graph replay with the eager results,
+    # replay after replay, with eager work on the outputs in between
+    B, L, h_q, h_kv, d = 2, 256, 16, 4, 128
+    q, k, v = (t.to(dev) for t in wl.prefill_inputs(B, L, h_q, h_kv, d, 95, 1.0, torch.bfloat16))
+    seqlens, dq, kc, vc = wl.decode_inputs(4, 32, 8, 1024, 128, 96, (1, 1024))
+    kp, vp, table = wl.to_pages(kc, vc, seqlens, 64, 97)
+    seqlens, dq, kp, vp, table = (t.to(dev) for t in (seqlens, dq, kp, vp, table))
+    po, do = torch.empty_like(q), torch.empty_like(dq)
+    ws = torch.empty(gqa.decode_workspace_bytes(4, 32, 8, 128), dtype=torch.uint8, device=dev)
+
+    def step():
+        gqa.prefill(q, k, v, causal=True, out=po)
+        gqa.decode_paged(dq, kp, vp, table, seqlens, out=do, workspace=ws)
+
+    say("graph capture of prefill + paged decode")
+    step()
+    torch.cuda.synchronize()
+    ref_p, ref_d = po.clone(), do.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(4):
+        po.zero_()
+        do.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(po, ref_p) and torch.equal(do, ref_d)
