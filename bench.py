@@ -13,7 +13,9 @@ steps the same step runs untimed for --settle-seconds (default 0.5 s) so the GPU
 reaches its working clocks; then K steps are timed back to back between two
 device synchronisations; ``value`` is the
 algorithmic TFLOP/s of that timed region (4 * B * h_q * d * visible (query,
-key) pairs per step; causal counts L(L+1)/2 pairs per head).
+key) pairs per step; causal counts L(L+1)/2 pairs per head).  K more steps
+follow, each between two HIP events on the launch stream, for the kernel's
+average duration in ``roofline``.
 
 The decode entry point is timed next on its own workload (64 sequences, 32
 query heads over 8 key/value heads, d=128, S=8192, lengths U{1024..8192}).  A
@@ -209,7 +211,17 @@ def bench_prefill(w, steps, warmup, settle_s=0.0):
     settle_clocks(step, settle_s)
     for _ in range(warmup):
         step()
-    wall, ev = time_launches(step, steps)
+    # the K timed steps run back to back between two synchronisations; then K
+    # more steps are timed one by one with events on the launch stream for
+    # the kernel's own average (an event pair between launches leaves a small
+    # gap on the GPU, so it is kept out of the throughput's timed region)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    _, ev = time_launches(step, steps)
     flops = prefill_flops(w, None if kv_lens is None else kv_lens.tolist())
     avg_ms = sum(ev) / len(ev)
     return {
