@@ -295,15 +295,21 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
                     s[kb][r] = masked ? -INFINITY : s[kb][r];
                 }
         }
-        float m8[8];  // pairwise tree: short dependency chains
+        // a tree of three-input maxima (v_max3_f32): 32 values in 16 instructions
+        float x[32];
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            m8[r] = fmaxf(fmaxf(s[0][2 * r], s[0][2 * r + 1]), fmaxf(s[1][2 * r], s[1][2 * r + 1]));
+        for (int r = 0; r < 16; ++r) {
+            x[r] = s[0][r];
+            x[16 + r] = s[1][r];
+        }
+        float t[11];
 #pragma unroll
-        for (int w = 4; w >= 1; w >>= 1)
-#pragma unroll
-            for (int r = 0; r < w; ++r) m8[r] = fmaxf(m8[r], m8[r + w]);
-        const float mx = fmaxf(m8[0], other_half(m8[0]));  // tile row max, relative to mu
+        for (int i = 0; i < 10; ++i) t[i] = fmaxf(fmaxf(x[3 * i], x[3 * i + 1]), x[3 * i + 2]);
+        t[10] = fmaxf(x[30], x[31]);
+        const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]), u1 = fmaxf(fmaxf(t[3], t[4]), t[5]);
+        const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]), u3 = fmaxf(t[9], t[10]);
+        const float m0 = fmaxf(fmaxf(u0, u1), fmaxf(u2, u3));
+        const float mx = fmaxf(m0, other_half(m0));  // tile row max, relative to mu
         if (__any(m_run == -INFINITY || mx > PF_TAU)) {
             const float m2 = m_run == -INFINITY ? mu + mx : fmaxf(m_run, mu + mx);
             const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m2);
