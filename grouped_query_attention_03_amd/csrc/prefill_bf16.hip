@@ -100,7 +100,8 @@ __device__ __forceinline__ void block_barrier() {
 // ROPE: q is rotated as it is loaded (the keys arrive rotated already).
 // VARLEN: sequence b has a.kv_lens[b] visible keys (a padded batch).
 template <int D, bool CAUSAL, bool ROPE, bool VARLEN>
-__global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(PF_THREADS, D == 64 ? 4 : 2)  // waves per SIMD
+void prefill_bf16_kernel(PrefillArgs a) {
     using Lay = PfLay<D>;
     constexpr int KSTEPS = Lay::KSTEPS, DB = Lay::DB, DPW = Lay::DMA_PER_WAVE;
     __shared__ __attribute__((aligned(1024))) char smem[PF_SLOTS * Lay::SLOT_BYTES];
@@ -109,7 +110,11 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
     // Lane id used for LDS/global address arithmetic inside the tile loop.  It
     // is passed through an empty asm at every iteration so the compiler
     // recomputes the (cheap) swizzled offsets instead of hoisting them out of
-    // the loop and spilling them.
+    // the loop and spilling them there.  The plain non-causal d = 64 kernel
+    // hoists them instead (a fifth fewer vector instructions per tile); its few
+    // spills then fall outside the loop, and the launch bound keeps four waves
+    // per SIMD.
+    constexpr bool PIN_LANE = D == 128 || CAUSAL || ROPE || VARLEN;
     int ln = lane;
     const int lid = xcd_contiguous_id(blockIdx.x, gridDim.x);
     const int unit = lid / a.n_qtiles;
@@ -363,7 +368,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void prefill_bf16_kernel(PrefillArgs
     block_barrier();
     for (int j = 0; j < ntiles; ++j) {
         ln = lane;
-        asm volatile("" : "+v"(ln));
+        if (PIN_LANE) asm volatile("" : "+v"(ln));
         if (j + PF_DIST < ntiles) issue_tile(j + PF_DIST);
         if (active(j)) {
             qk(j);
