@@ -126,6 +126,31 @@ def test_prefill_is_deterministic(dev):
     assert torch.equal(o1, o2)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_prefill_running_max_jumps(d, causal, dev):
+    """Keys that grow along the sequence, plus one spike key, so a row's max
+    rises by more than the lazy-rescale threshold in later tiles, and for most
+    rows once by far more than the fp32 exponent range (2^128): the rescale
+    and the recomputed-tile paths of the online softmax must agree with the
+    plain row softmax.
+
+    The kernel folds scale*log2(e) into q before rounding it to bf16, which
+    perturbs scores of this size (hundreds of log2 units) by more than the
+    tolerance allows.  scale = ln(2)/8 makes that factor 1/8, a power of two,
+    so the folded q is exact and the test measures the softmax alone."""
+    B, L, h_q, h_kv = 1, 700, 8, 2
+    q, k, v = wl.prefill_inputs(B, L, h_q, h_kv, d, 35 + d, 1 / math.sqrt(2), torch.bfloat16)
+    grow = 1.0 + torch.arange(L, dtype=torch.float32) / 40.0
+    grow[517] *= 60.0
+    k = (k.float() * grow[None, :, None, None]).to(torch.bfloat16)
+    scale = math.log(2) / 8
+    say(f"prefill rising keys d{d} causal={causal}")
+    out = run_prefill(q, k, v, causal, scale, dev)
+    ref = oracle.prefill(f64(q), f64(k), f64(v), causal=causal, scale=scale)
+    check(f64(out), ref, "bf16", f"prefill rising keys d{d}")
+
+
 def test_prefill_head_map_discriminates(dev):
     """Key/value head 0 has all-zero keys, so heads 0..G-1 must return running means of V0."""
     B, L, h_q, h_kv, d = 1, 96, 8, 2, 64
