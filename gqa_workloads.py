@@ -109,6 +109,11 @@ WORKLOADS = {
         causal=True, std=1.0 / math.sqrt(2.0), seqlen_range=(128, 2048), seed=8,
         description="bf16 causal prefill of a padded batch, B=16 L=2048 lengths U{128..2048} "
                     "h_q=32 h_kv=8 d=128"),
+    "long_context_group_prefill_bf16": Workload(
+        "long_context_group_prefill_bf16", "prefill", "bf16", B=1, L=32768, h_q=8, h_kv=1, d=128,
+        causal=True, std=1.0 / math.sqrt(2.0), seed=9,
+        description="bf16 causal prefill of one key/value group of the long-context shape "
+                    "(an eighth of its heads), B=1 L=32768 h_q=8 h_kv=1 d=128"),
     "batched_decode_paged_bf16": Workload(
         "batched_decode_paged_bf16", "decode_paged", "bf16", B=64, h_q=32, h_kv=8, d=128,
         S=8192, std=1.0, seqlen_range=(1024, 8192), seed=4, page_size=64,
@@ -122,7 +127,8 @@ WORKLOADS = {
 WORKLOAD_ORDER = ["tiny_prefill_f32", "worked_example_prefill_bf16", "llama2_7b_prefill_bf16",
                   "batched_decode_bf16", "long_context_prefill_bf16", "chunked_prefill_bf16",
                   "batched_decode_append_bf16", "batched_decode_paged_bf16",
-                  "llama2_7b_prefill_rope_bf16", "varlen_prefill_bf16"]
+                  "llama2_7b_prefill_rope_bf16", "varlen_prefill_bf16",
+                  "long_context_group_prefill_bf16"]
 
 
 def _draw(gen, shape, std, dtype):

@@ -116,9 +116,22 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // per SIMD.
     constexpr bool PIN_LANE = D == 128 || CAUSAL || ROPE || VARLEN;
     int ln = lane;
-    const int lid = xcd_contiguous_id(blockIdx.x, gridDim.x);
-    const int unit = lid / a.n_qtiles;
-    int qt = lid % a.n_qtiles;
+    // Work-group -> (unit, query tile).  Dispatch sends work-group i to XCD
+    // i % 8.  Equal-cost tiles are mapped XCD-contiguously, so the tiles of one
+    // key/value head run on one XCD and share its L2.  Causal and
+    // variable-length tiles differ in cost, so they are dealt round-robin over
+    // the units instead, longest first: with a multiple of 8 units each unit
+    // still stays on one XCD, and otherwise (one head, say) every XCD still gets
+    // an equal mix of long and short tiles.
+    int unit, qt;
+    if (CAUSAL || VARLEN) {
+        unit = blockIdx.x % a.n_units;
+        qt = blockIdx.x / a.n_units;
+    } else {
+        const int lid = xcd_contiguous_id(blockIdx.x, gridDim.x);
+        unit = lid / a.n_qtiles;
+        qt = lid % a.n_qtiles;
+    }
     if (CAUSAL) qt = a.n_qtiles - 1 - qt;  // longest rows first
     const int sub = unit % a.nsub;
     const int bk = unit / a.nsub;

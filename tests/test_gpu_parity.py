@@ -205,6 +205,12 @@ def test_workload_long_context_prefill(dev):
     _sampled_prefill("long_context_prefill_bf16", 96, dev)
 
 
+def test_workload_long_context_group_prefill(dev):
+    """One key/value group of the long-context shape: the share of one device
+    when the heads are split by group (G = 8, a single key/value head)."""
+    _sampled_prefill("long_context_group_prefill_bf16", 128, dev)
+
+
 # ------------------------------------------------ prefill against existing keys
 
 def run_prefill_chunk(q, k, v, causal, scale, dev):
