@@ -107,15 +107,6 @@ void prefill_bf16_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[PF_SLOTS * Lay::SLOT_BYTES];
 
     const int lane = threadIdx.x & 63, wave = wave_id();
-    // Lane id used for LDS/global address arithmetic inside the tile loop.  It
-    // is passed through an empty asm at every iteration so the compiler
-    // recomputes the (cheap) swizzled offsets instead of hoisting them out of
-    // the loop and spilling them there.  The plain non-causal d = 64 kernel
-    // hoists them instead (a fifth fewer vector instructions per tile); its few
-    // spills then fall outside the loop, and the launch bound keeps four waves
-    // per SIMD.
-    constexpr bool PIN_LANE = D == 128 || CAUSAL || ROPE || VARLEN;
-    int ln = lane;
     // Work-group -> (unit, query tile).  Dispatch sends work-group i to XCD
     // i % 8.  Equal-cost tiles are mapped XCD-contiguously, so the tiles of one
     // key/value head run on one XCD and share its L2.  Causal and
@@ -133,10 +124,15 @@ void prefill_bf16_kernel(PrefillArgs a) {
         qt = lid % a.n_qtiles;
     }
     if (CAUSAL) qt = a.n_qtiles - 1 - qt;  // longest rows first
-    const int sub = unit % a.nsub;
-    const int bk = unit / a.nsub;
-    const int kvh = bk % a.h_kv;
-    const int b = bk / a.h_kv;
+    // The integer divisions above and below run partly on the vector ALU; their
+    // wave-uniform results are moved to scalar registers, so they do not hold
+    // vector registers for the whole kernel.
+    unit = __builtin_amdgcn_readfirstlane(unit);
+    qt = __builtin_amdgcn_readfirstlane(qt);
+    const int sub = __builtin_amdgcn_readfirstlane(unit % a.nsub);
+    const int bk = __builtin_amdgcn_readfirstlane(unit / a.nsub);
+    const int kvh = __builtin_amdgcn_readfirstlane(bk % a.h_kv);
+    const int b = __builtin_amdgcn_readfirstlane(bk / a.h_kv);
     const int L = a.L, off = a.off;  // query rows, position of row 0
     const int Lt = a.Lk;             // key rows per sequence in the tensors
     // visible keys of this sequence: all, or its length (clamped to [0, Lt])
@@ -254,12 +250,12 @@ void prefill_bf16_kernel(PrefillArgs a) {
     static_assert(NSTEP == 4 * DB, "QK and PV have the same number of MFMA steps");
     auto kread = [&](const char *kt, int st) {
         const int ks = st >> 1, kb = st & 1;
-        const int r = 32 * kb + (ln & 31);
-        const int ch = (2 * ks + (ln >> 5)) ^ pf_kswz<D>(r);
+        const int r = 32 * kb + (lane & 31);
+        const int ch = (2 * ks + (lane >> 5)) ^ pf_kswz<D>(r);
         return *reinterpret_cast<const bf16x8 *>(kt + r * Lay::ROW_BYTES + 16 * ch);
     };
     auto vread = [&](const char *vt, int st) {
-        const int grp = ln >> 4, jl = ln & 15;
+        const int grp = lane >> 4, jl = lane & 15;
         const int vrq = 4 * (grp >> 1) + (jl >> 2);      // V row within a 16-key step (+8 for hi)
         const int vcq = 2 * (grp & 1) + ((jl & 3) >> 1);  // 16-byte chunk within a 32-wide d block
         const int vsw = pf_vswz<D>(vrq);                  // same for vrq + 8 and every step
@@ -380,8 +376,6 @@ void prefill_bf16_kernel(PrefillArgs a) {
     else wait_vmcnt<0>();
     block_barrier();
     for (int j = 0; j < ntiles; ++j) {
-        ln = lane;
-        if (PIN_LANE) asm volatile("" : "+v"(ln));
         if (j + PF_DIST < ntiles) issue_tile(j + PF_DIST);
         if (active(j)) {
             qk(j);
@@ -402,12 +396,16 @@ void prefill_bf16_kernel(PrefillArgs a) {
 
     // ---- epilogue: O / l, round to bf16, store
     const float lt = l_run + other_half(l_run);
-    const int pos = pos0 + (lane & 31);
+    // the row address is recomputed here (the lane id passes an empty asm), not
+    // shared with the Q load's and kept in registers across the tile loop
+    int le = lane;
+    asm volatile("" : "+v"(le));
+    const int pos = pos0 + (le & 31);
     if (pos < L) {
         // no visible key (only a zero-length sequence): a zero row
         const float inv = (!VARLEN || lt > 0.f) ? 1.f / lt : 0.f;
         __bf16 *op = static_cast<__bf16 *>(a.o) + (((size_t)b * L + pos) * a.h_q + head) * D +
-                     4 * (lane >> 5);
+                     4 * (le >> 5);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
