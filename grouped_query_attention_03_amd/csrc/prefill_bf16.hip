@@ -394,18 +394,24 @@ void prefill_bf16_kernel(PrefillArgs a) {
         block_barrier();
     }
 
-    // ---- epilogue: O / l, round to bf16, store
+    // ---- epilogue: O / l, round to bf16, store.  The ring is free after the
+    // last barrier; each wave stages its 32 rows in its own part of it and
+    // writes them back as whole rows (16-byte lanes, consecutive within a
+    // row), not as the accumulators' scattered 8-byte pieces of 32 rows.
     const float lt = l_run + other_half(l_run);
-    // the row address is recomputed here (the lane id passes an empty asm), not
-    // shared with the Q load's and kept in registers across the tile loop
+    // no visible key (only a zero-length sequence): a zero row
+    const float inv = (!VARLEN || lt > 0.f) ? 1.f / lt : 0.f;
+    // the lane id passes an empty asm, so the addresses below are computed
+    // here and not kept in registers across the tile loop
     int le = lane;
     asm volatile("" : "+v"(le));
-    const int pos = pos0 + (le & 31);
-    if (pos < L) {
-        // no visible key (only a zero-length sequence): a zero row
-        const float inv = (!VARLEN || lt > 0.f) ? 1.f / lt : 0.f;
-        __bf16 *op = static_cast<__bf16 *>(a.o) + (((size_t)b * L + pos) * a.h_q + head) * D +
-                     4 * (le >> 5);
+    char *stage = smem + wave * 32 * Lay::ROW_BYTES;
+    {
+        // row r = lane % 32 holds columns 32 db + 8 rq + 4 h .. + 3 (h = lane / 32):
+        // 8 bytes of 16-byte chunk 4 db + rq, stored at chunk position
+        // (4 db + rq) ^ swz(r), the K tiles' swizzle, so that the rows written
+        // together fall in different banks
+        const int r = le & 31, h = le >> 5;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -413,8 +419,24 @@ void prefill_bf16_kernel(PrefillArgs a) {
                 bf16x4 w;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[db][4 * rq + e] * inv);
-                *reinterpret_cast<bf16x4 *>(op + 32 * db + 8 * rq) = w;
+                const int ch = (4 * db + rq) ^ pf_kswz<D>(r);
+                *reinterpret_cast<bf16x4 *>(stage + r * Lay::ROW_BYTES + 16 * ch + 8 * h) = w;
             }
+    }
+    {
+        // one pass covers 64 / CPR rows, lane = (row in pass) * CPR + chunk
+        constexpr int RPP = 64 / Lay::CPR;
+        const int rr = le / Lay::CPR, ch = le % Lay::CPR;
+#pragma unroll
+        for (int p = 0; p < 32 / RPP; ++p) {
+            const int r = p * RPP + rr;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(
+                stage + r * Lay::ROW_BYTES + 16 * (ch ^ pf_kswz<D>(r)));
+            if (pos0 + r < L)
+                *reinterpret_cast<u32x4 *>(static_cast<__bf16 *>(a.o) +
+                                           (((size_t)b * L + pos0 + r) * a.h_q + head) * D +
+                                           8 * ch) = v;
+        }
     }
 }
 
