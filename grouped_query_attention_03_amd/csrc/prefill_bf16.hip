@@ -47,6 +47,10 @@
 //   bf16-rounded P that the PV product uses.
 //   Causal: tiles wholly above the diagonal are never loaded or computed; the
 //   diagonal and the sequence tail are masked element-wise.
+//   Work-groups map to XCDs so that a key/value head's tiles share one L2, and
+//   causal or variable-length work is dealt round-robin, longest first.
+//   The output rows are staged in the (then free) LDS ring and stored as whole
+//   rows.
 #include "gqa_device.h"
 #include "gqa_kernels.h"
 
