@@ -66,6 +66,11 @@ enum {
  * Limits: B * h_q * L and B * h_kv * L must each fit in 2^31 elements of d;
  * for GQA_BF16 also L * h_kv * d * 2 (the bytes spanned by one sequence's
  * key or value rows) must be below 2^32.  Larger calls return GQA_ERR_SIZE.
+ * Precision (GQA_BF16): scale * log2(e) is folded into q, which is rounded to
+ * bf16 once, and the probabilities are rounded to bf16 before the product
+ * with v; accumulation and the softmax statistics are fp32.  A score s thus
+ * carries a relative error of about 2^-9, which matters only for |s| of many
+ * tens (in log2 units) with near ties; a power-of-two scale * log2(e) is exact.
  */
 gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *o, int B, int L,
                        int h_q, int h_kv, int d, gqa_dtype dt, int causal, float scale,
