@@ -83,6 +83,10 @@ PREFILL_SMALL = [
     (1, 150, 12, 2, 64, "bf16", False),    # G = 6
     (3, 64, 8, 8, 64, "bf16", True),       # exactly one tile
     (1, 513, 32, 8, 128, "bf16", True),
+    (2, 99, 3, 1, 64, "bf16", True),       # G = 3 (odd: one head per work-group), d = 64
+    (1, 161, 10, 2, 128, "bf16", False),   # G = 5, ragged tail, non-causal
+    (3, 65, 8, 2, 64, "bf16", True),       # one full tile plus one key, three sequences
+    (1, 2, 64, 8, 128, "bf16", True),      # L = 2 with G = 8: every wave but one past the end
 ]
 
 
