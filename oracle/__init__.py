@@ -94,6 +94,12 @@ def _load():
     lib.gqa_oracle_prefill_rope.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I,
                                             ctypes.c_double]
     lib.gqa_oracle_prefill_rope.restype = I
+    lib.gqa_oracle_prefill_mask.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, ctypes.c_double,
+                                            P]
+    lib.gqa_oracle_prefill_mask.restype = I
+    lib.gqa_oracle_prefill_mask_rows.argtypes = [P, P, ctypes.c_int64, P, P, P, I, I, I, I, I, I,
+                                                 I, ctypes.c_double, P, P]
+    lib.gqa_oracle_prefill_mask_rows.restype = I
     lib.gqa_oracle_num_threads.argtypes = []
     lib.gqa_oracle_num_threads.restype = I
     _lib = lib
@@ -245,6 +251,55 @@ def prefill_varlen_rows(q_rows, rows_bih, k, v, kv_lens, h_q: int, causal: bool,
                                                 float(scale), _ptr(out))
     if rc != 0:
         raise ValueError("oracle prefill_varlen_rows rejected its arguments (rc=%d)" % rc)
+    return out
+
+
+def _mask_u8(mask, B, Lq, Lk):
+    m = np.asarray(mask)
+    if m.shape != (B, Lq, Lk):
+        raise ValueError("mask must be [B, L_q, L_k]")
+    return np.ascontiguousarray(m != 0, dtype=np.uint8)
+
+
+def prefill_mask(q, k, v, mask, causal: bool, scale: float, return_probs: bool = False):
+    """Prefill with a keep-mask: q [B,L_q,h_q,d], k/v [B,L_k,h_kv,d], mask
+    [B,L_q,L_k] (key j visible to row i iff mask[b,i,j] != 0, and j <= L_k -
+    L_q + i when causal) -> o [B,L_q,h_q,d]; a row with no visible key is zero.
+    With ``return_probs`` also returns [B, h_q, L_q, L_k]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Lq, h_q, d = q.shape
+    Lk, h_kv = k.shape[1], k.shape[2]
+    if k.shape != (B, Lk, h_kv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, L_k, h_kv, d] matching q")
+    m = _mask_u8(mask, B, Lq, Lk)
+    o = np.empty_like(q)
+    probs = np.empty((B, h_q, Lq, Lk)) if return_probs else None
+    rc = _load().gqa_oracle_prefill_mask(_ptr(q), _ptr(k), _ptr(v), _ptr(m), _ptr(o), B, Lq, Lk,
+                                         h_q, h_kv, d, int(bool(causal)), float(scale),
+                                         _ptr(probs) if probs is not None else None)
+    if rc != 0:
+        raise ValueError("oracle prefill_mask rejected its arguments (rc=%d)" % rc)
+    return (o, probs) if return_probs else o
+
+
+def prefill_mask_rows(q_rows, rows_bih, k, v, mask, h_q: int, causal: bool, scale: float):
+    """Selected rows (b, i, h) of the keep-mask prefill; mask [B, L_q, L_k].
+    Returns [n, d]."""
+    q_rows = _f64(q_rows)
+    rows = np.ascontiguousarray(np.asarray(rows_bih, dtype=np.int64).reshape(-1, 3))
+    k, v = _f64(k), _f64(v)
+    B, Lk, h_kv, d = k.shape
+    Lq = np.asarray(mask).shape[1]
+    m = _mask_u8(mask, B, Lq, Lk)
+    n = rows.shape[0]
+    if q_rows.shape != (n, d):
+        raise ValueError("q_rows must be [n, d]")
+    out = np.empty((n, d))
+    rc = _load().gqa_oracle_prefill_mask_rows(_ptr(q_rows), _ptr(rows), n, _ptr(k), _ptr(v),
+                                              _ptr(m), B, Lq, Lk, h_q, h_kv, d,
+                                              int(bool(causal)), float(scale), _ptr(out), None)
+    if rc != 0:
+        raise ValueError("oracle prefill_mask_rows rejected its arguments (rc=%d)" % rc)
     return out
 
 

@@ -112,3 +112,28 @@ def rope(x, cos, sin):
             ob.append(op)
         out.append(ob)
     return out
+
+
+def prefill_mask(q, k, v, mask, causal, scale):
+    """q [B][Lq][h_q][d], k/v [B][Lk][h_kv][d], mask [B][Lq][Lk] -> o [B][Lq][h_q][d].
+
+    Key j is visible to query row i of sequence b iff mask[b][i][j] is nonzero
+    and, when causal, j <= Lk - Lq + i (the pages' masked_fill(mask == 0,
+    -inf) convention, "Implementing GQA from scratch in PyTorch", §3.3); a row
+    with no visible key is zeros."""
+    B, Lq, h_q = len(q), len(q[0]), len(q[0][0])
+    Lk, h_kv = len(k[0]), len(k[0][0])
+    if h_q % h_kv or Lq > Lk:
+        raise ValueError("need h_q a multiple of h_kv and Lq <= Lk")
+    G = h_q // h_kv
+    o = [[[None] * h_q for _ in range(Lq)] for _ in range(B)]
+    for b in range(B):
+        for i in range(Lq):
+            seen = [j for j in range(Lk)
+                    if mask[b][i][j] and (not causal or j <= Lk - Lq + i)]
+            for h in range(h_q):
+                g = h // G
+                out, _ = _softmax_average(q[b][i][h], [k[b][j][g] for j in seen],
+                                          [v[b][j][g] for j in seen], scale)
+                o[b][i][h] = out
+    return o

@@ -65,6 +65,13 @@
  *   is visible iff j < kv_lens[b] (and j <= i when causal).  Every query row
  *   is computed, padded ones included; a row with no visible key is zero.
  *
+ *   A general keep-mask (the same page's optional mask, and the attn_mask
+ *   argument of the GQA module in "Modern LLM architecture (1)", §2.3): key j
+ *   is visible to query row i of sequence b iff mask[b][i][j] != 0 (and
+ *   j <= L_k - L_q + i when causal).  Each row's visible set is listed
+ *   explicitly and the row attends over exactly those keys; an empty set
+ *   gives a zero row.
+ *
  *   Rotary position embedding before the scores ("Attention in Qwen,
  *   DeepSeek and LLaMA3", §1, apply_rotary_pos_emb; the model-family table
  *   of "Modern LLM architecture (1)", §1 lists RoPE for every GQA family).
@@ -336,6 +343,135 @@ int gqa_oracle_prefill_varlen_rows(const double *q_rows, const int64_t *row_bih,
     if (!kv_lens) return ORACLE_ERR_ARG;
     return prefill_rows_general(q_rows, row_bih, n_rows, k, v, B, L, L, h_q, h_kv, d, causal,
                                 scale, out, NULL, kv_lens);
+}
+
+/*
+ * Prefill with a keep-mask, for a list of query rows.
+ *   q_rows  [n_rows][d], row_bih [n_rows][3] (b, i, h), 0 <= i < L_q
+ *   k, v    [B][L_k][h_kv][d]
+ *   mask    [B][L_q][L_k] bytes: key j is visible to row (b, i) iff
+ *           mask[b][i][j] != 0, and also j <= L_k - L_q + i when causal
+ *   out     [n_rows][d]
+ *   probs   NULL, or [n_rows][L_k]: the softmax row (zeros at hidden keys)
+ * The row's head is repeated into a slab, its visible keys and values are
+ * gathered in ascending j, and attend_one_row evaluates the softmax over
+ * exactly that set.  No visible key gives a zero row.
+ */
+int gqa_oracle_prefill_mask_rows(const double *q_rows, const int64_t *row_bih, int64_t n_rows,
+                                 const double *k, const double *v, const uint8_t *mask, int B,
+                                 int Lq, int Lk, int h_q, int h_kv, int d, int causal,
+                                 double scale, double *out, double *probs) {
+    if (!mask || B <= 0 || Lq <= 0 || Lk < Lq || d <= 0 || n_rows < 0) return ORACLE_ERR_ARG;
+    if (check_heads(h_q, h_kv)) return ORACLE_ERR_ARG;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t b = row_bih[3 * r], i = row_bih[3 * r + 1], h = row_bih[3 * r + 2];
+        if (b < 0 || b >= B || i < 0 || i >= Lq || h < 0 || h >= h_q) return ORACLE_ERR_ARG;
+    }
+    const long sh = d, sj = (long)h_kv * d, sb = (long)Lk * sj;
+    const int first = Lk - Lq; /* position of query row 0 */
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *kslab = (double *)malloc(sizeof(double) * (size_t)Lk * d);
+        double *vslab = (double *)malloc(sizeof(double) * (size_t)Lk * d);
+        double *kvis = (double *)malloc(sizeof(double) * (size_t)Lk * d);
+        double *vvis = (double *)malloc(sizeof(double) * (size_t)Lk * d);
+        double *scores = (double *)malloc(sizeof(double) * (size_t)Lk);
+        double *pvis = (double *)malloc(sizeof(double) * (size_t)Lk);
+        int *vis = (int *)malloc(sizeof(int) * (size_t)Lk);
+        if (!kslab || !vslab || !kvis || !vvis || !scores || !pvis || !vis) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+            int cur_b = -1, cur_kvh = -1;
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < n_rows; ++r) {
+                int b = (int)row_bih[3 * r], i = (int)row_bih[3 * r + 1];
+                int kvh = kv_head_of((int)row_bih[3 * r + 2], h_q, h_kv);
+                if (b != cur_b || kvh != cur_kvh) {
+                    /* explicit repeat of this head's keys and values */
+                    repeat_kv_slab(k, sb, sj, sh, b, kvh, Lk, d, kslab);
+                    repeat_kv_slab(v, sb, sj, sh, b, kvh, Lk, d, vslab);
+                    cur_b = b;
+                    cur_kvh = kvh;
+                }
+                /* the visible set of this row */
+                const uint8_t *mrow = mask + ((int64_t)b * Lq + i) * (int64_t)Lk;
+                int n_vis = 0;
+                for (int j = 0; j < Lk; ++j) {
+                    if (mrow[j] == 0) continue;
+                    if (causal && j > first + i) continue;
+                    vis[n_vis++] = j;
+                }
+                for (int t = 0; t < n_vis; ++t) {
+                    memcpy(kvis + (long)t * d, kslab + (long)vis[t] * d, sizeof(double) * (size_t)d);
+                    memcpy(vvis + (long)t * d, vslab + (long)vis[t] * d, sizeof(double) * (size_t)d);
+                }
+                attend_one_row(q_rows + r * (int64_t)d, kvis, vvis, n_vis, d, scale, scores,
+                               out + r * (int64_t)d, probs ? pvis : NULL);
+                if (probs) {
+                    double *prow = probs + r * (int64_t)Lk;
+                    for (int j = 0; j < Lk; ++j) prow[j] = 0.0;
+                    for (int t = 0; t < n_vis; ++t) prow[vis[t]] = pvis[t];
+                }
+            }
+        }
+        free(kslab);
+        free(vslab);
+        free(kvis);
+        free(vvis);
+        free(scores);
+        free(pvis);
+        free(vis);
+    }
+    return failed ? ORACLE_ERR_NOMEM : 0;
+}
+
+/*
+ * Full prefill with a keep-mask: q, o [B][L_q][h_q][d], k, v [B][L_k][h_kv][d],
+ * mask [B][L_q][L_k] (see gqa_oracle_prefill_mask_rows); probs NULL or
+ * [B][h_q][L_q][L_k].
+ */
+int gqa_oracle_prefill_mask(const double *q, const double *k, const double *v,
+                            const uint8_t *mask, double *o, int B, int Lq, int Lk, int h_q,
+                            int h_kv, int d, int causal, double scale, double *probs) {
+    if (B <= 0 || Lq <= 0 || Lk < Lq || d <= 0) return ORACLE_ERR_ARG;
+    if (check_heads(h_q, h_kv)) return ORACLE_ERR_ARG;
+    int64_t n = (int64_t)B * h_q * Lq;
+    int64_t *bih = (int64_t *)malloc(sizeof(int64_t) * 3 * (size_t)n);
+    double *qr = (double *)malloc(sizeof(double) * (size_t)(n * d));
+    double *orow = (double *)malloc(sizeof(double) * (size_t)(n * d));
+    if (!bih || !qr || !orow) {
+        free(bih);
+        free(qr);
+        free(orow);
+        return ORACLE_ERR_NOMEM;
+    }
+    /* rows ordered by (b, h, i), which is also the order of probs */
+    int64_t r = 0;
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < h_q; ++h)
+            for (int i = 0; i < Lq; ++i, ++r) {
+                bih[3 * r] = b;
+                bih[3 * r + 1] = i;
+                bih[3 * r + 2] = h;
+                memcpy(qr + r * d, q + (((int64_t)b * Lq + i) * h_q + h) * d,
+                       sizeof(double) * (size_t)d);
+            }
+    int rc = gqa_oracle_prefill_mask_rows(qr, bih, n, k, v, mask, B, Lq, Lk, h_q, h_kv, d, causal,
+                                          scale, orow, probs);
+    if (rc == 0) {
+        r = 0;
+        for (int b = 0; b < B; ++b)
+            for (int h = 0; h < h_q; ++h)
+                for (int i = 0; i < Lq; ++i, ++r)
+                    memcpy(o + (((int64_t)b * Lq + i) * h_q + h) * d, orow + r * d,
+                           sizeof(double) * (size_t)d);
+    }
+    free(bih);
+    free(qr);
+    free(orow);
+    return rc;
 }
 
 /*

@@ -647,6 +647,103 @@ def pin_rope_decode_step():
     _close(k1[:, :, :n + 1], k2[:, :, :n + 1], 0.0, "identity tables: appended permuted key")
 
 
+def pin_mask_golden():
+    """The hand-worked keep-mask case: closed-form weights, a fully hidden row
+    that is zero, and the causal mask applied on top of the keep-mask."""
+    g = _golden("mask_by_hand.json")
+    q, k, v, m = (np.array(g[n]) for n in ("q", "k", "v", "mask"))
+    tol = g["tolerance"]
+    for causal, key in ((False, "expected_noncausal"), (True, "expected_causal")):
+        o = oracle.prefill_mask(q, k, v, m, causal, g["scale"])
+        _close(o, g[key], tol, f"mask by hand causal={causal}")
+        ob = brute.prefill_mask(g["q"], g["k"], g["v"], g["mask"], causal, g["scale"])
+        _close(ob, g[key], tol, f"brute force mask by hand causal={causal}")
+    assert np.array_equal(oracle.prefill_mask(q, k, v, m, False, 1.0)[0, 1],
+                          np.zeros((2, 2))), "a row with no visible key is exactly zero"
+
+
+def _random_mask(shape, seed, density=0.5):
+    g = np.random.default_rng(seed)
+    return (g.random(shape) < density).astype(np.uint8)
+
+
+def pin_mask_library():
+    """Against torch's fp64 SDPA with a boolean attn_mask (the keep-mask, and
+    bottom-right causal folded in) and enable_gqa for the head map, on an
+    asymmetric random mask with L_q < L_k; rows with no visible key are zero."""
+    B, Lq, Lk, h_q, h_kv, d = 2, 9, 13, 6, 2, 5
+    q, k, v = (_rand((B, Lq, h_q, d), 260), _rand((B, Lk, h_kv, d), 261),
+               _rand((B, Lk, h_kv, d), 262))
+    m = _random_mask((B, Lq, Lk), 263, 0.45)
+    m[1, 4] = 0  # one row with no visible key
+    for causal in (False, True):
+        keep = torch.from_numpy(m != 0)
+        if causal:
+            i = torch.arange(Lq)[:, None]
+            j = torch.arange(Lk)[None, :]
+            keep = keep & (j <= Lk - Lq + i)[None]
+        o = oracle.prefill_mask(q, k, v, m, causal, 0.4)
+        tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3) for x in (q, k, v))
+        ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=keep[:, None], scale=0.4,
+                                             enable_gqa=True).permute(0, 2, 1, 3).numpy()
+        empty = ~keep.any(dim=-1).numpy()  # [B, Lq]
+        assert empty[1, 4], "the emptied row must have no visible key"
+        _close(o[~empty], ref[~empty], 1e-12, f"mask vs masked SDPA causal={causal}")
+        _close(o[empty], np.zeros_like(o[empty]), 0.0, "rows with no visible key are zero")
+
+
+def pin_mask_reductions():
+    """Masks that other entry points express: all ones is the prefill against
+    L_k keys, lengths are the padded variable-length prefill, and the lower
+    triangle without the causal flag is the causal prefill (bit for bit: the
+    same keys in the same order)."""
+    B, L, h_q, h_kv, d = 3, 10, 4, 2, 6
+    q, k, v = _rand((B, L, h_q, d), 270), _rand((B, L, h_kv, d), 271), _rand((B, L, h_kv, d), 272)
+    for causal in (False, True):
+        ones = np.ones((B, L, L), np.uint8)
+        _close(oracle.prefill_mask(q, k, v, ones, causal, 0.5),
+               oracle.prefill(q, k, v, causal=causal, scale=0.5), 0.0, "all-ones mask")
+        lens = [10, 3, 0]
+        bylen = np.zeros((B, L, L), np.uint8)
+        for b, n in enumerate(lens):
+            bylen[b, :, :n] = 1
+        _close(oracle.prefill_mask(q, k, v, bylen, causal, 0.5),
+               oracle.prefill_varlen(q, k, v, lens, causal, 0.5), 0.0, "length mask")
+    tril = np.broadcast_to(np.tril(np.ones((L, L), np.uint8)), (B, L, L))
+    _close(oracle.prefill_mask(q, k, v, tril, False, 0.5),
+           oracle.prefill(q, k, v, causal=True, scale=0.5), 0.0, "lower-triangle mask")
+    qc, kc, vc = q[:, 6:], k, v
+    onesc = np.ones((B, 4, L), np.uint8)
+    _close(oracle.prefill_mask(qc, kc, vc, onesc, True, 0.5),
+           oracle.prefill_cached(qc, kc, vc, True, 0.5), 0.0, "all-ones mask, L_q < L_k")
+
+
+def pin_mask_brute():
+    """Against the pure-Python brute force on random masks (causal and not,
+    L_q < L_k), and the rows entry against the full entry."""
+    B, Lq, Lk, h_q, h_kv, d = 2, 5, 8, 6, 3, 4
+    q, k, v = (_rand((B, Lq, h_q, d), 280), _rand((B, Lk, h_kv, d), 281),
+               _rand((B, Lk, h_kv, d), 282))
+    m = _random_mask((B, Lq, Lk), 283, 0.4)
+    for causal in (False, True):
+        o = oracle.prefill_mask(q, k, v, m, causal, 0.7)
+        ob = brute.prefill_mask(q.tolist(), k.tolist(), v.tolist(), m.tolist(), causal, 0.7)
+        _close(o, ob, 1e-12, f"mask vs brute force causal={causal}")
+        rows = [(0, 0, 0), (1, 4, 5), (0, 2, 3), (1, 1, 2)]
+        qr = np.array([q[b, i, h] for (b, i, h) in rows])
+        _close(oracle.prefill_mask_rows(qr, rows, k, v, m, h_q, causal, 0.7),
+               np.array([o[b, i, h] for (b, i, h) in rows]), 0.0, "mask rows vs full")
+    _, p = oracle.prefill_mask(q, k, v, m, True, 0.7, return_probs=True)
+    sums = p.sum(axis=-1)
+    vis = np.array([[(m[b, i] * (np.arange(Lk) <= Lk - Lq + i)).any() for i in range(Lq)]
+                    for b in range(B)])
+    ok = sums[np.broadcast_to(vis[:, None], sums.shape)]
+    _close(ok, np.ones_like(ok), 1e-15, "mask rows sum to 1")
+    hidden = (m[:, None] == 0) | (np.arange(Lk)[None, None, None] >
+                                  (Lk - Lq + np.arange(Lq))[None, None, :, None])
+    assert np.all(p[np.broadcast_to(hidden, p.shape)] == 0.0), "hidden keys get weight 0"
+
+
 ALL_PINS = [pin_hand_2x2, pin_head_map, pin_decode_golden, pin_mha_reduction,
             pin_mqa_reduction, pin_gqa_library, pin_rows_sum_to_one, pin_k_zero_mean,
             pin_causal_row0, pin_identical_heads, pin_invariances, pin_cross_path,
@@ -656,7 +753,8 @@ ALL_PINS = [pin_hand_2x2, pin_head_map, pin_decode_golden, pin_mha_reduction,
             pin_append_to_empty_cache, pin_append_brute_and_tail, pin_token_major_brute,
             pin_paged_brute, pin_paged_shared_prefix, pin_rope_golden,
             pin_rope_identity_tables, pin_rope_relative_position, pin_rope_brute,
-            pin_varlen_equals_truncated, pin_varlen_library, pin_rope_decode_step]
+            pin_varlen_equals_truncated, pin_varlen_library, pin_rope_decode_step,
+            pin_mask_golden, pin_mask_library, pin_mask_reductions, pin_mask_brute]
 
 
 def main(argv):

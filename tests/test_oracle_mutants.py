@@ -45,6 +45,10 @@ MUTANTS = {
                                "/* key padding dropped */"),
     "rope_decode_position_off_by_one": ("const long p = seqlens[b];",
                                         "const long p = seqlens[b] > 0 ? seqlens[b] - 1 : 0;"),
+    "mask_ignored": ("if (mrow[j] == 0) continue;", "/* keep-mask dropped */"),
+    "mask_transposed": ("if (mrow[j] == 0) continue;",
+                        "if (j < Lq && mask[((int64_t)b * Lq + j) * (int64_t)Lk + i] == 0) continue;"),
+    "mask_causal_dropped": ("if (causal && j > first + i) continue;", "/* causal dropped */"),
     "first_head_of_group_only": ("int kvh = kv_head_of(h, h_q, h_kv);\n                int n = seqlens[b];",
                                  "int kvh = 0;\n                int n = seqlens[b];"),
 }
