@@ -18,6 +18,11 @@ the device is not a gfx950 GPU, the calls raise.
         -> o [B, 1, h_q, d].
     prefill_varlen(q, k, v, kv_lens, causal=..., scale=None, out=None)
         padded batch; key j of sequence b visible iff j < kv_lens[b].
+    prefill_mask(q, k, v, mask, causal=..., scale=None, out=None)
+        q [B, L_q, h_q, d] against k/v [B, L_k, h_kv, d]; key j visible to query
+        row i of sequence b only where mask[b, i, j] != 0 (mask [B, L_q, L_k]
+        or [L_q, L_k], bool or uint8, on the GPU), and causally as in
+        prefill_chunk; a row with no visible key is zero.
     prefill_rope(q, k, v, cos, sin, causal=..., scale=None, out=None, k_rot=None)
         q and k rotated (tables cos, sin [L, d/2]), then prefill; returns
         (o, k_rot).
@@ -82,6 +87,9 @@ def lib() -> ctypes.CDLL:
     L.gqa_decode_paged.restype = I
     L.gqa_prefill_varlen.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P]
     L.gqa_prefill_varlen.restype = I
+    LL = ctypes.c_longlong
+    L.gqa_prefill_mask.argtypes = [P, P, P, P, LL, LL, P, I, I, I, I, I, I, I, I, F, P]
+    L.gqa_prefill_mask.restype = I
     L.gqa_prefill_rope.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
     L.gqa_prefill_rope.restype = I
     L.gqa_decode_append_rope.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P,
@@ -122,6 +130,48 @@ def _check(t: torch.Tensor, name: str, ndim: int):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _same(ref: torch.Tensor, *named):
+    """Every (tensor, name) pair shares ref's dtype and device."""
+    for t, name in named:
+        if t.dtype != ref.dtype:
+            raise TypeError(f"{name} must have dtype {ref.dtype}, got {t.dtype}")
+        if t.device != ref.device:
+            raise ValueError(f"{name} must be on {ref.device}, got {t.device}")
+
+
+def _on_device(ref: torch.Tensor, *named):
+    """Every (tensor, name) pair sits on ref's device."""
+    for t, name in named:
+        if t.device != ref.device:
+            raise ValueError(f"{name} must be on {ref.device}, got {t.device}")
+
+
+def _check_out(out, like: torch.Tensor, name: str = "out"):
+    """A caller-supplied output must be a contiguous GPU tensor of like's shape and dtype."""
+    _check(out, name, like.dim())
+    if out.shape != like.shape or out.dtype != like.dtype:
+        raise ValueError(f"{name} must match {tuple(like.shape)} {like.dtype}, got "
+                         f"{tuple(out.shape)} {out.dtype}")
+    if out.device != like.device:
+        raise ValueError(f"{name} must be on {like.device}")
+
+
+def _workspace(workspace, need: int, like: torch.Tensor):
+    """The caller's workspace (a GPU tensor of at least need bytes), or a new one."""
+    if workspace is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=like.device)
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+        raise ValueError("workspace must be a GPU tensor")
+    if workspace.device != like.device:
+        raise ValueError(f"workspace must be on {like.device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} "
+                         f"bytes, {need} needed")
+    return workspace
+
+
 def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -134,14 +184,11 @@ def prefill(q, k, v, *, causal: bool, scale: float | None = None, out=None):
     h_kv = k.shape[2]
     if tuple(k.shape) != (B, L, h_kv, d) or v.shape != k.shape:
         raise ValueError("k and v must be [B, L, h_kv, d] with q's B, L and d")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise TypeError("q, k and v must share one dtype")
+    _same(q, (k, "k"), (v, "v"))
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check(out, "out", 4)
-        if out.shape != q.shape or out.dtype != q.dtype:
-            raise ValueError("out must match q in shape and dtype")
+        _check_out(out, q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = lib().gqa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, L, h_q,
@@ -162,14 +209,11 @@ def prefill_chunk(q, k, v, *, causal: bool, scale: float | None = None, out=None
     Lk, h_kv = k.shape[1], k.shape[2]
     if tuple(k.shape) != (B, Lk, h_kv, d) or v.shape != k.shape:
         raise ValueError("k and v must be [B, L_k, h_kv, d] with q's B and d")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise TypeError("q, k and v must share one dtype")
+    _same(q, (k, "k"), (v, "v"))
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check(out, "out", 4)
-        if out.shape != q.shape or out.dtype != q.dtype:
-            raise ValueError("out must match q in shape and dtype")
+        _check_out(out, q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = lib().gqa_prefill_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Lq,
@@ -201,15 +245,14 @@ def decode(q, k_cache, v_cache, seqlens, *, out=None, workspace=None, num_splits
         raise ValueError("caches must be [B, h_kv, S, d] with q's B and d")
     if seqlens.dtype != torch.int32 or seqlens.shape[0] != B:
         raise ValueError("seqlens must be int32 [B]")
+    _same(q, (k_cache, "k_cache"), (v_cache, "v_cache"))
+    _on_device(q, (seqlens, "seqlens"))
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check(out, "out", 4)
-        if out.shape != q.shape or out.dtype != q.dtype:
-            raise ValueError("out must match q in shape and dtype")
+        _check_out(out, q)
     need = decode_workspace_bytes(B, h_q, h_kv, d, num_splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q)
     st = lib().gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                           seqlens.data_ptr(), out.data_ptr(), B, h_q, h_kv, S, d, _dtype_code(q),
                           int(num_splits), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -241,15 +284,14 @@ def decode_append(q, k_new, v_new, k_cache, v_cache, seqlens, *, out=None, works
         raise ValueError("k_new and v_new must be [B, 1, h_kv, d]")
     if seqlens.dtype != torch.int32 or seqlens.shape[0] != B:
         raise ValueError("seqlens must be int32 [B]")
+    _same(q, (k_cache, "k_cache"), (v_cache, "v_cache"), (k_new, "k_new"), (v_new, "v_new"))
+    _on_device(q, (seqlens, "seqlens"))
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check(out, "out", 4)
-        if out.shape != q.shape or out.dtype != q.dtype:
-            raise ValueError("out must match q in shape and dtype")
+        _check_out(out, q)
     need = decode_workspace_bytes(B, h_q, h_kv, d, num_splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q)
     st = lib().gqa_decode_append(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
                                  k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
                                  out.data_ptr(), B, h_q, h_kv, S, d, _dtype_code(q),
@@ -264,12 +306,9 @@ def _decode_out_ws(q, out, workspace, B, h_q, h_kv, d, num_splits):
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check(out, "out", 4)
-        if out.shape != q.shape or out.dtype != q.dtype:
-            raise ValueError("out must match q in shape and dtype")
+        _check_out(out, q)
     need = decode_workspace_bytes(B, h_q, h_kv, d, num_splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q)
     return out, workspace
 
 
@@ -286,6 +325,8 @@ def decode_token_major(q, k_cache, v_cache, seqlens, *, out=None, workspace=None
         raise ValueError("need q [B, 1, h_q, d] and caches [B, S, h_kv, d]")
     if seqlens.dtype != torch.int32 or seqlens.shape[0] != B:
         raise ValueError("seqlens must be int32 [B]")
+    _same(q, (k_cache, "k_cache"), (v_cache, "v_cache"))
+    _on_device(q, (seqlens, "seqlens"))
     out, workspace = _decode_out_ws(q, out, workspace, B, h_q, h_kv, d, num_splits)
     st = lib().gqa_decode_token_major(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                       seqlens.data_ptr(), out.data_ptr(), B, h_q, h_kv, S, d,
@@ -313,6 +354,8 @@ def decode_paged(q, k_pages, v_pages, block_table, seqlens, *, out=None, workspa
         raise ValueError("block_table must be int32 [B, max_blocks]")
     if seqlens.dtype != torch.int32 or seqlens.shape[0] != B:
         raise ValueError("seqlens must be int32 [B]")
+    _same(q, (k_pages, "k_pages"), (v_pages, "v_pages"))
+    _on_device(q, (seqlens, "seqlens"), (block_table, "block_table"))
     out, workspace = _decode_out_ws(q, out, workspace, B, h_q, h_kv, d, num_splits)
     st = lib().gqa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
                                 block_table.data_ptr(), seqlens.data_ptr(), out.data_ptr(), B,
@@ -339,14 +382,16 @@ def prefill_rope(q, k, v, cos, sin, *, causal: bool, scale=None, out=None, k_rot
     if (cos.dtype != torch.float32 or sin.dtype != torch.float32
             or tuple(cos.shape) != (L, d // 2) or sin.shape != cos.shape):
         raise ValueError("cos and sin must be float32 [L, d/2]")
+    _same(q, (k, "k"), (v, "v"))
+    _on_device(q, (cos, "cos"), (sin, "sin"))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if k_rot is None:
         k_rot = torch.empty_like(k)
-    _check(out, "out", 4)
-    _check(k_rot, "k_rot", 4)
+    _check_out(out, q)
+    _check_out(k_rot, k, "k_rot")
     st = lib().gqa_prefill_rope(q.data_ptr(), k.data_ptr(), v.data_ptr(), cos.data_ptr(),
                                 sin.data_ptr(), out.data_ptr(), k_rot.data_ptr(), B, L, h_q, h_kv,
                                 d, _dtype_code(q), int(bool(causal)), float(scale), _stream(q))
@@ -367,16 +412,86 @@ def prefill_varlen(q, k, v, kv_lens, *, causal: bool, scale=None, out=None):
         raise ValueError("k and v must be [B, L, h_kv, d] with q's B, L and d")
     if kv_lens.dtype != torch.int32 or kv_lens.shape[0] != B:
         raise ValueError("kv_lens must be int32 [B]")
+    _same(q, (k, "k"), (v, "v"))
+    _on_device(q, (kv_lens, "kv_lens"))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
-    _check(out, "out", 4)
+    _check_out(out, q)
     st = lib().gqa_prefill_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                   kv_lens.data_ptr(), B, L, h_q, h_kv, d, _dtype_code(q),
                                   int(bool(causal)), float(scale), _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_prefill_varlen")
+    return out
+
+
+def mask_layout(mask: torch.Tensor, B: int, Lq: int, Lk: int):
+    """(uint8 tensor, row stride, batch stride) of a keep-mask [B, L_q, L_k] as
+    the kernels read it.
+
+    The kernels read each mask row as 16-byte pieces: the row stride (bytes)
+    must be a multiple of 16 and at least L_k, the batch stride a multiple of
+    16 (0 shares one mask across the batch), and the storage must hold
+    (B - 1) * batch stride + L_q * row stride bytes.  A mask laid out that way
+    is used in place (a bool mask as its uint8 view); any other is copied into
+    rows padded to a multiple of 16 bytes."""
+    if mask.dtype not in (torch.bool, torch.uint8):
+        raise TypeError("mask must be bool or uint8")
+    m = mask.view(torch.uint8) if mask.dtype == torch.bool else mask
+    pad = -(-Lk // 16) * 16
+    sr = m.stride(1) if Lq > 1 else pad
+    sb = m.stride(0) if B > 1 else 0
+    ok = (m.stride(2) == 1 or Lk == 1) and sr % 16 == 0 and sr >= Lk and sb % 16 == 0 \
+        and sb >= 0 and m.data_ptr() % 16 == 0
+    if ok:
+        avail = m.untyped_storage().nbytes() - m.storage_offset()
+        ok = avail >= (B - 1) * sb + Lq * sr
+    if not ok:
+        buf = torch.zeros(B, Lq, pad, dtype=torch.uint8, device=m.device)
+        buf[..., :Lk] = m
+        m, sr, sb = buf, pad, Lq * pad
+    return m, sr, sb
+
+
+def prefill_mask(q, k, v, mask, *, causal: bool, scale=None, out=None):
+    """Prefill with a keep-mask.  q [B,L_q,h_q,d], k/v [B,L_k,h_kv,d] (L_q <=
+    L_k, causal rows bottom-right aligned as in prefill_chunk), mask
+    [B,L_q,L_k] or [L_q,L_k] (shared by the batch), bool or uint8 on the GPU:
+    key j is visible to query row i of sequence b only where the mask is
+    nonzero.  A row with no visible key is zero.  k and v must be finite
+    everywhere (a hidden key has weight exactly 0, and 0 * NaN is NaN).
+    -> o [B,L_q,h_q,d]."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, 4)
+    B, Lq, h_q, d = q.shape
+    Lk, h_kv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Lk, h_kv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, L_k, h_kv, d] with q's B and d")
+    _same(q, (k, "k"), (v, "v"))
+    if not isinstance(mask, torch.Tensor):
+        raise TypeError("mask must be a torch.Tensor")
+    if mask.dim() == 2:
+        mask = mask.unsqueeze(0).expand(B, Lq, Lk)
+    if tuple(mask.shape) != (B, Lq, Lk):
+        raise ValueError(f"mask must be [B, L_q, L_k] = {(B, Lq, Lk)} or [L_q, L_k], got "
+                         f"{tuple(mask.shape)}")
+    if not mask.is_cuda:
+        raise ValueError("mask must be on the GPU")
+    _on_device(q, (mask, "mask"))
+    m, row_stride, batch_stride = mask_layout(mask, B, Lq, Lk)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_out(out, q)
+    st = lib().gqa_prefill_mask(q.data_ptr(), k.data_ptr(), v.data_ptr(), m.data_ptr(),
+                                int(row_stride), int(batch_stride), out.data_ptr(), B, Lq, Lk,
+                                h_q, h_kv, d, _dtype_code(q), int(bool(causal)), float(scale),
+                                _stream(q))
+    if st != 0:
+        raise GQAError(st, "gqa_prefill_mask")
     return out
 
 
@@ -407,12 +522,13 @@ def decode_append_rope(q, k_new, v_new, k_cache, v_cache, seqlens, cos, sin, *, 
         raise ValueError("cos and sin must be float32 [S, d/2]")
     if seqlens.dtype != torch.int32 or seqlens.shape[0] != B:
         raise ValueError("seqlens must be int32 [B]")
+    _same(q, (k_cache, "k_cache"), (v_cache, "v_cache"), (k_new, "k_new"), (v_new, "v_new"))
+    _on_device(q, (seqlens, "seqlens"), (cos, "cos"), (sin, "sin"))
     if out is None:
         out = torch.empty_like(q)
-    _check(out, "out", 4)
+    _check_out(out, q)
     need = decode_rope_workspace_bytes(B, h_q, h_kv, d, num_splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q)
     st = lib().gqa_decode_append_rope(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
                                       k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
                                       cos.data_ptr(), sin.data_ptr(), out.data_ptr(), B, h_q, h_kv,

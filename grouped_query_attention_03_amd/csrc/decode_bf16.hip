@@ -162,12 +162,22 @@ __device__ __forceinline__ void dc_block(const GQA_LDS char *qt, const GQA_LDS c
     }
 }
 
+// Rows sequence b attends: its length clamped to [0, S - extra], plus extra
+// (1 when the new token's row is appended and attended).  The clamp keeps a
+// length outside its precondition from reading past the sequence's cache
+// rows (or its block-table row); every use of a length goes through here.
+__device__ __forceinline__ int dc_clamp_rows(int len, int extra, int S) {
+    return min(max(len, 0), S - extra) + extra;
+}
+__device__ __forceinline__ int dc_rows(const int32_t *seqlens, int b, int extra, int S) {
+    return dc_clamp_rows(load_const(seqlens, b), extra, S);
+}
+
 // Segment bookkeeping shared by the split and merge passes.  Segments are
 // ordered (sequence b, key/value head, query-head subgroup); segment
-// (b, kv, qs) has nblk(b) = ceil((seqlens[b] + extra) / 32) blocks, extra = 1
-// when the new token's row is appended and attended.
-__device__ __forceinline__ int dc_nblk(const int32_t *seqlens, int b, int extra) {
-    return (load_const(seqlens, b) + extra + DC_BK - 1) / DC_BK;
+// (b, kv, qs) has nblk(b) = ceil(rows(b) / 32) blocks.
+__device__ __forceinline__ int dc_nblk(const int32_t *seqlens, int b, int extra, int S) {
+    return (dc_rows(seqlens, b, extra, S) + DC_BK - 1) / DC_BK;
 }
 
 __device__ __forceinline__ long long dc_slice_start(int w, long long T, int NW) {
@@ -189,7 +199,7 @@ __device__ __forceinline__ long long dc_wave_sum(long long x) {
 
 // Blocks of the whole list (T) and blocks of the sequences before `upto` (P),
 // one sequence per lane, 64 at a time.
-__device__ __forceinline__ void dc_block_totals(const int32_t *seqlens, int extra, int B,
+__device__ __forceinline__ void dc_block_totals(const int32_t *seqlens, int extra, int S, int B,
                                                 int segs_per_b, int upto, long long &T,
                                                 long long &P) {
     const int lane = threadIdx.x & 63;
@@ -198,7 +208,8 @@ __device__ __forceinline__ void dc_block_totals(const int32_t *seqlens, int extr
         const int bb = b0 + lane;
         if (bb < B) {
             const long long n =
-                (long long)((seqlens[bb] + extra + DC_BK - 1) / DC_BK) * segs_per_b;
+                (long long)((dc_clamp_rows(seqlens[bb], extra, S) + DC_BK - 1) / DC_BK) *
+                segs_per_b;
             t += n;
             if (bb < upto) p += n;
         }
@@ -210,7 +221,7 @@ __device__ __forceinline__ void dc_block_totals(const int32_t *seqlens, int extr
 // The sequence whose segments hold global block `pos` (0 <= pos < T) and the
 // number of blocks before its first segment: an inclusive scan over 64
 // sequences at a time and a ballot.
-__device__ __forceinline__ void dc_locate(const int32_t *seqlens, int extra, int B,
+__device__ __forceinline__ void dc_locate(const int32_t *seqlens, int extra, int S, int B,
                                           int segs_per_b, long long pos, int &b_out,
                                           long long &cum_out) {
     const int lane = threadIdx.x & 63;
@@ -220,7 +231,9 @@ __device__ __forceinline__ void dc_locate(const int32_t *seqlens, int extra, int
     for (int b0 = 0; b0 < B; b0 += 64) {
         const int bb = b0 + lane;
         const long long n =
-            bb < B ? (long long)((seqlens[bb] + extra + DC_BK - 1) / DC_BK) * segs_per_b : 0;
+            bb < B ? (long long)((dc_clamp_rows(seqlens[bb], extra, S) + DC_BK - 1) / DC_BK) *
+                         segs_per_b
+                   : 0;
         long long incl = n;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -277,7 +290,7 @@ __global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs 
 
     // total blocks and this wave's slice
     long long T, unused;
-    dc_block_totals(a.seqlens, a.extra, a.B, segs_per_b, 0, T, unused);
+    dc_block_totals(a.seqlens, a.extra, a.S, a.B, segs_per_b, 0, T, unused);
     const long long pos = dc_slice_start(w, T, a.NW);
     const long long end = dc_slice_start(w + 1, T, a.NW);
     if (pos >= end) return;
@@ -289,21 +302,21 @@ __global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs 
     {
         int b0;
         long long cum;
-        dc_locate(a.seqlens, a.extra, a.B, segs_per_b, pos, b0, cum);
+        dc_locate(a.seqlens, a.extra, a.S, a.B, segs_per_b, pos, b0, cum);
         b0 = __builtin_amdgcn_readfirstlane(b0);
-        const long long nb = dc_nblk(a.seqlens, b0, a.extra);  // > 0: the block at pos lies in b0
+        const long long nb = dc_nblk(a.seqlens, b0, a.extra, a.S);  // > 0: the block at pos lies in b0
         cur = Cur{b0, (int)((pos - cum) / nb), (int)((pos - cum) % nb)};
     }
     const float c = a.c;
 
     auto advance = [&](Cur &u) {
-        if (++u.blk == dc_nblk(a.seqlens, u.b, a.extra)) {
+        if (++u.blk == dc_nblk(a.seqlens, u.b, a.extra, a.S)) {
             u.blk = 0;
             if (++u.seg == segs_per_b) {
                 u.seg = 0;
                 do {
                     ++u.b;
-                } while (u.b < a.B && dc_nblk(a.seqlens, u.b, a.extra) == 0);
+                } while (u.b < a.B && dc_nblk(a.seqlens, u.b, a.extra, a.S) == 0);
             }
         }
     };
@@ -312,7 +325,7 @@ __global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs 
     // clamped to its last head), K rows, V rows (clamped to the last valid key)
     auto issue = [&](const Cur &u, GQA_LDS char *qt, GQA_LDS char *kt, GQA_LDS char *vt) {
         const int kvh = u.seg / a.n_qsub, qs = u.seg % a.n_qsub;
-        const int kend = load_const(a.seqlens, u.b) + a.extra;
+        const int kend = dc_rows(a.seqlens, u.b, a.extra, a.S);
         const int head0 = kvh * a.G + 16 * qs;
         const int key0 = DC_BK * u.blk;
         // rows key0 .. key0 + 31 of (b, kvh): base, row stride and the block's
@@ -344,12 +357,13 @@ __global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs 
     // 16-byte chunk per lane, from the block's LDS tiles, which hold them
     // already (chunk c of tile row r at r * ROW_BYTES + 16 (c ^ swz(r))), so
     // no global load has to be waited for.
-    // Skipped when seqlens[b] >= S, a broken precondition.
+    // Skipped when seqlens[b] is outside [0, S - 1], a broken precondition
+    // (the attention then sees the clamped length's rows and the new row).
     auto store_new_rows = [&](const Cur &u, const GQA_LDS char *kt, const GQA_LDS char *vt) {
         constexpr int CPR = Lay::CPR;
         const int kvh = u.seg / a.n_qsub;
         const int row = load_const(a.seqlens, u.b);
-        if (row >= a.S || lane >= 2 * CPR) return;
+        if (row < 0 || row >= a.S || lane >= 2 * CPR) return;
         const bool is_v = lane >= CPR;
         const int ch = is_v ? lane - CPR : lane;
         const int r = row - DC_BK * u.blk;  // the row's place in the tile
@@ -401,9 +415,10 @@ __global__ __launch_bounds__(DC_THREADS, 1) void decode_split_kernel(DecodeArgs 
         // issued in between only make the wait stricter
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"((DC_SLOTS - 1) * OPS) : "memory");
         dc_block<D, QD * Lay::ROWS_PER_DMA>(qt, kt, vt, DC_BK * cur.blk,
-                    load_const(a.seqlens, cur.b) + a.extra, qcol < heads_in(cur), c, m_run, l_run, acc);
+                    dc_rows(a.seqlens, cur.b, a.extra, a.S), qcol < heads_in(cur), c, m_run, l_run,
+                    acc);
         --left;
-        const bool last_block = cur.blk + 1 == dc_nblk(a.seqlens, cur.b, a.extra);
+        const bool last_block = cur.blk + 1 == dc_nblk(a.seqlens, cur.b, a.extra, a.S);
         if (APPEND && last_block && cur.seg % a.n_qsub == 0) store_new_rows(cur, kt, vt);
         if (last_block || left == 0) close_segment(cur);
         advance(cur);
@@ -441,14 +456,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     const int kvh = h / a.G, hg = h % a.G, qs = hg / 16, qcol = hg % 16;
     const int segs_per_b = a.h_kv * a.n_qsub;
     __bf16 *op = static_cast<__bf16 *>(a.o) + (size_t)wid * D + PER * lane;
-    const int nb = dc_nblk(a.seqlens, b, a.extra);
+    const int nb = dc_nblk(a.seqlens, b, a.extra, a.S);
     if (nb == 0) {
 #pragma unroll
         for (int e = 0; e < PER; ++e) op[e] = (__bf16)0.f;
         return;
     }
     long long T, P;
-    dc_block_totals(a.seqlens, a.extra, a.B, segs_per_b, b, T, P);
+    dc_block_totals(a.seqlens, a.extra, a.S, a.B, segs_per_b, b, T, P);
     const int seg_in_b = kvh * a.n_qsub + qs;
     P += (long long)seg_in_b * nb;  // first block of this segment
     const long long seg_global = (long long)b * segs_per_b + seg_in_b;

@@ -78,8 +78,19 @@ gqa_status prefill_impl(const void *q, const void *k, const void *v, void *o, in
                         void *hip_stream, const float *rope_cos = nullptr,
                         const float *rope_sin = nullptr, void *k_rot = nullptr,
                         bool rope = false, const int32_t *kv_lens = nullptr,
-                        bool varlen = false) {
+                        bool varlen = false, const uint8_t *mask = nullptr,
+                        long long mask_row = 0, long long mask_batch = 0,
+                        bool masked = false) {
     if (!q || !k || !v || !o) return GQA_ERR_NULL_POINTER;
+    if (masked) {
+        if (!mask) return GQA_ERR_NULL_POINTER;
+        if (!aligned16(mask)) return GQA_ERR_ALIGNMENT;
+        // rows of 16-byte pieces covering the L_k keys; one batch's rows
+        // addressed with 32-bit byte offsets
+        if (mask_row < Lk || mask_row % 16 != 0 || mask_batch < 0 || mask_batch % 16 != 0)
+            return GQA_ERR_SIZE;
+        if (Lq > 0 && mask_row > (long long)0xffffffff / Lq) return GQA_ERR_SIZE;
+    }
     if (varlen) {
         if (!kv_lens) return GQA_ERR_NULL_POINTER;
         if ((reinterpret_cast<uintptr_t>(kv_lens) & 3u) != 0) return GQA_ERR_ALIGNMENT;
@@ -124,6 +135,14 @@ gqa_status prefill_impl(const void *q, const void *k, const void *v, void *o, in
     a.rope_cos = rope ? rope_cos : nullptr;
     a.rope_sin = rope ? rope_sin : nullptr;
     a.kv_lens = varlen ? kv_lens : nullptr;
+    a.mask = masked ? mask : nullptr;
+    a.mask_row = masked ? mask_row : 0;
+    a.mask_batch = masked ? mask_batch : 0;
+    {
+        // an exact power of two may be folded into q (q * 2^e is exact in bf16)
+        int e = 0;
+        a.fold = frexpf(a.c, &e) == 0.5f ? 1 : 0;
+    }
     if ((int64_t)a.n_units * a.n_qtiles > 0x7fffffff) return GQA_ERR_SIZE;
 
     gqa_status st = check_device();
@@ -180,6 +199,15 @@ gqa_status gqa_prefill_varlen(const void *q, const void *k, const void *v, void 
                               gqa_dtype dt, int causal, float scale, void *hip_stream) {
     return prefill_impl(q, k, v, o, B, L, L, h_q, h_kv, d, dt, causal, scale, hip_stream, nullptr,
                         nullptr, nullptr, false, kv_lens, true);
+}
+
+gqa_status gqa_prefill_mask(const void *q, const void *k, const void *v, const uint8_t *mask,
+                            long long mask_row_stride, long long mask_batch_stride, void *o,
+                            int B, int L_q, int L_k, int h_q, int h_kv, int d, gqa_dtype dt,
+                            int causal, float scale, void *hip_stream) {
+    return prefill_impl(q, k, v, o, B, L_q, L_k, h_q, h_kv, d, dt, causal, scale, hip_stream,
+                        nullptr, nullptr, nullptr, false, nullptr, false, mask, mask_row_stride,
+                        mask_batch_stride, true);
 }
 
 int gqa_decode_default_splits(void) { return kDefaultSplits; }

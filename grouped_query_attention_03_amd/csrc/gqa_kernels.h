@@ -19,12 +19,20 @@ struct PrefillArgs {
     int n_units;   // B * h_kv * nsub
     int n_qtiles;  // ceil(L / BM)
     float c;       // scale * log2(e)
+    // c is an exact power of two: q * c is exact in bf16 and may be folded
+    // into q (the plain bf16 form only); otherwise c multiplies the fp32 scores
+    int fold;
     // rotary tables cos, sin [positions][d/2] fp32 (row p for position p);
     // non-null only in the rotary form, where q is rotated as it is loaded
     const float *rope_cos, *rope_sin;
     // per-sequence key lengths [B] (key j of sequence b visible iff j <
     // kv_lens[b]), or null: all Lk keys
     const int32_t *kv_lens;
+    // keep-mask bytes, or null: key j is visible to query row i of sequence b
+    // only if mask[b * mask_batch + i * mask_row + j] != 0 (strides in bytes;
+    // mask_row a multiple of 16, L * mask_row < 2^32)
+    const uint8_t *mask;
+    long long mask_row, mask_batch;
 };
 
 // Rotary embedding of rows x [rows][d] into out, tables cos, sin [L][d/2].

@@ -24,6 +24,10 @@
 //   P = exp2(S * scale*log2(e) - m) with a lazily updated running max m: the
 //   accumulators are rescaled only when a row max grows by more than TAU (in
 //   log2 units), so every P <= 2^TAU and almost no rescale is executed.
+//   The factor scale*log2(e) multiplies the fp32 scores (one fma per score,
+//   fused with the subtraction of m), so q enters the product exactly as
+//   given.  Only when the factor is an exact power of two is it folded into q
+//   instead (q * 2^e is exact in bf16), which saves that fma.
 //   O^T[d][query] += V^T P^T: P^T comes straight out of the S^T accumulators
 //   (keys permuted consistently on both operands), V^T is read from the
 //   row-major V tile with the transposing ds_read_b64_tr_b16.
@@ -41,10 +45,14 @@
 //   Each wave waits for its own share of the next tile (s_waitcnt vmcnt) before
 //   the barrier that ends an iteration, so after that barrier the whole tile is
 //   visible: one work-group barrier per tile.
-//   Scale * log2(e) is folded into Q once, and every QK accumulator chain
-//   starts from -mu (the MFMA C operand), so S arrives in log2 units already
-//   shifted by the running max; row sums are taken with v_dot2_f32_bf16 on the
-//   bf16-rounded P that the PV product uses.
+//   In the folded form every QK accumulator chain starts from -mu (the MFMA C
+//   operand), so S arrives in log2 units already shifted by the running max;
+//   row sums are taken with v_dot2_f32_bf16 on the bf16-rounded P that the PV
+//   product uses.
+//   Keep-mask form: the mask bytes of the work-group's rows for each key tile
+//   are moved into the same ring slot by the same direct loads (a 3-slot ring,
+//   since a slot then also holds up to 256 rows x 64 bytes of mask); a wave
+//   whose 32 rows see no key of a tile skips that tile's products.
 //   Causal: tiles wholly above the diagonal are never loaded or computed; the
 //   diagonal and the sequence tail are masked element-wise.
 //   Work-groups map to XCDs so that a key/value head's tiles share one L2, and
@@ -60,9 +68,11 @@ namespace {
 constexpr int PF_WAVES = 8;
 constexpr int PF_THREADS = 64 * PF_WAVES;
 constexpr int PF_BN = 64;       // keys per tile
-constexpr int PF_SLOTS = 4;     // LDS ring depth (tiles)
 constexpr float PF_TAU = 8.0f;  // lazy-rescale threshold, log2 units
-constexpr int PF_DIST = 3;      // tiles issued ahead of the one being computed
+
+// Forms of the kernel: q rotated at load (ROPE), per-sequence key lengths
+// (VARLEN), a keep-mask of bytes (MASK).
+enum PfForm { kPfPlain = 0, kPfRope = 1, kPfVarlen = 2, kPfMask = 3 };
 
 template <int D>
 struct PfLay {
@@ -72,11 +82,25 @@ struct PfLay {
     static constexpr int TILE_BYTES = PF_BN * ROW_BYTES;     // one K or V tile
     static constexpr int DMA_PER_TENSOR = TILE_BYTES / 1024;
     static constexpr int DMA_PER_WAVE = 2 * DMA_PER_TENSOR / PF_WAVES;
-    static constexpr int SLOT_BYTES = 2 * TILE_BYTES;        // K tile then V tile
     static constexpr int ROWS_PER_SWEEP = 256 / ROW_BYTES;   // rows per pass over the banks
     static constexpr int KSTEPS = D / 16;                    // MFMA k-steps over d
     static constexpr int DB = D / 32;                        // 32-wide blocks of d
 };
+
+// The LDS ring: SLOTS slots, each the K tile, the V tile and (keep-mask form)
+// the mask bytes of up to 256 rows x 64 keys; tile x is issued PF_DIST = SLOTS - 1
+// iterations ahead into slot x % SLOTS.
+template <int D, int FORM>
+struct PfRing {
+    static constexpr int MASK_BYTES = FORM == kPfMask ? 256 * 64 : 0;
+    static constexpr int SLOT_BYTES = 2 * PfLay<D>::TILE_BYTES + MASK_BYTES;
+    static constexpr int SLOTS = FORM == kPfMask ? 3 : 4;
+    static constexpr int DIST = SLOTS - 1;
+};
+
+// Mask tile rows are 64 bytes (4 chunks of 16); logical chunk c of row r sits
+// at chunk position c ^ swz(r), so the rows read together spread over the banks.
+__device__ __forceinline__ int pf_mswz(int r) { return (r >> 2) & 3; }
 
 // Tiles are stored unpadded (each direct load writes 64 consecutive 16-byte
 // chunks); 16-byte chunk c of row r sits at chunk position c ^ swz(r).
@@ -97,29 +121,57 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// s_waitcnt vmcnt with a wave-uniform count known only at run time (0 .. 15;
+// larger counts wait for everything, which is only stricter).
+__device__ __forceinline__ void wait_vmcnt_rt(int n) {
+    switch (n) {
+        case 1: wait_vmcnt<1>(); break;
+        case 2: wait_vmcnt<2>(); break;
+        case 3: wait_vmcnt<3>(); break;
+        case 4: wait_vmcnt<4>(); break;
+        case 5: wait_vmcnt<5>(); break;
+        case 6: wait_vmcnt<6>(); break;
+        case 7: wait_vmcnt<7>(); break;
+        case 8: wait_vmcnt<8>(); break;
+        case 9: wait_vmcnt<9>(); break;
+        case 10: wait_vmcnt<10>(); break;
+        case 11: wait_vmcnt<11>(); break;
+        case 12: wait_vmcnt<12>(); break;
+        case 13: wait_vmcnt<13>(); break;
+        case 14: wait_vmcnt<14>(); break;
+        case 15: wait_vmcnt<15>(); break;
+        default: wait_vmcnt<0>(); break;
+    }
+}
+
 __device__ __forceinline__ void block_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-// ROPE: q is rotated as it is loaded (the keys arrive rotated already).
-// VARLEN: sequence b has a.kv_lens[b] visible keys (a padded batch).
-template <int D, bool CAUSAL, bool ROPE, bool VARLEN>
+// FORM (PfForm): kPfRope rotates q as it is loaded (the keys arrive rotated
+// already); kPfVarlen gives sequence b a.kv_lens[b] visible keys (a padded
+// batch); kPfMask hides key j from query row i unless its mask byte is nonzero.
+// FOLD: scale * log2(e) is an exact power of two and is folded into q.
+template <int D, bool CAUSAL, int FORM, bool FOLD>
 __global__ __launch_bounds__(PF_THREADS, D == 64 ? 4 : 2)  // waves per SIMD
 void prefill_bf16_kernel(PrefillArgs a) {
     using Lay = PfLay<D>;
+    using Ring = PfRing<D, FORM>;
+    constexpr bool ROPE = FORM == kPfRope, VARLEN = FORM == kPfVarlen, MASK = FORM == kPfMask;
     constexpr int KSTEPS = Lay::KSTEPS, DB = Lay::DB, DPW = Lay::DMA_PER_WAVE;
-    __shared__ __attribute__((aligned(1024))) char smem[PF_SLOTS * Lay::SLOT_BYTES];
+    constexpr int SLOTS = Ring::SLOTS, DIST = Ring::DIST, SLOT_BYTES = Ring::SLOT_BYTES;
+    __shared__ __attribute__((aligned(1024))) char smem[SLOTS * SLOT_BYTES];
 
     const int lane = threadIdx.x & 63, wave = wave_id();
     // Work-group -> (unit, query tile).  Dispatch sends work-group i to XCD
     // i % 8.  Equal-cost tiles are mapped XCD-contiguously, so the tiles of one
-    // key/value head run on one XCD and share its L2.  Causal and
-    // variable-length tiles differ in cost, so they are dealt round-robin over
-    // the units instead, longest first: with a multiple of 8 units each unit
-    // still stays on one XCD, and otherwise (one head, say) every XCD still gets
-    // an equal mix of long and short tiles.
+    // key/value head run on one XCD and share its L2.  Causal, variable-length
+    // and masked tiles differ in cost, so they are dealt round-robin over the
+    // units instead, longest first: with a multiple of 8 units each unit still
+    // stays on one XCD, and otherwise (one head, say) every XCD still gets an
+    // equal mix of long and short tiles.
     int unit, qt;
-    if (CAUSAL || VARLEN) {
+    if (CAUSAL || VARLEN || MASK) {
         unit = blockIdx.x % a.n_units;
         qt = blockIdx.x / a.n_units;
     } else {
@@ -173,15 +225,43 @@ void prefill_bf16_kernel(PrefillArgs a) {
         const int chunk = (lane % Lay::CPR) ^ (loads_v ? pf_vswz<D>(row) : pf_kswz<D>(row));
         loff[u] = (unsigned)(lane / Lay::CPR) * krb + 16u * chunk;
     }
-    // this wave's share of the loads of tile x into ring slot x % PF_SLOTS
+    // Keep-mask form: the mask tile of tile x holds rows p0 .. p0 + BM - 1, keys
+    // 64 x .. 64 x + 63 (64 bytes a row); one 1 KiB direct load moves 16 rows,
+    // and wave w moves pieces w and w + 8 of the BM / 16.  Rows at or past L
+    // read as zeros (out of the resource's range); bytes of keys at or past
+    // L_k may hold the next row's bytes, which the key bound discards.
+    const int mpieces = MASK ? a.BM / 16 : 0;
+    const int mpw = MASK ? (wave < mpieces) + (wave + 8 < mpieces) : 0;  // this wave's pieces
+    const int opw = DPW + mpw;  // this wave's direct loads per tile
+    u32x4 mrsrc = u32x4{0u, 0u, 0u, 0u};
+    unsigned moff = 0;
+    if constexpr (MASK) {
+        mrsrc = make_buffer_rsrc(a.mask + (size_t)b * (size_t)a.mask_batch,
+                                 (unsigned)((long long)L * a.mask_row));
+        const int r = 16 * wave + (lane >> 2);  // row of this lane's first piece
+        moff = (unsigned)(p0 + r) * (unsigned)a.mask_row + 16u * ((lane & 3) ^ pf_mswz(r));
+    }
+    // this wave's share of the loads of tile x into ring slot x % SLOTS
     auto issue_tile = [&](int x) {
+        char *slot = smem + (x % SLOTS) * SLOT_BYTES;
 #pragma unroll
         for (int u = 0; u < DPW; ++u) {
             const int i = i0 + u;
             const unsigned row0 = (unsigned)(x * PF_BN + i * Lay::ROWS_PER_DMA);
             dma16_to_lds_buf(rsrc, loff[u % NLO] + row0 * krb,
-                             (GQA_LDS char *)(smem + (x % PF_SLOTS) * Lay::SLOT_BYTES +
-                                              (loads_v ? Lay::TILE_BYTES : 0) + i * 1024));
+                             (GQA_LDS char *)(slot + (loads_v ? Lay::TILE_BYTES : 0) + i * 1024));
+        }
+        if constexpr (MASK) {
+            // piece i = wave + 8 u covers rows 16 i .. 16 i + 15; the swizzle of
+            // row r depends on r % 16 only, so one lane offset serves both pieces
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                if (u < mpw)
+                    dma16_to_lds_buf(mrsrc,
+                                     moff + (unsigned)(128 * u) * (unsigned)a.mask_row +
+                                         (unsigned)(x * PF_BN),
+                                     (GQA_LDS char *)(slot + 2 * Lay::TILE_BYTES +
+                                                      (wave + 8 * u) * 1024));
         }
     };
 
@@ -195,12 +275,16 @@ void prefill_bf16_kernel(PrefillArgs a) {
             const __bf16 *qp = qrow + 8 * (lane >> 5);
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
-                // fold scale * log2(e) into Q once (rounded to bf16): S^T then
-                // comes out of the MFMA already in log2 units
-                if (!ROPE) {
+                if constexpr (!ROPE) {
                     const bf16x8 raw = __builtin_bit_cast(bf16x8, load16(qp + 16 * ks));
+                    if constexpr (FOLD) {
+                        // scale * log2(e) = 2^e: q * 2^e is exact in bf16, and S^T
+                        // then comes out of the MFMA already in log2 units
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)raw[e] * a.c);
+                        for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)raw[e] * a.c);
+                    } else {
+                        qf[ks] = raw;
+                    }
                 } else {
                     // rotated columns c0 .. c0 + 7: pairs i0 .. i0 + 7 of the row,
                     // first half x0 cos - x1 sin, second half x0 sin + x1 cos
@@ -223,7 +307,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
                         const float x0 = (float)(e < 4 ? xa[2 * e] : xb[2 * e - 8]);
                         const float x1 = (float)(e < 4 ? xa[2 * e + 1] : xb[2 * e - 7]);
                         const float r = first ? x0 * cc[e] - x1 * ss[e] : x0 * ss[e] + x1 * cc[e];
-                        qf[ks][e] = (__bf16)(r * a.c);
+                        // the rotated q, rounded to bf16 once
+                        qf[ks][e] = (__bf16)(FOLD ? r * a.c : r);
                     }
                 }
             }
@@ -237,11 +322,13 @@ void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
     f32x16 s[2] = {f32x16{}, f32x16{}};
-    // -mu in every element: the C operand of the first QK MFMA of each chain,
-    // so the accumulators hold S * scale*log2(e) - mu with no VALU work.
-    // mu is the running max (0 before the first tile).
+    // Folded form: -mu in every element, the C operand of the first QK MFMA of
+    // each chain, so the accumulators hold S * scale*log2(e) - mu with no VALU
+    // work.  mu is the reference the exponentials are taken against: 0 until a
+    // row sees its first key, then the running max (raised lazily).
     f32x16 negm = f32x16{};
     float mu = 0.f;
+    const float c = a.c;
     bf16x8 pb[2][2];  // P^T of the current tile: [key block][16-key half]
     float m_run = -INFINITY, l_run = 0.f;
     const bool has_rows = pos0 < L;
@@ -270,26 +357,30 @@ void prefill_bf16_kernel(PrefillArgs a) {
         short4v hi = lds_read_tr16(reinterpret_cast<const __bf16 *>(p0 + 8 * Lay::ROW_BYTES));
         return join_tr(lo, hi);
     };
-    auto qk = [&](int j) {  // S^T = K Q^T - mu for tile j
-        const char *kt = smem + (j % PF_SLOTS) * Lay::SLOT_BYTES;
+    auto qk = [&](int j) {  // S^T = K Q^T (folded form: minus mu) for tile j
+        const char *kt = smem + (j % SLOTS) * SLOT_BYTES;
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) {
             const int ks = st >> 1, kb = st & 1;
-            s[kb] = mfma32x32x16(kread(kt, st), qf[ks], ks == 0 ? negm : s[kb]);
+            if constexpr (FOLD)
+                s[kb] = mfma32x32x16(kread(kt, st), qf[ks], ks == 0 ? negm : s[kb]);
+            else
+                s[kb] = mfma32x32x16(kread(kt, st), qf[ks], ks == 0 ? f32x16{} : s[kb]);
         }
     };
     // At d = 128 the V^T operands of the whole tile are read into registers
     // right after QK, so their LDS latency passes under the softmax; at d = 64
-    // the extra registers would cost a wave per SIMD, and PV reads them as it goes.
-    constexpr bool V_EARLY = D == 128;
+    // the extra registers would cost a wave per SIMD, and PV reads them as it goes
+    // (as it does in the keep-mask form, whose softmax needs registers for the mask).
+    constexpr bool V_EARLY = D == 128 && !MASK;
     bf16x8 vf[V_EARLY ? NSTEP : 1];
     auto vload = [&](int j) {
-        const char *vt = smem + (j % PF_SLOTS) * Lay::SLOT_BYTES + Lay::TILE_BYTES;
+        const char *vt = smem + (j % SLOTS) * SLOT_BYTES + Lay::TILE_BYTES;
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) vf[V_EARLY ? st : 0] = vread(vt, st);
     };
     auto pv = [&](int j) {  // O^T += V^T P^T for tile j
-        const char *vt = smem + (j % PF_SLOTS) * Lay::SLOT_BYTES + Lay::TILE_BYTES;
+        const char *vt = smem + (j % SLOTS) * SLOT_BYTES + Lay::TILE_BYTES;
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) {
             const int kh = st / DB, db = st % DB;
@@ -297,19 +388,44 @@ void prefill_bf16_kernel(PrefillArgs a) {
                                    pb[kh >> 1][kh & 1], acc[db]);
         }
     };
+    // Keep-mask form: this lane's mask bytes of tile j, mk[g] = the 4 bytes of
+    // keys 64 j + 8 g + 4 (lane / 32) .. + 3 for its query row (the keys of
+    // scores s[g / 4][4 (g % 4) .. + 3]).
+    unsigned mk[8];
+    auto mask_read = [&](int j) {
+        const int r = 32 * (wave % PB) + (lane & 31);  // the lane's row in the mask tile
+        const char *mrow = smem + (j % SLOTS) * SLOT_BYTES + 2 * Lay::TILE_BYTES + r * 64 +
+                           4 * (lane >> 5);
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+            // dwords 4 ch + h and 4 ch + h + 2 of the row: g = 2 ch and 2 ch + 1
+            const char *p = mrow + 16 * (ch ^ pf_mswz(r));
+            mk[2 * ch] = *reinterpret_cast<const unsigned *>(p);
+            mk[2 * ch + 1] = *reinterpret_cast<const unsigned *>(p + 8);
+        }
+    };
     // Softmax of tile j: mask, running max, P = exp2(S c - m), row sums.
-    // s holds S c - mu.  The max is raised (and O, l rescaled) only when a row's
-    // new max exceeds mu by more than TAU, or on the first tile.
-    auto softmax = [&](int j) {
+    // The max is raised (and O, l rescaled) only when a row's new max exceeds
+    // mu by more than TAU, or when the row sees its first key.
+    // full_tile (keep-mask form): every mask byte of the tile is nonzero.
+    auto softmax = [&](int j, bool full_tile) {
         const int j0 = j * PF_BN;
-        if (j0 + PF_BN > Lk || (CAUSAL && j0 + PF_BN - 1 > off + pos0)) {
+        if ((MASK && !full_tile) || j0 + PF_BN > Lk || (CAUSAL && j0 + PF_BN - 1 > off + pos0)) {
+            if constexpr (MASK) {
+                // read again here rather than kept in registers since the
+                // tile test (the empty asm keeps the two reads apart)
+                asm volatile("" ::: "memory");
+                mask_read(j);
+            }
             const int pos = pos0 + (lane & 31);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = j0 + 32 * kb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    const bool masked = key >= Lk || (CAUSAL && key > off + pos);
+                    bool masked = key >= Lk || (CAUSAL && key > off + pos);
+                    if constexpr (MASK)
+                        masked = masked || ((mk[4 * kb + (r >> 2)] >> (8 * (r & 3))) & 0xffu) == 0u;
                     s[kb][r] = masked ? -INFINITY : s[kb][r];
                 }
         }
@@ -327,31 +443,51 @@ void prefill_bf16_kernel(PrefillArgs a) {
         const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]), u1 = fmaxf(fmaxf(t[3], t[4]), t[5]);
         const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]), u3 = fmaxf(t[9], t[10]);
         const float m0 = fmaxf(fmaxf(u0, u1), fmaxf(u2, u3));
-        const float mx = fmaxf(m0, other_half(m0));  // tile row max, relative to mu
-        if (__any(m_run == -INFINITY || mx > PF_TAU)) {
-            const float m2 = m_run == -INFINITY ? mu + mx : fmaxf(m_run, mu + mx);
-            const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m2);
-            const float delta = (m2 == -INFINITY) ? 0.f : m2 - mu;
-            m_run = m2;
-            mu += delta;
-            l_run *= alpha;
+        const float mx = fmaxf(m0, other_half(m0));  // tile row max (folded: relative to mu)
+        // a row that has seen no key and sees none in this tile (a padding row,
+        // a row the mask hides) changes nothing and must not trigger the
+        // wave-wide rescale, so that it leaves the other rows' schedule alone
+        if constexpr (FOLD) {
+            if (__any((m_run == -INFINITY && mx != -INFINITY) || mx > PF_TAU)) {
+                const float m2 = m_run == -INFINITY ? mu + mx : fmaxf(m_run, mu + mx);
+                const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m2);
+                const float delta = (m2 == -INFINITY) ? 0.f : m2 - mu;
+                m_run = m2;
+                mu += delta;
+                l_run *= alpha;
 #pragma unroll
-            for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+                for (int db = 0; db < DB; ++db) acc[db] *= alpha;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) s[kb] -= delta;
+                for (int kb = 0; kb < 2; ++kb) s[kb] -= delta;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) negm[r] = -mu;
+                for (int r = 0; r < 16; ++r) negm[r] = -mu;
+            }
+        } else {
+            // the scores are raw q.k; c (> 0) keeps their order, so the tile
+            // max in log2 units is mx * c
+            const float mt = mx * c;
+            if (__any((m_run == -INFINITY && mt != -INFINITY) || mt > mu + PF_TAU)) {
+                const float m2 = fmaxf(m_run, mt);  // -inf while nothing is visible
+                const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m2);
+                m_run = m2;
+                mu = (m2 == -INFINITY) ? mu : m2;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+            }
         }
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        // folded form: s holds S c - mu; else s holds S and one fma gives S c - mu
+        auto arg = [&](float v) { return FOLD ? v : fmaf(v, c, -mu); };
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                 for (int i = 0; i < 8; i += 2) {
-                    const bf16x2 p2 = {(__bf16)fast_exp2(s[kb][8 * hh + i]),
-                                       (__bf16)fast_exp2(s[kb][8 * hh + i + 1])};
+                    const bf16x2 p2 = {(__bf16)fast_exp2(arg(s[kb][8 * hh + i])),
+                                       (__bf16)fast_exp2(arg(s[kb][8 * hh + i + 1]))};
                     pb[kb][hh][i] = p2[0];
                     pb[kb][hh][i + 1] = p2[1];
                     // row sum of the bf16-rounded P that the PV product uses
@@ -362,9 +498,9 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // V rows past the sequence end meet P = 0 and must be finite: zero the V
     // halves of the ring once, in case an out-of-range load leaves its LDS
     // bytes untouched.
-    for (int i = threadIdx.x; i < PF_SLOTS * Lay::TILE_BYTES / 16; i += PF_THREADS) {
+    for (int i = threadIdx.x; i < SLOTS * Lay::TILE_BYTES / 16; i += PF_THREADS) {
         const int sl = i / (Lay::TILE_BYTES / 16), off = i % (Lay::TILE_BYTES / 16);
-        store16_lds(smem + sl * Lay::SLOT_BYTES + Lay::TILE_BYTES + 16 * off, u32x4{0u, 0u, 0u, 0u});
+        store16_lds(smem + sl * SLOT_BYTES + Lay::TILE_BYTES + 16 * off, u32x4{0u, 0u, 0u, 0u});
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     block_barrier();
@@ -372,29 +508,51 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // loads read zeros without touching memory
     issue_tile(0);
 #pragma unroll
-    for (int x = 1; x < PF_DIST; ++x)
+    for (int x = 1; x < DIST; ++x)
         if (x < ntiles) issue_tile(x);
-    // tile 0 has landed once at most the loads of tiles 1 .. PF_DIST - 1 are pending
-    if (ntiles >= 3) wait_vmcnt<2 * DPW>();
-    else if (ntiles == 2) wait_vmcnt<DPW>();
-    else wait_vmcnt<0>();
+    // Tile x has landed once at most the loads issued after it are pending:
+    // those of tiles x + 1 .. x + DIST - 1 that exist, opw a tile.  Without the
+    // mask every wave issues DPW loads a tile and the counts are immediates.
+    auto wait_tile = [&](int pending) {
+        if constexpr (MASK) {
+            wait_vmcnt_rt(pending * opw);
+        } else {
+            static_assert(DIST == 3, "the immediate waits assume a prefetch distance of 3");
+            if (pending >= 2) wait_vmcnt<2 * DPW>();
+            else if (pending == 1) wait_vmcnt<DPW>();
+            else wait_vmcnt<0>();
+        }
+    };
+    wait_tile(min(ntiles, DIST) - 1);
     block_barrier();
     for (int j = 0; j < ntiles; ++j) {
-        if (j + PF_DIST < ntiles) issue_tile(j + PF_DIST);
+        if (j + DIST < ntiles) issue_tile(j + DIST);
         if (active(j)) {
-            qk(j);
-            if (V_EARLY) {
-                vload(j);
-                __builtin_amdgcn_sched_barrier(0);
+            bool go = true, full = true;
+            if constexpr (MASK) {
+                // skip a tile whose mask hides every key from this wave's rows
+                mask_read(j);
+                unsigned any = 0, zero = 0;
+#pragma unroll
+                for (int g = 0; g < 8; ++g) {
+                    any |= mk[g];
+                    zero |= (mk[g] - 0x01010101u) & ~mk[g] & 0x80808080u;  // a zero byte
+                }
+                go = __any(any != 0u);
+                full = !__any(zero != 0u);
             }
-            softmax(j);
-            pv(j);
+            if (go) {
+                qk(j);
+                if (V_EARLY) {
+                    vload(j);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                softmax(j, full);
+                pv(j);
+            }
         }
-        // tile j + 1 must have landed; tiles j + 2 .. j + PF_DIST may be pending
-        const int pending = min(ntiles - 1, j + PF_DIST) - (j + 1);
-        if (pending >= 2) wait_vmcnt<2 * DPW>();
-        else if (pending == 1) wait_vmcnt<DPW>();
-        else wait_vmcnt<0>();
+        // tile j + 1 must have landed; tiles j + 2 .. j + DIST may be pending
+        wait_tile(max(min(ntiles - 1, j + DIST) - (j + 1), 0));
         block_barrier();
     }
 
@@ -403,8 +561,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // writes them back as whole rows (16-byte lanes, consecutive within a
     // row), not as the accumulators' scattered 8-byte pieces of 32 rows.
     const float lt = l_run + other_half(l_run);
-    // no visible key (only a zero-length sequence): a zero row
-    const float inv = (!VARLEN || lt > 0.f) ? 1.f / lt : 0.f;
+    // no visible key (a zero-length sequence, a fully masked row): a zero row
+    const float inv = (!(VARLEN || MASK) || lt > 0.f) ? 1.f / lt : 0.f;
     // the lane id passes an empty asm, so the addresses below are computed
     // here and not kept in registers across the tile loop
     int le = lane;
@@ -444,32 +602,32 @@ void prefill_bf16_kernel(PrefillArgs a) {
     }
 }
 
+template <int D, bool C>
+void launch_form(const PrefillArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
+    if (a.rope_cos != nullptr)
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, C, kPfRope, false>), grid, block, 0, stream, a);
+    else if (a.kv_lens != nullptr)
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, C, kPfVarlen, false>), grid, block, 0, stream,
+                           a);
+    else if (a.mask != nullptr)
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, C, kPfMask, false>), grid, block, 0, stream, a);
+    else if (a.fold)
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, C, kPfPlain, true>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, C, kPfPlain, false>), grid, block, 0, stream, a);
+}
+
 }  // namespace
 
 int launch_prefill_bf16(const PrefillArgs &a, int d, bool causal, hipStream_t stream) {
     dim3 grid(a.n_units * a.n_qtiles), block(PF_THREADS);
-    // forms: plain, rotary (q rotated at load), variable length
-    const int form = a.rope_cos != nullptr ? 1 : a.kv_lens != nullptr ? 2 : 0;
-#define GQA_PF_LAUNCH(D_, C_)                                                                  \
-    do {                                                                                       \
-        if (form == 1)                                                                         \
-            hipLaunchKernelGGL((prefill_bf16_kernel<D_, C_, true, false>), grid, block, 0,     \
-                               stream, a);                                                     \
-        else if (form == 2)                                                                    \
-            hipLaunchKernelGGL((prefill_bf16_kernel<D_, C_, false, true>), grid, block, 0,     \
-                               stream, a);                                                     \
-        else                                                                                   \
-            hipLaunchKernelGGL((prefill_bf16_kernel<D_, C_, false, false>), grid, block, 0,    \
-                               stream, a);                                                     \
-    } while (0)
     if (d == 128) {
-        if (causal) GQA_PF_LAUNCH(128, true);
-        else GQA_PF_LAUNCH(128, false);
+        if (causal) launch_form<128, true>(a, grid, block, stream);
+        else launch_form<128, false>(a, grid, block, stream);
     } else {
-        if (causal) GQA_PF_LAUNCH(64, true);
-        else GQA_PF_LAUNCH(64, false);
+        if (causal) launch_form<64, true>(a, grid, block, stream);
+        else launch_form<64, false>(a, grid, block, stream);
     }
-#undef GQA_PF_LAUNCH
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -8,6 +8,8 @@
 // head floor(h / G): "Modern LLM architecture (1): GQA and RMSNorm", §2.3).
 // The softmax is the exact running-max form: per 32-key tile, new max, rescale
 // of the running sum and output, then accumulation of exp2(s - m) v.
+// Key j is hidden from a row past the sequence's length (kv_lens), above the
+// causal diagonal, or where the keep-mask byte of (row, j) is zero.
 #include "gqa_device.h"
 #include "gqa_kernels.h"
 
@@ -44,6 +46,11 @@ __global__ __launch_bounds__(PF32_THREADS) void prefill_f32_kernel(PrefillArgs a
     const float *kg = static_cast<const float *>(a.k) + ((size_t)b * Lt * a.h_kv + kvh) * D;
     const float *vg = static_cast<const float *>(a.v) + ((size_t)b * Lt * a.h_kv + kvh) * D;
     const size_t kv_row = (size_t)a.h_kv * D;
+    // this row's keep-mask bytes (keep-mask form), keys 0 .. Lk - 1
+    const uint8_t *mrow = a.mask && pos < L
+                              ? a.mask + (size_t)b * (size_t)a.mask_batch +
+                                    (size_t)pos * (size_t)a.mask_row
+                              : nullptr;
 
     float qv[D], ov[D];
     if (pos < L) {
@@ -84,6 +91,7 @@ __global__ __launch_bounds__(PF32_THREADS) void prefill_f32_kernel(PrefillArgs a
             for (int cc = 0; cc < D; ++cc) dot = fmaf(qv[cc], ksm[kk * D + cc], dot);
             int key = j0 + kk;
             bool masked = key >= Lk || (CAUSAL && key > off + pos);
+            if (a.mask) masked = masked || mrow == nullptr || mrow[key] == 0;
             s[kk] = masked ? -INFINITY : dot;
             mx = fmaxf(mx, s[kk]);
         }

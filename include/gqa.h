@@ -66,11 +66,14 @@ enum {
  * Limits: B * h_q * L and B * h_kv * L must each fit in 2^31 elements of d;
  * for GQA_BF16 also L * h_kv * d * 2 (the bytes spanned by one sequence's
  * key or value rows) must be below 2^32.  Larger calls return GQA_ERR_SIZE.
- * Precision (GQA_BF16): scale * log2(e) is folded into q, which is rounded to
- * bf16 once, and the probabilities are rounded to bf16 before the product
- * with v; accumulation and the softmax statistics are fp32.  A score s thus
- * carries a relative error of about 2^-9, which matters only for |s| of many
- * tens (in log2 units) with near ties; a power-of-two scale * log2(e) is exact.
+ * Precision (GQA_BF16): q and k enter the products exactly as given; the
+ * scores are accumulated in fp32 and multiplied by scale * log2(e) in fp32
+ * (one fused multiply-add with the running max), so a score of any size is
+ * exact to fp32 rounding.  When scale * log2(e) is an exact power of two it is
+ * folded into q instead (exact in bf16 unless q * scale * log2(e) leaves the
+ * normal range).  The probabilities are rounded to bf16 before the product
+ * with v, and the row sums are taken over the rounded values; accumulation
+ * and the softmax statistics are fp32.
  */
 gqa_status gqa_prefill(const void *q, const void *k, const void *v, void *o, int B, int L,
                        int h_q, int h_kv, int d, gqa_dtype dt, int causal, float scale,
@@ -115,6 +118,36 @@ gqa_status gqa_prefill_varlen(const void *q, const void *k, const void *v, void 
                               gqa_dtype dt, int causal, float scale, void *hip_stream);
 
 /*
+ * Prefill with a keep-mask: key j is visible to query row i of sequence b only
+ * if its mask byte is nonzero, the masked_fill(mask == 0, -inf) convention of
+ * "Implementing GQA from scratch in PyTorch", §3.3 and of the attn_mask
+ * argument in "Modern LLM architecture (1): GQA and RMSNorm", §2.3, combined
+ * with the causal mask when causal != 0.  The mask is shared by all heads.
+ *   q, o : [B, L_q, h_q, d]; k, v : [B, L_k, h_kv, d] (1 <= L_q <= L_k), as
+ *          gqa_prefill_chunk: query row i sits at position L_k - L_q + i, and
+ *          causally sees keys 0 .. L_k - L_q + i.
+ *   mask : device bytes, 16-byte aligned; the byte of (b, i, j) is
+ *          mask[b * mask_batch_stride + i * mask_row_stride + j].
+ *   mask_row_stride   : bytes between rows, a multiple of 16 and >= L_k, with
+ *          L_q * mask_row_stride below 2^32 (a dense [B, L_q, L_k] mask whose
+ *          L_k is not a multiple of 16 is padded per row to one that is).
+ *   mask_batch_stride : bytes between sequences, a multiple of 16; 0 shares one
+ *          [L_q, L_k] mask across the batch.  The caller's buffer must hold
+ *          (B - 1) * mask_batch_stride + L_q * mask_row_stride bytes; the
+ *          bytes of a row past L_k are read but ignored.
+ * A row with no visible key is zero.  Masked keys receive weight exactly 0, so
+ * every key/value row must be finite (0 times a NaN would still be NaN).
+ * With every mask byte nonzero the result equals gqa_prefill_chunk.
+ * Other arguments, limits and errors as gqa_prefill_chunk (both dtypes); a
+ * NULL mask gives GQA_ERR_NULL_POINTER, a misaligned one GQA_ERR_ALIGNMENT and
+ * strides breaking the rules above GQA_ERR_SIZE.
+ */
+gqa_status gqa_prefill_mask(const void *q, const void *k, const void *v, const uint8_t *mask,
+                            long long mask_row_stride, long long mask_batch_stride, void *o,
+                            int B, int L_q, int L_k, int h_q, int h_kv, int d, gqa_dtype dt,
+                            int causal, float scale, void *hip_stream);
+
+/*
  * Prefill with rotary position embedding: q and k are rotated, then the
  * prefill above runs on the rotated q, k and the unrotated v ("Attention in
  * Qwen, DeepSeek and LLaMA3", §1, apply_rotary_pos_emb).  For a row x at
@@ -132,8 +165,9 @@ gqa_status gqa_prefill_varlen(const void *q, const void *k, const void *v, void 
  *          the attention reads the keys from here.  It must not overlap k
  *          (k_rot == k returns GQA_ERR_SIZE).
  * The keys are rotated by one small kernel (fp32 arithmetic, one rounding to
- * bf16); q is rotated in fp32 as the prefill kernel loads it, then scaled and
- * rounded to bf16 once, as in gqa_prefill.  Two kernels run on `hip_stream`.
+ * bf16); q is rotated in fp32 as the prefill kernel loads it and rounded to
+ * bf16 once; the scores are then scaled in fp32 as in gqa_prefill.  Two
+ * kernels run on `hip_stream`.
  */
 gqa_status gqa_prefill_rope(const void *q, const void *k, const void *v, const float *cos_table,
                             const float *sin_table, void *o, void *k_rot, int B, int L, int h_q,

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("gqa_prefill", "gqa_prefill_chunk", "gqa_decode", "gqa_decode_append",
               "gqa_decode_token_major", "gqa_decode_paged", "gqa_prefill_rope",
-              "gqa_prefill_varlen", "gqa_decode_append_rope", "gqa_decode_rope_workspace_bytes",
+              "gqa_prefill_varlen", "gqa_prefill_mask", "gqa_decode_append_rope",
+              "gqa_decode_rope_workspace_bytes",
               "gqa_decode_workspace_bytes",
               "gqa_decode_default_splits", "gqa_status_string"):
         assert n in names
@@ -126,6 +127,35 @@ def test_prefill_varlen_without_a_gpu_reports_the_device():
         pytest.skip("a GPU is present")
     assert varlen_status(kl=A + 4) == DEVICE
     assert varlen_status(dt=0) == DEVICE  # fp32 is served too
+
+
+def mask_status(q=A, k=A, v=A, m=A, mr=64, mb=0, o=A, B=2, Lq=16, Lk=64, h_q=8, h_kv=2, d=64,
+                dt=1, causal=1, scale=0.125):
+    return gqa.lib().gqa_prefill_mask(q, k, v, m, mr, mb, o, B, Lq, Lk, h_q, h_kv, d, dt, causal,
+                                      ctypes.c_float(scale), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(m=None), NULLP), (dict(q=None), NULLP), (dict(m=A + 8), ALIGN), (dict(k=MIS), ALIGN),
+    # the row stride must cover L_k and be a multiple of 16; the batch stride a
+    # non-negative multiple of 16
+    (dict(mr=48), SIZE), (dict(mr=72), SIZE), (dict(mb=-16), SIZE), (dict(mb=8), SIZE),
+    # one sequence's mask rows must be addressable with 32-bit offsets
+    (dict(Lq=1 << 16, Lk=1 << 16, mr=1 << 16), SIZE),
+    (dict(Lq=65, Lk=64), SIZE), (dict(B=0), SIZE), (dict(h_q=8, h_kv=3), HEADS),
+    (dict(d=96), HEADDIM), (dict(dt=3), DTYPE), (dict(scale=-1.0), SIZE),
+])
+def test_prefill_mask_rejects_bad_arguments(kw, status):
+    assert mask_status(**kw) == status
+
+
+def test_prefill_mask_without_a_gpu_reports_the_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert mask_status() == DEVICE
+    assert mask_status(mb=16 * 64, dt=0) == DEVICE   # fp32, one mask per sequence
+    assert mask_status(Lq=64, Lk=64, mr=80) == DEVICE  # a padded row stride
 
 
 def append_rope_status(q=A, kn=A, vn=A, kc=A, vc=A, sl=A, c=A, s=A, o=A, B=4, h_q=32, h_kv=8,
