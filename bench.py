@@ -2,20 +2,25 @@
 """Benchmark of the grouped-query attention core on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--extra-prefill NAME,NAME,...|none]
                     [--decode-workload NAME|none] [--append-workload NAME|none]
-                    [--paged-workload NAME|none]
-                    [--no-cpu-baseline]
+                    [--paged-workload NAME|none] [--no-cpu-baseline]
 
 Prints ONE JSON line on stdout.  A step is one call of the prefill entry point
-on the selected workload (default: the pages' worked example, B=32, L=1024,
-8 query heads over 4 key/value heads, d=64, bf16, non-causal).  Before the W warmup
-steps the same step runs untimed for --settle-seconds (default 0.5 s) so the GPU
-reaches its working clocks; then K steps are timed back to back between two
-device synchronisations; ``value`` is the
-algorithmic TFLOP/s of that timed region (4 * B * h_q * d * visible (query,
-key) pairs per step; causal counts L(L+1)/2 pairs per head).  K more steps
-follow, each between two HIP events on the launch stream, for the kernel's
-average duration in ``roofline``.
+on the selected workload (default: the long-context shape, B=1, L=32768, 64
+query heads over 8 key/value heads, d=128, bf16, causal: the largest of the
+named configurations that fits one GPU).  Before the W warmup steps the same
+step runs untimed for --settle-seconds (default 0.5 s) so the GPU reaches its
+working clocks; then K steps are timed back to back between two device
+synchronisations; ``value`` is the algorithmic TFLOP/s of that timed region
+(4 * B * h_q * d * visible (query, key) pairs per step; causal counts
+L(L+1)/2 pairs per head).  K more steps follow, each between two HIP events on
+the launch stream, for the kernel's average duration in ``roofline``.
+
+The other prefill workloads named by --extra-prefill (default: the pages'
+worked example, the Llama-2-shaped causal layer and the packed-documents
+keep-mask prefill) are timed the same way and reported under
+``prefill_extra``, each with its own ``roofline``.
 
 The decode entry point is timed next on its own workload (64 sequences, 32
 query heads over 8 key/value heads, d=128, S=8192, lengths U{1024..8192}).  A
@@ -35,10 +40,14 @@ inputs in a shuffled pool of 64-row pages) is reported under ``decode_paged``.
 average duration measured with HIP events on the launch stream; ``traffic``
 comes from the rocprofv3 HBM counter summary under ``profiles/`` when that
 summary was taken on the current kernel source, else null.  ``cpu_baseline``
-times the fp64 CPU oracle on a bounded sample of the same workload.
+times the fp64 CPU oracle on a bounded sample of the same workload's rows.
 
-With ``--copy-calibration`` it instead runs a plain 1 GiB device copy (for
-scaling the HBM byte counters) and prints nothing else.
+Other modes (each prints its own output and nothing else):
+  --copy-calibration      a plain 1 GiB device copy, for scaling the HBM counters
+  --trace-summary CSV     per (kernel, grid size) statistics of the last
+                          --trace-last dispatches in a rocprofv3 kernel trace
+  --pmc-summary CSV       per (kernel, grid size) mean of each counter in a
+                          rocprofv3 counter collection
 """
 from __future__ import annotations
 
@@ -83,7 +92,22 @@ def varlen_pairs(L: int, n: int, causal: bool) -> int:
     return n * (n + 1) // 2 + (L - n) * n
 
 
-def prefill_flops(w, kv_lens=None) -> float:
+def mask_pairs(mask, causal: bool) -> int:
+    """(query, key) pairs a keep-mask [B, L_q, L_k] leaves visible (and the
+    causal bound, query row i seeing keys up to L_k - L_q + i)."""
+    import torch
+    keep = mask != 0
+    if causal:
+        Lq, Lk = keep.shape[1], keep.shape[2]
+        i = torch.arange(Lq)[:, None]
+        j = torch.arange(Lk)[None, :]
+        keep = keep & (j <= Lk - Lq + i)[None]
+    return int(keep.sum())
+
+
+def prefill_flops(w, kv_lens=None, mask=None) -> float:
+    if w.path == "prefill_mask":
+        return 4.0 * w.h_q * w.d * mask_pairs(mask, w.causal)
     if w.path == "prefill_varlen":
         pairs = sum(varlen_pairs(w.L, int(n), w.causal) for n in kv_lens)
         return 4.0 * w.h_q * w.d * pairs
@@ -189,12 +213,18 @@ def bench_prefill(w, steps, warmup, settle_s=0.0):
     q, k, v = ins[:3]
     out = torch.empty_like(q)
 
-    kv_lens = None
+    kv_lens = mask_cpu = None
     if w.path == "prefill_varlen":
         kv_lens = ins[3]
 
         def step():
             gqa.prefill_varlen(q, k, v, kv_lens, causal=w.causal, scale=w.scale, out=out)
+    elif w.path == "prefill_mask":
+        mask_cpu = wl.workload_inputs(w)[3]
+        mask = ins[3]
+
+        def step():
+            gqa.prefill_mask(q, k, v, mask, causal=w.causal, scale=w.scale, out=out)
     elif w.path == "prefill_rope":  # two kernels: the key rotation, then the prefill
         cos, sin = ins[3:]
         k_rot = torch.empty_like(k)
@@ -222,7 +252,7 @@ def bench_prefill(w, steps, warmup, settle_s=0.0):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     _, ev = time_launches(step, steps)
-    flops = prefill_flops(w, None if kv_lens is None else kv_lens.tolist())
+    flops = prefill_flops(w, None if kv_lens is None else kv_lens.tolist(), mask_cpu)
     avg_ms = sum(ev) / len(ev)
     return {
         "value": flops * steps / wall / 1e12,
@@ -295,68 +325,88 @@ def bench_decode(w, steps, warmup):
     }
 
 
-def cpu_baseline(w, budget_s=12.0):
-    """The fp64 oracle timed on about budget_s seconds of the workload's own rows.
+def host_cpu():
+    """(CPU model, logical CPUs, CPUs this process may run on)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return model, os.cpu_count(), avail
 
-    Whole batch elements are run (all heads, all positions); when the whole
-    workload takes less than the budget it is run repeatedly and the mean rate
-    is reported.
-    """
+
+def cpu_baseline(w, budget_s=12.0):
+    """The fp64 oracle timed on a seeded sample of the workload's own query rows
+    (b, i, h), each against all of its visible keys, the sample sized to about
+    budget_s seconds; the rate counts 4 d flops per visible (row, key) pair."""
+    import numpy as np
     import gqa_workloads as wl
     import oracle
     ins = wl.workload_inputs(w)
-    qd, kd, vd = (t.double().numpy() for t in ins[:3])
-
-    if w.path == "prefill_chunk":
-        return _cpu_baseline_chunk(w, qd, kd, vd, budget_s)
-
-    def run(nb):
-        t0 = time.perf_counter()
-        if w.path == "prefill_rope":
-            oracle.prefill_rope(qd[:nb], kd[:nb], vd[:nb], ins[3].double().numpy(),
-                                ins[4].double().numpy(), causal=w.causal, scale=w.scale)
-        elif w.path == "prefill_varlen":
-            oracle.prefill_varlen(qd[:nb], kd[:nb], vd[:nb], ins[3][:nb].numpy(), causal=w.causal,
-                                  scale=w.scale)
-        else:
-            oracle.prefill(qd[:nb], kd[:nb], vd[:nb], causal=w.causal, scale=w.scale)
-        return time.perf_counter() - t0
-
-    t1 = run(1)
-    nb = int(max(1, min(w.B, round(budget_s / max(t1, 1e-3)))))
-    reps, total = 0, 0.0
-    while total < budget_s or reps == 0:
-        total += run(nb) if (nb > 1 or reps > 0) else t1
-        reps += 1
-    if w.path == "prefill_varlen":
-        work = 4.0 * w.h_q * w.d * sum(varlen_pairs(w.L, int(n), w.causal) for n in ins[3][:nb])
+    q, k, v = ins[:3]
+    kd, vd = k.double().numpy(), v.double().numpy()
+    Lk = w.Lk if w.path == "prefill_chunk" else w.L
+    first = Lk - w.L  # causal: query row i sees keys 0 .. first + i
+    if w.path == "prefill_rope":
+        cos, sin = ins[3].double().numpy(), ins[4].double().numpy()
+        qsrc = oracle.rope(q.double().numpy(), cos, sin)
+        kd = oracle.rope(kd, cos, sin)
     else:
-        work = prefill_flops(w) / w.B * nb
-    return {"value": work * reps / total / 1e12, "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle", "seconds": total,
-            "sample": f"{nb} of {w.B} batch elements of {w.name} (all {w.h_q} heads x {w.L} "
-                      f"positions each), run {reps} time(s), fp64"}
+        qsrc = None
+    mask = ins[3].numpy() if w.path == "prefill_mask" else None
+    lens = ins[3].numpy() if w.path == "prefill_varlen" else None
 
+    def visible(b, i):
+        n = first + i + 1 if w.causal else Lk
+        if lens is not None:
+            n = min(n, int(lens[b]))
+        if mask is not None:
+            n = int((mask[b, i, :n] != 0).sum())
+        return n
 
-def _cpu_baseline_chunk(w, qd, kd, vd, budget_s):
-    """The oracle on the newest m query rows of the chunk against all L_k keys
-    (the same form of work), m sized to about budget_s seconds."""
-    import oracle
-
-    def run(m):
+    def run(n):
+        rows = wl.sample_rows(n, w.B, w.L, w.h_q, w.seed + 17)
+        idx = np.asarray(rows)
+        if qsrc is not None:
+            qr = qsrc[idx[:, 0], idx[:, 1], idx[:, 2]]
+        else:
+            qr = q[idx[:, 0], idx[:, 1], idx[:, 2]].double().numpy()
         t0 = time.perf_counter()
-        oracle.prefill_cached(qd[:1, -m:], kd[:1], vd[:1], causal=w.causal, scale=w.scale)
-        return time.perf_counter() - t0
+        if w.path == "prefill_chunk":
+            oracle.prefill_cached_rows(qr, rows, kd, vd, w.h_q, w.L, w.causal, w.scale)
+        elif w.path == "prefill_varlen":
+            oracle.prefill_varlen_rows(qr, rows, kd, vd, lens, w.h_q, w.causal, w.scale)
+        elif w.path == "prefill_mask":
+            oracle.prefill_mask_rows(qr, rows, kd, vd, mask, w.h_q, w.causal, w.scale)
+        else:
+            oracle.prefill_rows(qr, rows, kd, vd, w.h_q, causal=w.causal, scale=w.scale)
+        t = time.perf_counter() - t0
+        pairs = sum(visible(b, i) for b, i, _ in rows)
+        return t, len(rows), pairs
 
-    m0 = min(16, w.L)
-    t1 = run(m0)
-    m = int(max(m0, min(w.L, round(m0 * budget_s / max(t1, 1e-3)))))
-    t = run(m) if m != m0 else t1
-    flops = 4.0 * w.h_q * w.d * visible_pairs(m, w.Lk, w.causal)
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": t,
-            "sample": f"the newest {m} of the {w.L} query positions of one sequence of {w.name} "
-                      f"against all {w.Lk} keys, all {w.h_q} heads, fp64"}
+    # two calibration samples separate the fixed cost of a call (the repeated
+    # key/value slab of every head the sample touches) from the cost per row
+    total_rows = w.B * w.L * w.h_q
+    t1, n1, _ = run(min(64, total_rows))
+    t2, n2, _ = run(min(512, total_rows))
+    per_row = max((t2 - t1) / max(n2 - n1, 1), 1e-7)
+    fixed = max(t2 - per_row * n2, 0.0)
+    n = int(max(n2, min(total_rows, (budget_s - fixed) / per_row)))
+    t, n, pairs = run(n)
+    model, ncpu, avail = host_cpu()
+    return {"value": 4.0 * w.d * pairs / t / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle", "seconds": t,
+            "cpu_model": model, "nproc": ncpu, "cpus_available": avail,
+            "sample": f"{n} seeded query rows (b, i, h) of {w.name} ({total_rows} in all), each "
+                      f"against all of its visible keys ({pairs} (row, key) pairs), fp64"}
 
 
 def copy_calibration():
@@ -371,16 +421,95 @@ def copy_calibration():
     log(f"copied {n} bytes 3 times")
 
 
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _grid(row):
+    """Grid size (work-items) of a rocprofv3 CSV row, whichever columns it has."""
+    if row.get("Grid_Size"):
+        return int(float(row["Grid_Size"]))
+    n = 1
+    for ax in ("X", "Y", "Z"):
+        x = row.get(f"Grid_Size_{ax}")
+        if x:
+            n *= int(float(x))
+    return n
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "") if len(name) > 90 else name
+
+
+def trace_summary(path, last):
+    """Markdown table of a rocprofv3 kernel trace: per (kernel, grid size), the
+    count, average, minimum and maximum duration of its last `last` dispatches
+    (the timed region of a bench run; earlier ones ran while the clocks rose)."""
+    groups = {}
+    for r in _csv_rows(path):
+        key = (r["Kernel_Name"], _grid(r))
+        groups.setdefault(key, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    print(f"| kernel | grid (work-items) | dispatches in trace | dispatches summarised | "
+          f"average us | min us | max us |")
+    print("|---|---|---|---|---|---|---|")
+    for (name, grid), ds in sorted(groups.items(), key=lambda kv: min(x[0] for x in kv[1])):
+        ds.sort()
+        tail = ds[-last:] if last > 0 else ds
+        dur = [(e - b) / 1e3 for b, e in tail]
+        print(f"| `{_short(name)}` | {grid} | {len(ds)} | {len(tail)} | "
+              f"{sum(dur) / len(dur):.3f} | {min(dur):.3f} | {max(dur):.3f} |")
+
+
+def pmc_summary(path):
+    """Markdown table of a rocprofv3 counter collection: per (kernel, grid
+    size, counter), the mean value per dispatch and the number of dispatches."""
+    groups = {}
+    for r in _csv_rows(path):
+        key = (r["Kernel_Name"], _grid(r), r["Counter_Name"])
+        groups.setdefault(key, {}).setdefault(r.get("Dispatch_Id", len(groups)), 0.0)
+        groups[key][r.get("Dispatch_Id")] += float(r["Counter_Value"])
+    print("| kernel | grid (work-items) | counter | mean per dispatch | dispatches |")
+    print("|---|---|---|---|---|")
+    for (name, grid, ctr), per in sorted(groups.items()):
+        vals = list(per.values())
+        print(f"| `{_short(name)}` | {grid} | {ctr} | {sum(vals) / len(vals):.1f} | {len(vals)} |")
+
+
+def prefill_line(w, pf):
+    """The measured figures of one prefill workload: throughput and roofline."""
+    peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+    achieved = pf["flops_per_launch"] / (pf["kernel_ms_avg"] * 1e-3) / 1e12
+    cfg = {"workload": w.name, "path": w.path, "B": w.B, "L": w.L, "h_q": w.h_q,
+           "h_kv": w.h_kv, "d": w.d, "causal": w.causal, "scale": w.scale}
+    if w.path == "prefill_chunk":
+        cfg["L_k"] = w.Lk
+    roof = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": achieved,
+            "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+            "traffic": recorded_traffic("prefill", w.name),
+            "flops_per_launch": pf["flops_per_launch"],
+            "kernel_ms_avg": pf["kernel_ms_avg"], "kernel_ms_min": pf["kernel_ms_min"]}
+    log(f"prefill {w.name}: {pf['value']:.1f} TFLOP/s wall, kernel avg "
+        f"{pf['kernel_ms_avg']:.4f} ms ({achieved:.1f} TFLOP/s, {100 * achieved / peak:.1f}% "
+        f"of peak)")
+    return cfg, roof
+
+
+PREFILL_PATHS = ("prefill", "prefill_chunk", "prefill_rope", "prefill_varlen", "prefill_mask")
+DEFAULT_EXTRA = "worked_example_prefill_bf16,llama2_7b_prefill_bf16,document_masked_prefill_bf16"
+
+
 def main(argv=None):
     import gqa_workloads as wl
+    prefill_names = [n for n in wl.WORKLOAD_ORDER if wl.WORKLOADS[n].path in PREFILL_PATHS]
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="worked_example_prefill_bf16",
-                    choices=[n for n in wl.WORKLOAD_ORDER
-                             if wl.WORKLOADS[n].path in ("prefill", "prefill_chunk",
-                                                         "prefill_rope", "prefill_varlen")])
+    ap.add_argument("--workload", default="long_context_prefill_bf16", choices=prefill_names)
+    ap.add_argument("--extra-prefill", default=DEFAULT_EXTRA,
+                    help="comma-separated prefill workloads timed after the headline, or none")
     ap.add_argument("--decode-workload", default="batched_decode_bf16",
                     choices=["none"] + [n for n in wl.WORKLOAD_ORDER
                                         if wl.WORKLOADS[n].path == "decode"])
@@ -395,7 +524,21 @@ def main(argv=None):
                     help="untimed runs of the step before the warmup, to reach working clocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--trace-summary", metavar="CSV")
+    ap.add_argument("--trace-last", type=int, default=0)
+    ap.add_argument("--pmc-summary", metavar="CSV")
     args = ap.parse_args(argv)
+
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.trace_last)
+        return 0
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return 0
+    extra = [] if args.extra_prefill in ("", "none") else args.extra_prefill.split(",")
+    for n in extra:
+        if n not in prefill_names:
+            ap.error(f"--extra-prefill: unknown prefill workload {n}")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -414,8 +557,8 @@ def main(argv=None):
     w = wl.WORKLOADS[args.workload]
     log(f"prefill {w.name}: {w.description}; steps {args.steps} warmup {args.warmup}")
     pf = bench_prefill(w, args.steps, args.warmup, args.settle_seconds)
-    peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
-    achieved = pf["flops_per_launch"] / (pf["kernel_ms_avg"] * 1e-3) / 1e12
+    cfg, roof = prefill_line(w, pf)
+    cfg["parallelism"] = "single GPU"
     line = {
         "metric": METRIC,
         "value": pf["value"],
@@ -430,18 +573,19 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic: seeded i.i.d. normal draws cast to the compute dtype (no dataset)",
-        "config": {"workload": w.name, "path": w.path, "B": w.B, "L": w.L, "h_q": w.h_q,
-                   "h_kv": w.h_kv, "d": w.d, "causal": w.causal, "scale": w.scale,
-                   "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": achieved,
-                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": recorded_traffic("prefill", w.name),
-                     "kernel_ms_avg": pf["kernel_ms_avg"], "kernel_ms_min": pf["kernel_ms_min"]},
+        "config": cfg,
+        "roofline": roof,
     }
-    if w.path == "prefill_chunk":
-        line["config"]["L_k"] = w.Lk
-    log(f"prefill: {pf['value']:.1f} TFLOP/s wall, kernel avg {pf['kernel_ms_avg']:.4f} ms "
-        f"({achieved:.1f} TFLOP/s, {100 * achieved / peak:.1f}% of peak)")
+    if extra:
+        line["prefill_extra"] = {}
+    for name in extra:
+        ew = wl.WORKLOADS[name]
+        log(f"prefill {ew.name}: {ew.description}; steps {args.steps}")
+        epf = bench_prefill(ew, args.steps, args.warmup, args.settle_seconds)
+        ecfg, eroof = prefill_line(ew, epf)
+        line["prefill_extra"][name] = {"value": epf["value"], "unit": "TFLOP/s",
+                                       "ms_per_step": epf["ms_per_step"], "dtype": ew.dtype,
+                                       "config": ecfg, "roofline": eroof}
     if args.decode_workload != "none":
         dw = wl.WORKLOADS[args.decode_workload]
         log(f"decode {dw.name}: {dw.description}; steps {args.decode_steps}")

@@ -36,8 +36,8 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    # "prefill", "prefill_chunk", "prefill_rope", "prefill_varlen", "decode",
-    # "decode_append" or "decode_paged"
+    # "prefill", "prefill_chunk", "prefill_rope", "prefill_varlen", "prefill_mask",
+    # "decode", "decode_append" or "decode_paged"
     path: str
     dtype: str  # "f32" or "bf16"
     B: int
@@ -50,7 +50,8 @@ class Workload:
     causal: bool = False
     std: float = 1.0
     # decode: inclusive [lo, hi] of the lengths (decode_append: before the append);
-    # prefill_varlen: of the valid lengths in the padded batch
+    # prefill_varlen: of the valid lengths in the padded batch; prefill_mask: of
+    # the packed documents' lengths
     seqlen_range: tuple = (0, 0)
     seed: int = 0
     page_size: int = 0  # decode_paged: rows per page
@@ -119,6 +120,12 @@ WORKLOADS = {
         S=8192, std=1.0, seqlen_range=(1024, 8192), seed=4, page_size=64,
         description="bf16 decode over a paged cache: the batched-decode inputs in a shuffled "
                     "pool of 64-row group-aligned pages"),
+    "document_masked_prefill_bf16": Workload(
+        "document_masked_prefill_bf16", "prefill_mask", "bf16", B=1, L=4096, h_q=32, h_kv=8,
+        d=128, causal=True, std=1.0 / math.sqrt(2.0), seqlen_range=(128, 1024), seed=10,
+        description="bf16 causal prefill with a keep-mask: documents of lengths U{128..1024} "
+                    "packed into one sequence, each position seeing only its own document, "
+                    "B=1 L=4096 h_q=32 h_kv=8 d=128"),
 }
 
 # Order in which the workloads are listed everywhere: the five of the core
@@ -128,7 +135,7 @@ WORKLOAD_ORDER = ["tiny_prefill_f32", "worked_example_prefill_bf16", "llama2_7b_
                   "batched_decode_bf16", "long_context_prefill_bf16", "chunked_prefill_bf16",
                   "batched_decode_append_bf16", "batched_decode_paged_bf16",
                   "llama2_7b_prefill_rope_bf16", "varlen_prefill_bf16",
-                  "long_context_group_prefill_bf16"]
+                  "long_context_group_prefill_bf16", "document_masked_prefill_bf16"]
 
 
 def _draw(gen, shape, std, dtype):
@@ -223,6 +230,33 @@ def to_pages(k_cache, v_cache, seqlens, page_size, seed, spare=0):
     return k_pages, v_pages, table
 
 
+def document_lengths(L, lo, hi, seed):
+    """Lengths of documents packed into L positions: draws U{lo..hi} from a
+    generator seeded ``seed`` until they cover L, the last one cut to fit."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    lens, total = [], 0
+    while total < L:
+        n = int(torch.randint(lo, hi + 1, (1,), generator=gen))
+        n = min(n, L - total)
+        lens.append(n)
+        total += n
+    return lens
+
+
+def document_mask(lens):
+    """uint8 [L, L] keep-mask of packed documents: 1 where row and column lie
+    in the same document (a block-diagonal pattern; pure data layout)."""
+    L = sum(lens)
+    doc = torch.repeat_interleave(torch.arange(len(lens)), torch.tensor(lens))
+    return (doc[:, None] == doc[None, :]).to(torch.uint8).reshape(L, L)
+
+
+def random_mask(shape, density, seed):
+    """uint8 keep-mask of the given shape, each byte 1 with probability density."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    return (torch.rand(*shape, generator=gen) < density).to(torch.uint8)
+
+
 def workload_inputs(w: Workload):
     """Inputs of a named workload, as CPU tensors (see prefill_inputs/decode_inputs)."""
     if w.path == "prefill":
@@ -236,6 +270,12 @@ def workload_inputs(w: Workload):
         gen = torch.Generator(device="cpu").manual_seed(int(w.seed) + 1000)
         lens = torch.randint(lo, hi + 1, (w.B,), generator=gen, dtype=torch.int64)
         return q, k, v, lens.to(torch.int32)
+    if w.path == "prefill_mask":
+        q, k, v = prefill_inputs(w.B, w.L, w.h_q, w.h_kv, w.d, w.seed, w.std, w.torch_dtype())
+        lo, hi = w.seqlen_range
+        masks = [document_mask(document_lengths(w.L, lo, hi, w.seed + 1000 + b))
+                 for b in range(w.B)]
+        return q, k, v, torch.stack(masks)
     if w.path == "prefill_rope":
         q, k, v = prefill_inputs(w.B, w.L, w.h_q, w.h_kv, w.d, w.seed, w.std, w.torch_dtype())
         cos, sin = rope_tables(w.L, w.d)

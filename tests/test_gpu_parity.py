@@ -5,9 +5,13 @@ the exact values the GPU received (bf16 upcast exactly to float64).
 
 Tolerances (whole compared tensor): fp32 max-abs <= 1e-4; bf16 max-abs <= 2e-2
 and relative L2 <= 1e-2.  Small shapes are compared in full (several tiles,
-ragged tails, every group size class); the five named workloads run at their
-full sizes in the launch configuration the benchmark times and are compared on
-seeded samples of rows (decode: on sampled sequences, all heads).
+ragged tails, every group size class).  The named workloads run at their full
+sizes in the launch configuration the benchmark times: the worked example, the
+Llama-2-shaped layer (plain and rotary), the packed-documents keep-mask prefill
+and every decode workload are compared in full (decode: every sequence, 8 at a
+time); the 32K-position workloads, the chunked and the padded variable-length
+prefill are compared on one seeded row of every work-group plus seeded samples,
+and are checked for every output written.
 """
 import math
 
@@ -132,27 +136,27 @@ def test_prefill_is_deterministic(dev):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
-def test_prefill_running_max_jumps(d, causal, dev):
+@pytest.mark.parametrize("scale_kind", ["default", "power_of_two"])
+def test_prefill_running_max_jumps(d, causal, scale_kind, dev):
     """Keys that grow along the sequence, plus one spike key, so a row's max
     rises by more than the lazy-rescale threshold in later tiles, and for most
     rows once by far more than the fp32 exponent range (2^128): the rescale
     and the recomputed-tile paths of the online softmax must agree with the
-    plain row softmax.
+    plain row softmax, for scores of hundreds of log2 units.
 
-    The kernel folds scale*log2(e) into q before rounding it to bf16, which
-    perturbs scores of this size (hundreds of log2 units) by more than the
-    tolerance allows.  scale = ln(2)/8 makes that factor 1/8, a power of two,
-    so the folded q is exact and the test measures the softmax alone."""
+    At the default scale 1/sqrt(d) the kernel multiplies the fp32 scores by
+    scale*log2(e); at scale = ln(2)/8 that factor is 1/8, a power of two, and
+    the kernel folds it into q instead (exact in bf16): both must match."""
     B, L, h_q, h_kv = 1, 700, 8, 2
     q, k, v = wl.prefill_inputs(B, L, h_q, h_kv, d, 35 + d, 1 / math.sqrt(2), torch.bfloat16)
     grow = 1.0 + torch.arange(L, dtype=torch.float32) / 40.0
     grow[517] *= 60.0
     k = (k.float() * grow[None, :, None, None]).to(torch.bfloat16)
-    scale = math.log(2) / 8
-    say(f"prefill rising keys d{d} causal={causal}")
+    scale = 1 / math.sqrt(d) if scale_kind == "default" else math.log(2) / 8
+    say(f"prefill rising keys d{d} causal={causal} scale={scale}")
     out = run_prefill(q, k, v, causal, scale, dev)
     ref = oracle.prefill(f64(q), f64(k), f64(v), causal=causal, scale=scale)
-    check(f64(out), ref, "bf16", f"prefill rising keys d{d}")
+    check(f64(out), ref, "bf16", f"prefill rising keys d{d} scale {scale_kind}")
 
 
 def test_prefill_head_map_discriminates(dev):
@@ -172,13 +176,47 @@ def test_prefill_head_map_discriminates(dev):
 
 # ---------------------------------------------------------- named workloads, full size
 
+def workgroup_rows(B, L, h_q, h_kv, seed):
+    """One seeded (b, i, h) row from every prefill work-group: a work-group
+    holds GW query heads of one group (GW the largest power of two dividing
+    G, at most 8) times 256 / GW consecutive positions."""
+    G = h_q // h_kv
+    gw = 1
+    while gw < 8 and G % (2 * gw) == 0:
+        gw *= 2
+    bm = 256 // gw
+    gen = torch.Generator().manual_seed(int(seed) + 77)
+    rows = []
+    for b in range(B):
+        for kvh in range(h_kv):
+            for sub in range(G // gw):
+                for p0 in range(0, L, bm):
+                    n = min(bm, L - p0)
+                    i = p0 + int(torch.randint(0, n, (1,), generator=gen))
+                    h = kvh * G + sub * gw + int(torch.randint(0, gw, (1,), generator=gen))
+                    rows.append((b, i, h))
+    return rows
+
+
+def _full_prefill(name, dev):
+    """A named workload compared in full: every output row against the oracle."""
+    w = wl.WORKLOADS[name]
+    q, k, v = wl.workload_inputs(w)
+    say(f"prefill workload {name} ({w.description}) seed {w.seed}: every row")
+    out = run_prefill(q, k, v, w.causal, w.scale, dev)
+    ref = oracle.prefill(f64(q), f64(k), f64(v), causal=w.causal, scale=w.scale)
+    check(f64(out), ref, w.dtype, f"{name}: all {out.numel() // w.d} rows")
+
+
 def _sampled_prefill(name, n_rows, dev):
     w = wl.WORKLOADS[name]
     q, k, v = wl.workload_inputs(w)
     say(f"prefill workload {name} ({w.description}) seed {w.seed}")
     out = run_prefill(q, k, v, w.causal, w.scale, dev)
+    # seeded rows, the corners, and one row of every work-group
     rows = wl.sample_rows(n_rows, w.B, w.L, w.h_q, w.seed,
-                          include=[(0, 0, 0), (w.B - 1, w.L - 1, w.h_q - 1), (0, w.L - 1, 0)])
+                          include=[(0, 0, 0), (w.B - 1, w.L - 1, w.h_q - 1), (0, w.L - 1, 0),
+                                   *workgroup_rows(w.B, w.L, w.h_q, w.h_kv, w.seed)])
     idx = torch.tensor(rows)
     q_rows = q[idx[:, 0], idx[:, 1], idx[:, 2]]
     o_rows = out.cpu()[idx[:, 0], idx[:, 1], idx[:, 2]]
@@ -198,11 +236,11 @@ def test_workload_tiny_prefill_f32_full(dev):
 
 
 def test_workload_worked_example_prefill(dev):
-    _sampled_prefill("worked_example_prefill_bf16", 512, dev)
+    _full_prefill("worked_example_prefill_bf16", dev)
 
 
 def test_workload_llama2_prefill(dev):
-    _sampled_prefill("llama2_7b_prefill_bf16", 384, dev)
+    _full_prefill("llama2_7b_prefill_bf16", dev)
 
 
 def test_workload_long_context_prefill(dev):
@@ -279,7 +317,8 @@ def test_workload_chunked_prefill(dev):
     say(f"prefill_chunk workload {w.name} ({w.description}) seed {w.seed}")
     out = run_prefill_chunk(q, k, v, w.causal, w.scale, dev)
     rows = wl.sample_rows(96, w.B, w.L, w.h_q, w.seed,
-                          include=[(0, 0, 0), (0, w.L - 1, w.h_q - 1)])
+                          include=[(0, 0, 0), (0, w.L - 1, w.h_q - 1),
+                                   *workgroup_rows(w.B, w.L, w.h_q, w.h_kv, w.seed)])
     idx = torch.tensor(rows)
     q_rows = q[idx[:, 0], idx[:, 1], idx[:, 2]]
     o_rows = out.cpu()[idx[:, 0], idx[:, 1], idx[:, 2]]
@@ -312,11 +351,10 @@ def test_workload_batched_decode(dev):
     say(f"decode workload {w.name} ({w.description}) total keys {int(seqlens.sum())}")
     out = run_decode(seqlens, q, kc, vc, dev).cpu()
     assert not torch.isnan(out).any()
-    order = torch.argsort(seqlens).tolist()
-    picks = torch.randperm(w.B, generator=torch.Generator().manual_seed(w.seed))[:6].tolist()
-    bsel = sorted({order[0], order[-1], *picks})  # shortest, longest and 6 seeded sequences
-    ref = decode_ref(seqlens, q, kc, vc, bsel)
-    check(f64(out[torch.tensor(bsel), 0]), ref, "bf16", f"{w.name}: sequences {bsel}")
+    # every sequence, 8 at a time (bounds the fp64 copies of the caches)
+    refs = [decode_ref(seqlens, q, kc, vc, list(range(b0, min(b0 + 8, w.B))))
+            for b0 in range(0, w.B, 8)]
+    check(f64(out[:, 0]), np.concatenate(refs), "bf16", f"{w.name}: all {w.B} sequences")
 
 
 DECODE_SMALL = [
@@ -494,13 +532,19 @@ def test_workload_batched_decode_append(dev):
         exp[b_idx, :, sd.long()] = new.to(dev)[:, 0]
         assert torch.equal(got.view(torch.int16), exp.view(torch.int16)), f"{name}_cache"
         del exp
-    # the output and the whole cache slabs of sampled sequences against the oracle
+    # every sequence's output, and the whole cache slabs of 8 sampled
+    # sequences, against the oracle (8 sequences at a time)
+    o_refs = []
+    for b0 in range(0, w.B, 8):
+        bi = torch.arange(b0, min(b0 + 8, w.B))
+        o_ref, _, _ = append_ref(seqlens[bi], q[bi], kn[bi], vn[bi], kc[bi], vc[bi])
+        o_refs.append(o_ref)
+    check(f64(out[:, 0]), np.concatenate(o_refs), "bf16", f"{w.name}: all {w.B} sequences")
     order = torch.argsort(seqlens).tolist()
     picks = torch.randperm(w.B, generator=torch.Generator().manual_seed(w.seed))[:6].tolist()
     bsel = sorted({order[0], order[-1], *picks})
     bi = torch.tensor(bsel)
-    o_ref, kc_ref, vc_ref = append_ref(seqlens[bi], q[bi], kn[bi], vn[bi], kc[bi], vc[bi])
-    check(f64(out[bi, 0]), o_ref, "bf16", f"{w.name}: sequences {bsel}")
+    _, kc_ref, vc_ref = append_ref(seqlens[bi], q[bi], kn[bi], vn[bi], kc[bi], vc[bi])
     check_cache_exact(kcd[bi.to(dev)].cpu(), kc_ref, "k_cache slabs of the sampled sequences")
     check_cache_exact(vcd[bi.to(dev)].cpu(), vc_ref, "v_cache slabs of the sampled sequences")
 
@@ -652,20 +696,20 @@ def test_workload_batched_decode_paged(dev):
     s2, q2, kc, vc = wl.workload_inputs(dw)
     assert torch.equal(s2, seqlens) and torch.equal(q2, q)
     assert torch.equal(out, run_decode(s2, q2, kc, vc, dev).cpu())
-    order = torch.argsort(seqlens).tolist()
-    picks = torch.randperm(w.B, generator=torch.Generator().manual_seed(w.seed))[:4].tolist()
-    bsel = sorted({order[0], order[-1], *picks})
-    bi = torch.tensor(bsel)
-    # the oracle gets only the pages the sampled sequences use, renumbered
-    sub = table[bi]
-    used = sorted(set(int(x) for x in sub.flatten().tolist() if x >= 0))
-    remap = {p: i for i, p in enumerate(used)}
-    sub = torch.tensor([[remap.get(int(x), -1) for x in row] for row in sub.tolist()],
-                       dtype=torch.int32)
-    idx = torch.tensor(used)
-    ref = oracle.decode_paged(f64(q[bi, 0]), f64(kp[idx]), f64(vp[idx]), sub.numpy(),
-                              seqlens[bi].numpy())
-    check(f64(out[bi, 0]), ref, "bf16", f"{w.name}: sequences {bsel}")
+    # every sequence against the oracle, 8 at a time; the oracle gets only the
+    # pages those sequences use, renumbered
+    refs = []
+    for b0 in range(0, w.B, 8):
+        bi = torch.arange(b0, min(b0 + 8, w.B))
+        sub = table[bi]
+        used = sorted(set(int(x) for x in sub.flatten().tolist() if x >= 0))
+        remap = {p: i for i, p in enumerate(used)}
+        sub = torch.tensor([[remap.get(int(x), -1) for x in row] for row in sub.tolist()],
+                           dtype=torch.int32)
+        idx = torch.tensor(used)
+        refs.append(oracle.decode_paged(f64(q[bi, 0]), f64(kp[idx]), f64(vp[idx]), sub.numpy(),
+                                        seqlens[bi].numpy()))
+    check(f64(out[:, 0]), np.concatenate(refs), "bf16", f"{w.name}: all {w.B} sequences")
 
 
 # ------------------------------------------------------ prefill with rotary embedding
@@ -736,13 +780,8 @@ def test_workload_llama2_prefill_rope(dev):
     kr_ref = oracle.rope(f64(k), f64(cos), f64(sin))
     check_rotated_keys(k_rot, kr_ref, f"{w.name}: all rotated keys")
     q_rot = oracle.rope(f64(q), f64(cos), f64(sin))
-    rows = wl.sample_rows(256, w.B, w.L, w.h_q, w.seed,
-                          include=[(0, 0, 0), (0, w.L - 1, w.h_q - 1)])
-    idx = np.asarray(rows)
-    ref = oracle.prefill_rows(q_rot[idx[:, 0], idx[:, 1], idx[:, 2]], rows, kr_ref, f64(v), w.h_q,
-                              causal=w.causal, scale=w.scale)
-    ti = torch.tensor(rows)
-    check(f64(out[ti[:, 0], ti[:, 1], ti[:, 2]]), ref, "bf16", f"{w.name}: {len(rows)} sampled rows")
+    ref = oracle.prefill(q_rot, kr_ref, f64(v), causal=w.causal, scale=w.scale)
+    check(f64(out), ref, "bf16", f"{w.name}: all {out.numel() // w.d} rows")
 
 
 # ------------------------------------------------ prefill of variable-length sequences
@@ -804,7 +843,8 @@ def test_workload_varlen_prefill(dev):
     n0 = int(kv_lens[b0])
     rows = wl.sample_rows(192, w.B, w.L, w.h_q, w.seed,
                           include=[(b0, n0 - 1, 0), (b0, min(n0, w.L - 1), w.h_q - 1),
-                                   (w.B - 1, w.L - 1, 3)])
+                                   (w.B - 1, w.L - 1, 3),
+                                   *workgroup_rows(w.B, w.L, w.h_q, w.h_kv, w.seed)])
     idx = torch.tensor(rows)
     ref = oracle.prefill_varlen_rows(f64(q[idx[:, 0], idx[:, 1], idx[:, 2]]), rows, f64(k), f64(v),
                                      kv_lens.numpy(), w.h_q, w.causal, w.scale)
@@ -950,3 +990,156 @@ def test_graph_capture_replays_match_eager(dev):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(po, ref_p) and torch.equal(do, ref_d)
+
+
+# ------------------------------------------------------------ prefill with a keep-mask
+
+def run_prefill_mask(q, k, v, mask, causal, scale, dev):
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.full_like(qd, float("nan"))
+    gqa.prefill_mask(qd, kd, vd, mask.to(dev), causal=causal, scale=scale, out=out)
+    torch.cuda.synchronize()
+    return out
+
+
+def _case_mask(B, Lq, Lk, density, kind, seed):
+    """A keep-mask [B, Lq, Lk] (uint8, CPU): random bytes of the given density,
+    or packed documents ("blocks"); row 3 of sequence 0 hides every key."""
+    if kind == "blocks":
+        rows = []
+        for b in range(B):
+            lens = wl.document_lengths(Lk, 16, 96, seed + b)
+            rows.append(wl.document_mask(lens)[Lk - Lq:])
+        m = torch.stack(rows)
+    else:
+        m = wl.random_mask((B, Lq, Lk), density, seed)
+        # nonzero keep values other than 1 mean keep too
+        m = m * torch.randint(1, 256, m.shape, generator=torch.Generator().manual_seed(seed),
+                              dtype=torch.int64).to(torch.uint8).clamp(min=1)
+    if Lq > 3:
+        m[0, 3] = 0
+    return m
+
+
+MASK_SMALL = [
+    # B, L_q, L_k, h_q, h_kv, d, dtype, causal, density, kind
+    (2, 300, 300, 8, 2, 128, "bf16", True, 0.5, "random"),     # G = 4
+    (1, 257, 257, 8, 4, 64, "bf16", False, 0.3, "random"),     # G = 2, ragged tail
+    (2, 100, 333, 16, 2, 128, "bf16", True, 0.6, "random"),    # L_q < L_k, rows padded to 336
+    (1, 200, 200, 6, 2, 128, "bf16", False, 0.5, "blocks"),    # G = 3: 256 rows a work-group
+    (3, 65, 65, 8, 8, 64, "bf16", True, 0.5, "random"),        # MHA
+    (1, 129, 129, 16, 1, 64, "bf16", False, 0.05, "random"),   # G = 16, sparse
+    (1, 700, 700, 16, 2, 128, "bf16", True, 1.0, "blocks"),    # G = 8, block-diagonal documents
+    (2, 77, 90, 4, 2, 64, "f32", True, 0.5, "random"),
+    (1, 50, 50, 8, 2, 128, "f32", False, 0.5, "blocks"),
+]
+
+
+@pytest.mark.parametrize("case", MASK_SMALL, ids=lambda c: "B{}_Lq{}_Lk{}_hq{}_hkv{}_d{}_{}_c{}_{}".format(
+    *c[:8], c[9]))
+def test_prefill_mask_matches_oracle(case, dev):
+    B, Lq, Lk, h_q, h_kv, d, dt, causal, density, kind = case
+    seed = 5000 + Lq + Lk + h_q
+    dtype = torch.float32 if dt == "f32" else torch.bfloat16
+    q, k, v = wl.prefill_chunk_inputs(B, Lq, Lk, h_q, h_kv, d, seed, dtype=dtype)
+    m = _case_mask(B, Lq, Lk, density, kind, seed)
+    say(f"prefill_mask {case} seed {seed}")
+    out = run_prefill_mask(q, k, v, m, causal, 1 / math.sqrt(d), dev)
+    ref = oracle.prefill_mask(f64(q), f64(k), f64(v), m.numpy(), causal, 1 / math.sqrt(d))
+    check(f64(out), ref, dt, f"prefill_mask {case}")
+    if Lq > 3:
+        assert torch.equal(out[0, 3].cpu(), torch.zeros_like(out[0, 3].cpu())), \
+            "a row with no visible key must be zero"
+
+
+def test_prefill_mask_shared_2d_mask(dev):
+    """One [L_q, L_k] mask for the whole batch (batch stride 0)."""
+    B, L, h_q, h_kv, d = 3, 190, 8, 2, 128
+    q, k, v = wl.prefill_inputs(B, L, h_q, h_kv, d, 5101)
+    m2 = wl.random_mask((L, L), 0.4, 5102)
+    say("prefill_mask with one mask for the batch")
+    out = run_prefill_mask(q, k, v, m2, True, 0.09, dev)
+    ref = oracle.prefill_mask(f64(q), f64(k), f64(v), m2.expand(B, L, L).numpy(), True, 0.09)
+    check(f64(out), ref, "bf16", "shared 2-D mask")
+
+
+def test_prefill_mask_all_ones_is_chunk(dev):
+    """Every byte nonzero: the chunked prefill's result, bit for bit."""
+    for (B, Lq, Lk, h_q, h_kv, d, dtype) in ((2, 150, 300, 8, 2, 128, torch.bfloat16),
+                                            (1, 257, 257, 8, 4, 64, torch.bfloat16),
+                                            (1, 70, 99, 4, 1, 64, torch.float32)):
+        q, k, v = wl.prefill_chunk_inputs(B, Lq, Lk, h_q, h_kv, d, 5200 + Lq, dtype=dtype)
+        ones = torch.full((B, Lq, Lk), 7, dtype=torch.uint8)
+        for causal in (True, False):
+            say(f"prefill_mask all ones {B, Lq, Lk, h_q, h_kv, d, dtype} causal={causal}")
+            a = run_prefill_mask(q, k, v, ones, causal, 0.1, dev)
+            b = run_prefill_chunk(q, k, v, causal, 0.1, dev)
+            assert torch.equal(a, b)
+
+
+def test_prefill_mask_lengths_is_varlen(dev):
+    """A key-padding mask given as bytes: the variable-length prefill, bit for bit."""
+    B, L, h_q, h_kv, d = 4, 300, 8, 2, 128
+    q, k, v = wl.prefill_inputs(B, L, h_q, h_kv, d, 5300)
+    lens = torch.tensor([300, 1, 64, 129], dtype=torch.int32)
+    m = torch.zeros(B, L, L, dtype=torch.uint8)
+    for b, n in enumerate(lens.tolist()):
+        m[b, :, :n] = 1
+    for causal in (True, False):
+        say(f"prefill_mask lengths vs varlen causal={causal}")
+        a = run_prefill_mask(q, k, v, m, causal, 0.1, dev)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        b = gqa.prefill_varlen(qd, kd, vd, lens.to(dev), causal=causal, scale=0.1)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+
+
+def test_workload_document_masked_prefill(dev):
+    """The packed-documents workload at full size, every output against the oracle."""
+    w = wl.WORKLOADS["document_masked_prefill_bf16"]
+    q, k, v, m = wl.workload_inputs(w)
+    say(f"prefill_mask workload {w.name} ({w.description}) seed {w.seed}")
+    out = run_prefill_mask(q, k, v, m, w.causal, w.scale, dev)
+    ref = oracle.prefill_mask(f64(q), f64(k), f64(v), m.numpy(), w.causal, w.scale)
+    check(f64(out), ref, w.dtype, f"{w.name}: all {out.numel() // w.d} rows")
+
+
+# ------------------------------------------------------------ binding argument checks
+
+def test_binding_rejects_mismatched_buffers(dev):
+    """Caller-supplied outputs, rotated-key buffers and workspaces of the wrong
+    shape, dtype or device are refused before anything is launched."""
+    B, L, h_q, h_kv, d = 2, 64, 8, 2, 64
+    q, k, v = (t.to(dev) for t in wl.prefill_inputs(B, L, h_q, h_kv, d, 9100))
+    lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    short = torch.empty(B, L - 1, h_q, d, dtype=q.dtype, device=dev)
+    f32 = torch.empty(B, L, h_q, d, dtype=torch.float32, device=dev)
+    with pytest.raises(ValueError):
+        gqa.prefill_varlen(q, k, v, lens, causal=True, out=short)
+    with pytest.raises(ValueError):
+        gqa.prefill_varlen(q, k, v, lens, causal=True, out=f32)
+    cos, sin = (t.to(dev) for t in wl.rope_tables(L, d))
+    with pytest.raises(ValueError):
+        gqa.prefill_rope(q, k, v, cos, sin, causal=True, out=f32)
+    with pytest.raises(ValueError):
+        gqa.prefill_rope(q, k, v, cos, sin, causal=True,
+                         k_rot=torch.empty(B, L, h_kv, d - 8, dtype=q.dtype, device=dev))
+    with pytest.raises(ValueError):
+        gqa.prefill_mask(q, k, v, torch.ones(B, L, L, dtype=torch.bool, device=dev),
+                         causal=True, out=short)
+    seqlens, qd, kc, vc = (t.to(dev) for t in wl.decode_inputs(B, h_q, h_kv, 128, d, 9101,
+                                                               (1, 128)))
+    need = gqa.decode_workspace_bytes(B, h_q, h_kv, d)
+    with pytest.raises(ValueError):
+        gqa.decode(qd, kc, vc, seqlens, workspace=torch.empty(need, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        gqa.decode(qd, kc, vc, seqlens, workspace=torch.empty(need - 1, dtype=torch.uint8,
+                                                              device=dev))
+    with pytest.raises(TypeError):
+        gqa.decode(qd, kc.float(), vc, seqlens)
+    kn = torch.zeros(B, 1, h_kv, d, dtype=qd.dtype, device=dev)
+    with pytest.raises(ValueError):
+        gqa.decode_append_rope(qd, kn, kn, kc, vc, seqlens, *(t.to(dev) for t in
+                                                              wl.rope_tables(128, d)),
+                               out=torch.empty(B, 1, h_q, d, dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
