@@ -440,7 +440,9 @@ def _grid(row):
 
 
 def _short(name):
-    return name.split("(")[0].replace("void ", "") if len(name) > 90 else name
+    """A kernel name without its namespaces' anonymous part, return type and arguments."""
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.rsplit("(", 1)[0] if name.endswith(")") else name
 
 
 def trace_summary(path, last):

@@ -180,8 +180,15 @@ __device__ __forceinline__ int dc_nblk(const int32_t *seqlens, int b, int extra,
     return (dc_rows(seqlens, b, extra, S) + DC_BK - 1) / DC_BK;
 }
 
+// floor(w * T / NW), the first block of wave w's slice.  A 64-bit integer
+// division is a long vector-ALU sequence; the quotient is taken in double
+// (off by at most one for T < 2^51) and corrected with exact products.
 __device__ __forceinline__ long long dc_slice_start(int w, long long T, int NW) {
-    return (long long)w * T / NW;
+    const long long x = (long long)w * T;
+    long long s = (long long)((double)x / (double)NW);
+    if (s * NW > x) --s;
+    else if ((s + 1) * NW <= x) ++s;
+    return s;
 }
 
 // A wave-uniform 64-bit value held in vector registers, made scalar.
@@ -468,7 +475,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     P += (long long)seg_in_b * nb;  // first block of this segment
     const long long seg_global = (long long)b * segs_per_b + seg_in_b;
     // waves whose slices intersect [P, P + nb)
-    int w0 = (int)min((long long)a.NW - 1, P * a.NW / T);
+    int w0 = (int)min((double)a.NW - 1, (double)P * a.NW / (double)T);
     while (w0 > 0 && dc_slice_start(w0, T, a.NW) > P) --w0;
     while (dc_slice_start(w0 + 1, T, a.NW) <= P) ++w0;
     // Rounds of 64 waves (one round unless more than 64 waves cover the

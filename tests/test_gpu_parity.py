@@ -357,6 +357,32 @@ def test_workload_batched_decode(dev):
     check(f64(out[:, 0]), np.concatenate(refs), "bf16", f"{w.name}: all {w.B} sequences")
 
 
+def test_decode_reuses_one_workspace(dev):
+    """One workspace serves many calls: its contents on entry are ignored, so a
+    second, smaller call (other lengths, fewer sequences, a zero length) and a
+    repeat of the first give the results of fresh workspaces, bit for bit,
+    also when the workspace starts out full of NaN bytes."""
+    B, h_q, h_kv, S, d = 6, 32, 8, 1100, 128
+    need = gqa.decode_workspace_bytes(B, h_q, h_kv, d)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=dev)
+    s1, q1, k1, v1 = wl.decode_inputs(B, h_q, h_kv, S, d, 4100, (1, S))
+    s2, q2, k2, v2 = wl.decode_inputs(3, h_q, h_kv, S, d, 4101, (1, S))
+    s2[0] = 0
+    q1d, k1d, v1d, s1d = q1.to(dev), k1.to(dev), v1.to(dev), s1.to(dev)
+    q2d, k2d, v2d, s2d = q2.to(dev), k2.to(dev), v2.to(dev), s2.to(dev)
+    say("decode: repeated calls on one workspace")
+    fresh1 = gqa.decode(q1d, k1d, v1d, s1d)
+    fresh2 = gqa.decode(q2d, k2d, v2d, s2d)
+    for rep in range(3):
+        a = gqa.decode(q1d, k1d, v1d, s1d, workspace=ws)
+        b = gqa.decode(q2d, k2d, v2d, s2d, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(a, fresh1), f"call {2 * rep} differs from a fresh workspace"
+        assert torch.equal(b, fresh2), f"call {2 * rep + 1} differs from a fresh workspace"
+    assert torch.equal(fresh2[0].cpu(), torch.zeros_like(fresh2[0].cpu()))
+    check(f64(fresh1.cpu()[:, 0]), decode_ref(s1, q1, k1, v1), "bf16", "decode reusing a workspace")
+
+
 DECODE_SMALL = [
     # B, h_q, h_kv, S, d, seqlens
     (6, 32, 8, 1100, 128, [0, 1, 511, 512, 513, 1100]),
