@@ -28,6 +28,8 @@ the device is not a gfx950 GPU, the calls raise.
         (o, k_rot).
     decode_append_rope(q, k_new, v_new, k_cache, v_cache, seqlens, cos, sin, ...)
         decode with append, q and k_new rotated at position seqlens[b] first.
+    decode_noalloc(q, k_cache, v_cache, seqlens, out=..., num_splits=0)
+        as decode, with the library's fixed scratch as workspace: allocates nothing.
     decode_token_major(q, k_cache, v_cache, seqlens, ...)
         as decode, with caches [B, S, h_kv, d].
     decode_paged(q, k_pages, v_pages, block_table, seqlens, ...)
@@ -81,6 +83,10 @@ def lib() -> ctypes.CDLL:
     L.gqa_decode_append.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P,
                                     ctypes.c_size_t, P]
     L.gqa_decode_append.restype = I
+    L.gqa_decode_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P]
+    L.gqa_decode_noalloc.restype = I
+    L.gqa_decode_noalloc_max_bytes.argtypes = []
+    L.gqa_decode_noalloc_max_bytes.restype = ctypes.c_size_t
     L.gqa_decode_token_major.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, ctypes.c_size_t, P]
     L.gqa_decode_token_major.restype = I
     L.gqa_decode_paged.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, ctypes.c_size_t, P]
@@ -259,6 +265,37 @@ def decode(q, k_cache, v_cache, seqlens, *, out=None, workspace=None, num_splits
                           _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_decode")
+    return out
+
+
+def decode_noalloc_max_bytes() -> int:
+    return int(lib().gqa_decode_noalloc_max_bytes())
+
+
+def decode_noalloc(q, k_cache, v_cache, seqlens, *, out, num_splits: int = 0):
+    """decode() with the library's fixed scratch as its workspace: the call
+    allocates nothing (out must be given).  Calls that overlap on one GPU race;
+    a call needing more than decode_noalloc_max_bytes() of workspace raises."""
+    _check(q, "q", 4)
+    _check(k_cache, "k_cache", 4)
+    _check(v_cache, "v_cache", 4)
+    _check(seqlens, "seqlens", 1)
+    B, one, h_q, d = q.shape
+    if one != 1:
+        raise ValueError("q must be [B, 1, h_q, d]")
+    _, h_kv, S, _ = k_cache.shape
+    if tuple(k_cache.shape) != (B, h_kv, S, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, h_kv, S, d] with q's B and d")
+    if seqlens.dtype != torch.int32 or seqlens.shape[0] != B:
+        raise ValueError("seqlens must be int32 [B]")
+    _same(q, (k_cache, "k_cache"), (v_cache, "v_cache"))
+    _on_device(q, (seqlens, "seqlens"))
+    _check_out(out, q)
+    st = lib().gqa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                  seqlens.data_ptr(), out.data_ptr(), B, h_q, h_kv, S, d,
+                                  _dtype_code(q), int(num_splits), _stream(q))
+    if st != 0:
+        raise GQAError(st, "gqa_decode_noalloc")
     return out
 
 

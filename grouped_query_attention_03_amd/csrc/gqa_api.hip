@@ -41,6 +41,26 @@ int heads_per_workgroup(int G) {
 }
 
 constexpr int kDefaultSplits = 256 * gqa::kDecodeWaves;  // every wave of the split pass resident on 256 CUs
+
+// The decode workspace of gqa_decode_noalloc: a fixed array in device memory,
+// one copy per GPU, held until the process ends.  In host code `scratch` is
+// only a stand-in for the symbol; the array's device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+std::atomic<void *> g_scratch[kMaxDevices];
+
+// The current device's scratch address, or nullptr if it cannot be had.
+void *device_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    void *q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    g_scratch[dev].store(q, std::memory_order_release);  // every thread finds the same address
+    return q;
+}
 constexpr int kMaxSplits = 1 << 20;
 
 bool splits_valid(int n) { return n >= 0 && n <= kMaxSplits; }
@@ -61,6 +81,7 @@ const char *gqa_status_string(gqa_status s) {
         case GQA_ERR_WORKSPACE: return "decode workspace is NULL or too small";
         case GQA_ERR_LAUNCH: return "the HIP runtime reported a launch error";
         case GQA_ERR_DEVICE: return "the current device is not a gfx950 GPU";
+        case GQA_ERR_SCRATCH: return "the call needs more than the fixed decode scratch holds";
         default: return "unknown status";
     }
 }
@@ -235,7 +256,9 @@ gqa_status decode_impl(const void *q, const void *k_new, const void *v_new, cons
                        int h_kv, int S, int d, gqa_dtype dt, int num_splits, void *workspace,
                        size_t workspace_bytes, void *hip_stream, int layout = gqa::kLayoutHeadMajor,
                        const int32_t *block_table = nullptr, int page_size = 0,
-                       int max_blocks = 0) {
+                       int max_blocks = 0, bool use_scratch = false) {
+    // use_scratch: the workspace is the library's fixed scratch of this device
+    // (gqa_decode_noalloc); a call needing more is refused
     const bool append = k_new != nullptr || v_new != nullptr;
     if (!q || !k_cache || !v_cache || !seqlens || !o) return GQA_ERR_NULL_POINTER;
     if (layout == gqa::kLayoutPaged) {
@@ -258,7 +281,11 @@ gqa_status decode_impl(const void *q, const void *k_new, const void *v_new, cons
     if (!splits_valid(num_splits)) return GQA_ERR_SIZE;
     if ((int64_t)B * h_q > 0x7fffffff / 4) return GQA_ERR_SIZE;
     const size_t need = gqa_decode_workspace_bytes(B, h_q, h_kv, d, num_splits);
-    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+    if (use_scratch) {
+        if (need > kScratchBytes) return GQA_ERR_SCRATCH;
+    } else if (!workspace || !aligned16(workspace) || workspace_bytes < need) {
+        return GQA_ERR_WORKSPACE;
+    }
 
     gqa::DecodeArgs a;
     a.q = q;
@@ -277,9 +304,6 @@ gqa_status decode_impl(const void *q, const void *k_new, const void *v_new, cons
     a.NW = num_splits == 0 ? kDefaultSplits : num_splits;
     a.n_qsub = (a.G + 15) / 16;
     const size_t slots = (size_t)a.NW + (size_t)B * h_kv * a.n_qsub;
-    a.opart = static_cast<float *>(workspace);
-    a.lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                      round_up_256(slots * 16 * d * sizeof(float)));
     a.c = (float)(1.4426950408889634 / sqrt((double)d));
     a.layout = layout;
     a.block_table = block_table;
@@ -288,6 +312,13 @@ gqa_status decode_impl(const void *q, const void *k_new, const void *v_new, cons
 
     gqa_status st = check_device();
     if (st != GQA_OK) return st;
+    if (use_scratch) {
+        workspace = device_scratch();
+        if (!workspace) return GQA_ERR_DEVICE;
+    }
+    a.opart = static_cast<float *>(workspace);
+    a.lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                      round_up_256(slots * 16 * d * sizeof(float)));
     int rc = gqa::launch_decode_bf16(a, d, static_cast<hipStream_t>(hip_stream));
     return rc == 0 ? GQA_OK : GQA_ERR_LAUNCH;
 }
@@ -302,6 +333,16 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
                       void *hip_stream) {
     return decode_impl(q, nullptr, nullptr, k_cache, v_cache, seqlens, o, B, h_q, h_kv, S, d, dt,
                        num_splits, workspace, workspace_bytes, hip_stream);
+}
+
+size_t gqa_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+gqa_status gqa_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *seqlens, void *o, int B, int h_q, int h_kv, int S,
+                              int d, gqa_dtype dt, int num_splits, void *hip_stream) {
+    return decode_impl(q, nullptr, nullptr, k_cache, v_cache, seqlens, o, B, h_q, h_kv, S, d, dt,
+                       num_splits, nullptr, 0, hip_stream, gqa::kLayoutHeadMajor, nullptr, 0, 0,
+                       true);
 }
 
 gqa_status gqa_decode_token_major(const void *q, const void *k_cache, const void *v_cache,

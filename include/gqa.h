@@ -51,7 +51,8 @@ enum {
     GQA_ERR_DTYPE = 6,         /* dtype not supported by this entry point */
     GQA_ERR_WORKSPACE = 7,     /* workspace NULL or smaller than required */
     GQA_ERR_LAUNCH = 8,        /* the HIP runtime reported an error at launch */
-    GQA_ERR_DEVICE = 9         /* the current device is not a gfx950 GPU */
+    GQA_ERR_DEVICE = 9,        /* the current device is not a gfx950 GPU */
+    GQA_ERR_SCRATCH = 10       /* gqa_decode_noalloc: the call needs more than its fixed scratch */
 };
 
 /*
@@ -201,6 +202,30 @@ gqa_status gqa_decode(const void *q, const void *k_cache, const void *v_cache,
                       const int32_t *seqlens, void *o, int B, int h_q, int h_kv, int S, int d,
                       gqa_dtype dt, int num_splits, void *workspace, size_t workspace_bytes,
                       void *hip_stream);
+
+/*
+ * Decode that allocates nothing, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid it): gqa_decode with its workspace in a fixed array in device memory
+ * that the library holds, one per GPU, until the process ends.
+ *   q, k_cache, v_cache, seqlens, o, B, h_q, h_kv, S, d, dt, num_splits,
+ *   hip_stream: as gqa_decode; the caller passes every input and output.
+ * The array holds gqa_decode_noalloc_max_bytes() bytes (32 MiB); a call whose
+ * gqa_decode_workspace_bytes(...) exceeds that returns GQA_ERR_SCRATCH (after
+ * the argument checks gqa_decode makes; nothing is launched).  No call
+ * allocates or frees memory; the first call on a GPU looks up the array's
+ * address there.
+ * Every call on one GPU uses that GPU's one array, so calls that overlap in
+ * time on one GPU (on different streams, or from different threads) race;
+ * calls in sequence on one stream are safe (the array's contents on entry
+ * are ignored).  Results are those of gqa_decode with the same arguments.
+ */
+gqa_status gqa_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *seqlens, void *o, int B, int h_q, int h_kv, int S,
+                              int d, gqa_dtype dt, int num_splits, void *hip_stream);
+
+/* Bytes of the fixed scratch array gqa_decode_noalloc uses on each GPU. */
+size_t gqa_decode_noalloc_max_bytes(void);
 
 /*
  * Decode over a token-major cache: as gqa_decode, with the cache laid out

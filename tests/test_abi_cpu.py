@@ -15,7 +15,7 @@ import grouped_query_attention_03_amd as gqa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gqa.h")
 
-OK, NULLP, ALIGN, SIZE, HEADS, HEADDIM, DTYPE, WORKSPACE, LAUNCH, DEVICE = range(10)
+OK, NULLP, ALIGN, SIZE, HEADS, HEADDIM, DTYPE, WORKSPACE, LAUNCH, DEVICE, SCRATCH = range(11)
 A = 0x10000   # a fake 16-byte-aligned address
 MIS = 0x10008  # a fake misaligned address
 
@@ -44,8 +44,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_are_distinct():
-    s = [gqa.status_string(i) for i in range(10)]
-    assert len(set(s)) == 10
+    s = [gqa.status_string(i) for i in range(11)]
+    assert len(set(s)) == 11
     assert gqa.status_string(99) == "unknown status"
 
 
@@ -236,6 +236,32 @@ def decode_status(q=A, kc=A, vc=A, sl=A, o=A, B=4, h_q=32, h_kv=8, S=1024, d=128
 ])
 def test_decode_rejects_bad_arguments(kw, status):
     assert decode_status(**kw) == status
+
+
+def noalloc_status(q=A, kc=A, vc=A, sl=A, o=A, B=4, h_q=32, h_kv=8, S=1024, d=128, dt=1,
+                   splits=0):
+    return gqa.lib().gqa_decode_noalloc(q, kc, vc, sl, o, B, h_q, h_kv, S, d, dt, splits, None)
+
+
+def test_noalloc_scratch_is_32_mib():
+    assert gqa.decode_noalloc_max_bytes() == 32 << 20
+
+
+@pytest.mark.parametrize("kw,status", [
+    # more workspace than the fixed scratch holds (after the argument checks)
+    (dict(B=4096), SCRATCH), (dict(splits=1 << 20), SCRATCH), (dict(B=4096, q=None), NULLP),
+    (dict(q=None), NULLP), (dict(o=MIS), ALIGN), (dict(B=0), SIZE), (dict(h_q=32, h_kv=5), HEADS),
+    (dict(d=96), HEADDIM), (dict(dt=0), DTYPE), (dict(splits=-2), SIZE),
+])
+def test_decode_noalloc_rejects_bad_arguments(kw, status):
+    assert noalloc_status(**kw) == status
+
+
+def test_decode_noalloc_without_a_gpu_reports_the_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert noalloc_status() == DEVICE
 
 
 def test_decode_without_a_gpu_reports_the_device():
