@@ -38,7 +38,11 @@
 extern "C" {
 #endif
 
-typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
+/* Element type of q, k, v and o.  A plain int, so that any value a caller
+ * passes is defined behaviour and is rejected with GQA_ERR_DTYPE when it is
+ * neither constant. */
+typedef int gqa_dtype;
+enum { GQA_F32 = 0, GQA_BF16 = 1 };
 
 typedef int gqa_status;
 enum {
