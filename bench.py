@@ -132,7 +132,8 @@ def source_digest(files) -> str:
 
 
 KERNEL_SOURCES = {
-    "prefill": ["prefill_bf16.hip", "prefill_f32.hip", "gqa_device.h", "gqa_kernels.h"],
+    "prefill": ["prefill_bf16.hip", "prefill_f32.hip", "prefill_layout.h", "gqa_device.h",
+                "gqa_kernels.h"],
     "decode": ["decode_bf16.hip", "gqa_device.h", "gqa_kernels.h"],
 }
 

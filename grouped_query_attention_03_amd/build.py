@@ -16,20 +16,21 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libgqa_hip.so")
 SOURCES = ["gqa_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode_bf16.hip",
            "rope_bf16.hip"]
-# Per-source additions.  The bf16 prefill kernel never orders NaNs (masked and
-# stale scores are replaced by -inf with a select before any max), so it runs
-# with the IEEE mode bit off: max/min then need no canonicalising copies.
-SOURCE_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+# Select the VGPR form of MFMA instructions: the register allocator then moves
+# only accumulator chains that never feed vector ALU work to AGPRs.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+# The bf16 prefill kernel never orders NaNs (masked and stale scores are
+# replaced by -inf with a select before any max), so it runs with the IEEE
+# mode bit off: max/min then need no canonicalising copies.
+NO_IEEE = ["-fno-honor-nans", "-mno-amdgpu-ieee"]
+# Per-source flags (default: VGPR_FORM).
+SOURCE_FLAGS = {"prefill_bf16.hip": VGPR_FORM + NO_IEEE}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from forming packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # select the VGPR form of MFMA instructions; the register allocator then
-    # moves only accumulator chains that never feed vector ALU work to AGPRs
-    # (prefill keeps its output accumulators there and its scores in VGPRs)
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 # hipcc's host pass does not know the packed-fp32 feature; that note is harmless
@@ -55,7 +56,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         for src in SOURCES:
             obj = os.path.join(PKG_DIR, src + tag + ".o")
             objs.append(obj)
-            _run([HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *extra_flags, "-I", INCLUDE,
+            _run([HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, VGPR_FORM), *extra_flags, "-I", INCLUDE,
                   "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         tmp = LIB_PATH + tag
         _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)

@@ -61,31 +61,13 @@
 //   rows.
 #include "gqa_device.h"
 #include "gqa_kernels.h"
+#include "prefill_layout.h"
 
 namespace gqa {
 namespace {
 
 constexpr int PF_WAVES = 8;
 constexpr int PF_THREADS = 64 * PF_WAVES;
-constexpr int PF_BN = 64;       // keys per tile
-constexpr float PF_TAU = 8.0f;  // lazy-rescale threshold, log2 units
-
-// Forms of the kernel: q rotated at load (ROPE), per-sequence key lengths
-// (VARLEN), a keep-mask of bytes (MASK).
-enum PfForm { kPfPlain = 0, kPfRope = 1, kPfVarlen = 2, kPfMask = 3 };
-
-template <int D>
-struct PfLay {
-    static constexpr int ROW_BYTES = 2 * D;
-    static constexpr int CPR = D / 8;                        // 16-byte chunks per row
-    static constexpr int ROWS_PER_DMA = 64 / CPR;            // rows per 64-lane 16-byte load
-    static constexpr int TILE_BYTES = PF_BN * ROW_BYTES;     // one K or V tile
-    static constexpr int DMA_PER_TENSOR = TILE_BYTES / 1024;
-    static constexpr int DMA_PER_WAVE = 2 * DMA_PER_TENSOR / PF_WAVES;
-    static constexpr int ROWS_PER_SWEEP = 256 / ROW_BYTES;   // rows per pass over the banks
-    static constexpr int KSTEPS = D / 16;                    // MFMA k-steps over d
-    static constexpr int DB = D / 32;                        // 32-wide blocks of d
-};
 
 // The LDS ring: SLOTS slots, each the K tile, the V tile and (keep-mask form)
 // the mask bytes of up to 256 rows x 64 keys; tile x is issued PF_DIST = SLOTS - 1
@@ -101,25 +83,6 @@ struct PfRing {
 // Mask tile rows are 64 bytes (4 chunks of 16); logical chunk c of row r sits
 // at chunk position c ^ swz(r), so the rows read together spread over the banks.
 __device__ __forceinline__ int pf_mswz(int r) { return (r >> 2) & 3; }
-
-// Tiles are stored unpadded (each direct load writes 64 consecutive 16-byte
-// chunks); 16-byte chunk c of row r sits at chunk position c ^ swz(r).
-//   K: 16 lanes reading one chunk of 16 consecutive rows hit distinct banks.
-//   V: a half-wave transposing read (4 rows x 64 bytes) hits distinct banks.
-template <int D>
-__device__ __forceinline__ int pf_kswz(int r) {
-    using Lay = PfLay<D>;
-    return (r / Lay::ROWS_PER_SWEEP) % Lay::CPR;
-}
-template <int D>
-__device__ __forceinline__ int pf_vswz(int r) {
-    return D == 128 ? 4 * (r % 4) : 4 * ((r / 2) % 2);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 // s_waitcnt vmcnt with a wave-uniform count known only at run time (0 .. 15;
 // larger counts wait for everything, which is only stricter).
@@ -144,10 +107,6 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n) {
     }
 }
 
-__device__ __forceinline__ void block_barrier() {
-    asm volatile("s_barrier" ::: "memory");
-}
-
 // FORM (PfForm): kPfRope rotates q as it is loaded (the keys arrive rotated
 // already); kPfVarlen gives sequence b a.kv_lens[b] visible keys (a padded
 // batch); kPfMask hides key j from query row i unless its mask byte is nonzero.
@@ -158,7 +117,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
     using Lay = PfLay<D>;
     using Ring = PfRing<D, FORM>;
     constexpr bool ROPE = FORM == kPfRope, VARLEN = FORM == kPfVarlen, MASK = FORM == kPfMask;
-    constexpr int KSTEPS = Lay::KSTEPS, DB = Lay::DB, DPW = Lay::DMA_PER_WAVE;
+    constexpr int KSTEPS = Lay::KSTEPS, DB = Lay::DB;
+    constexpr int DPW = 2 * Lay::DMA_PER_TENSOR / PF_WAVES;  // direct loads per wave per tile
     constexpr int SLOTS = Ring::SLOTS, DIST = Ring::DIST, SLOT_BYTES = Ring::SLOT_BYTES;
     __shared__ __attribute__((aligned(1024))) char smem[SLOTS * SLOT_BYTES];
 
@@ -264,6 +224,20 @@ void prefill_bf16_kernel(PrefillArgs a) {
                                                       (wave + 8 * u) * 1024));
         }
     };
+
+    // V rows past the sequence end meet P = 0 and must be finite: zero the V
+    // halves of the ring once, in case an out-of-range load leaves its LDS
+    // bytes untouched.
+    for (int i = threadIdx.x; i < SLOTS * Lay::TILE_BYTES / 16; i += PF_THREADS) {
+        const int sl = i / (Lay::TILE_BYTES / 16), off = i % (Lay::TILE_BYTES / 16);
+        store16_lds(smem + sl * SLOT_BYTES + Lay::TILE_BYTES + 16 * off, u32x4{0u, 0u, 0u, 0u});
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    block_barrier();
+    // Tile 0 streams in while q is read.  A zero-length sequence has no tile;
+    // its buffer range is empty, so these loads read zeros without touching
+    // memory.
+    issue_tile(0);
 
     // Q^T operand: lane holds 8 head-dim values of one query row.
     bf16x8 qf[KSTEPS];
@@ -411,6 +385,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
     auto softmax = [&](int j, bool full_tile) {
         const int j0 = j * PF_BN;
         if ((MASK && !full_tile) || j0 + PF_BN > Lk || (CAUSAL && j0 + PF_BN - 1 > off + pos0)) {
+            pf_keep_branch();  // only diagonal, tail and partly hidden tiles pay for it
             if constexpr (MASK) {
                 // read again here rather than kept in registers since the
                 // tile test (the empty asm keeps the two reads apart)
@@ -449,6 +424,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
         // wave-wide rescale, so that it leaves the other rows' schedule alone
         if constexpr (FOLD) {
             if (__any((m_run == -INFINITY && mx != -INFINITY) || mx > PF_TAU)) {
+                pf_keep_branch();  // rarely taken: no rescale work on other tiles
                 const float m2 = m_run == -INFINITY ? mu + mx : fmaxf(m_run, mu + mx);
                 const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m2);
                 const float delta = (m2 == -INFINITY) ? 0.f : m2 - mu;
@@ -467,6 +443,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
             // max in log2 units is mx * c
             const float mt = mx * c;
             if (__any((m_run == -INFINITY && mt != -INFINITY) || mt > mu + PF_TAU)) {
+                pf_keep_branch();  // rarely taken: no rescale work on other tiles
                 const float m2 = fmaxf(m_run, mt);  // -inf while nothing is visible
                 const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m2);
                 m_run = m2;
@@ -495,18 +472,10 @@ void prefill_bf16_kernel(PrefillArgs a) {
                 }
     };
 
-    // V rows past the sequence end meet P = 0 and must be finite: zero the V
-    // halves of the ring once, in case an out-of-range load leaves its LDS
-    // bytes untouched.
-    for (int i = threadIdx.x; i < SLOTS * Lay::TILE_BYTES / 16; i += PF_THREADS) {
-        const int sl = i / (Lay::TILE_BYTES / 16), off = i % (Lay::TILE_BYTES / 16);
-        store16_lds(smem + sl * SLOT_BYTES + Lay::TILE_BYTES + 16 * off, u32x4{0u, 0u, 0u, 0u});
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    block_barrier();
-    // a zero-length sequence has no tile; its buffer range is empty, so these
-    // loads read zeros without touching memory
-    issue_tile(0);
+    // q has landed: the compiler's own wait for the q loads stands here, where
+    // it also covers tile 0, and not inside the loop, where it would drain the
+    // prefetched tiles every iteration
+    pf_settle(qf);
 #pragma unroll
     for (int x = 1; x < DIST; ++x)
         if (x < ntiles) issue_tile(x);
