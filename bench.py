@@ -242,19 +242,28 @@ def bench_prefill(w, steps, warmup, settle_s=0.0):
     settle_clocks(step, settle_s)
     for _ in range(warmup):
         step()
-    # the K timed steps run back to back between two synchronisations; then K
-    # more steps are timed one by one with events on the launch stream for
-    # the kernel's own average (an event pair between launches leaves a small
-    # gap on the GPU, so it is kept out of the throughput's timed region)
+    # K steps timed one by one with events (for the shortest launch; an event
+    # pair around a launch adds a few microseconds, so this is not the
+    # average); then the K timed steps back to back between two
+    # synchronisations (the throughput); then K more back to back between one
+    # event pair on the launch stream (the kernel's average launch time, which
+    # a kernel trace of the last K dispatches reproduces)
+    _, ev = time_launches(step, steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    _, ev = time_launches(step, steps)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
     flops = prefill_flops(w, None if kv_lens is None else kv_lens.tolist(), mask_cpu)
-    avg_ms = sum(ev) / len(ev)
+    avg_ms = e0.elapsed_time(e1) / steps
     return {
         "value": flops * steps / wall / 1e12,
         "ms_per_step": wall * 1e3 / steps,

@@ -478,15 +478,57 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     int w0 = (int)min((double)a.NW - 1, (double)P * a.NW / (double)T);
     while (w0 > 0 && dc_slice_start(w0, T, a.NW) > P) --w0;
     while (dc_slice_start(w0 + 1, T, a.NW) <= P) ++w0;
-    // Rounds of 64 waves (one round unless more than 64 waves cover the
-    // segment): lane j holds the log-sum-exp of wave wb + j, or -inf for an
-    // empty slice or a wave past the segment; the partial rows of up to four
-    // waves are fetched together, then combined.
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
     float wsum = 0.f, Mrun = -INFINITY;
     const long long seg_end = P + nb;
+    // The waves that cover the segment follow from the slice bounds alone.
+    // When at most MQ of them do (the usual case), every log-sum-exp and
+    // partial row is requested at once: one memory round trip, not one per
+    // step.  An empty slice wrote no partial row, so its (stale) row is
+    // dropped by a select, never multiplied.
+    constexpr int MQ = 8;
+    int n_cov = 1;
+    while (n_cov <= MQ && w0 + n_cov < a.NW && dc_slice_start(w0 + n_cov, T, a.NW) < seg_end)
+        ++n_cov;
+    if (n_cov <= MQ) {
+        const bool mine = lane < n_cov && dc_slice_start(w0 + lane + 1, T, a.NW) >
+                                              dc_slice_start(w0 + lane, T, a.NW);
+        const float lse_l = mine ? a.lse[((size_t)(w0 + lane) + seg_global) * 16 + qcol] : -INFINITY;
+        float v[MQ][PER];
+#pragma unroll
+        for (int u = 0; u < MQ; ++u) {
+#pragma unroll
+            for (int e = 0; e < PER; ++e) v[u][e] = 0.f;
+            if (u < n_cov) {
+                const size_t slot = (size_t)(w0 + u) + seg_global;
+                const float *pp = a.opart + (slot * 16 + qcol) * D + PER * lane;
+#pragma unroll
+                for (int e = 0; e < PER; ++e) v[u][e] = pp[e];
+            }
+        }
+        float M = lse_l;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+#pragma unroll
+        for (int u = 0; u < MQ; ++u) {
+            const float lu = __shfl(lse_l, u);
+            const bool ok = u < n_cov && lu != -INFINITY;
+            const float f = ok ? fast_exp2(lu - M) : 0.f;
+            wsum += f;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] = ok ? fmaf(f, v[u][e], acc[e]) : acc[e];
+        }
+        const float inv = 1.f / wsum;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) op[e] = (__bf16)(acc[e] * inv);
+        return;
+    }
+    // More waves: rounds of 64 (one round unless more than 64 waves cover the
+    // segment): lane j holds the log-sum-exp of wave wb + j, or -inf for an
+    // empty slice or a wave past the segment; the partial rows of up to four
+    // waves are fetched together, then combined.
     for (int wb = w0; wb < a.NW && dc_slice_start(wb, T, a.NW) < seg_end; wb += 64) {
         const int wl = wb + lane;
         float lse_l = -INFINITY;
