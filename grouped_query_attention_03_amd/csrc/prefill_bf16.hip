@@ -78,6 +78,10 @@ struct PfRing {
     static constexpr int SLOT_BYTES = 2 * PfLay<D>::TILE_BYTES + MASK_BYTES;
     static constexpr int SLOTS = FORM == kPfMask ? 3 : 4;
     static constexpr int DIST = SLOTS - 1;
+    // keep-mask form: a flag byte and a 16-bit list entry per key tile, up to
+    // LIST tiles, and the per-wave counts of the list's prefix sum
+    static constexpr int LIST = FORM == kPfMask ? 4096 : 0;
+    static constexpr int LIST_BYTES = FORM == kPfMask ? LIST * 3 + 64 : 0;
 };
 
 // Mask tile rows are 64 bytes (4 chunks of 16); logical chunk c of row r sits
@@ -120,7 +124,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
     constexpr int KSTEPS = Lay::KSTEPS, DB = Lay::DB;
     constexpr int DPW = 2 * Lay::DMA_PER_TENSOR / PF_WAVES;  // direct loads per wave per tile
     constexpr int SLOTS = Ring::SLOTS, DIST = Ring::DIST, SLOT_BYTES = Ring::SLOT_BYTES;
-    __shared__ __attribute__((aligned(1024))) char smem[SLOTS * SLOT_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[SLOTS * SLOT_BYTES + Ring::LIST_BYTES];
 
     const int lane = threadIdx.x & 63, wave = wave_id();
     // Work-group -> (unit, query tile).  Dispatch sends work-group i to XCD
@@ -160,6 +164,22 @@ void prefill_bf16_kernel(PrefillArgs a) {
     const int pos0 = p0 + 32 * (wave % PB);
     const int kv_end = CAUSAL ? min(Lk, off + p0 + a.BM) : Lk;
     const int ntiles = (kv_end + PF_BN - 1) / PF_BN;
+    // The loop walks positions 0 .. npos - 1 of a list of key tiles: ring slot
+    // = position % SLOTS, keys of tile tile_of(position).  Without a mask the
+    // list is every tile, in order.  The keep-mask form lists (below) only the
+    // tiles the mask leaves visible to at least one of the work-group's rows,
+    // when it has at most Ring::LIST tiles.
+    int npos = ntiles;
+    bool use_list = false;
+    const uint16_t *tlist = reinterpret_cast<const uint16_t *>(smem + SLOTS * SLOT_BYTES +
+                                                               Ring::LIST);
+    auto tile_of = [&](int pos) -> int {
+        if constexpr (MASK) {
+            if (use_list)
+                return pos < npos ? __builtin_amdgcn_readfirstlane((int)tlist[pos]) : 0;
+        }
+        return pos;
+    };
 
     // ---- direct loads: waves 0-3 stream the K tile and waves 4-7 the V tile;
     // this wave moves 1 KiB pieces i0 .. i0 + DPW - 1 of every tile.
@@ -201,13 +221,14 @@ void prefill_bf16_kernel(PrefillArgs a) {
         const int r = 16 * wave + (lane >> 2);  // row of this lane's first piece
         moff = (unsigned)(p0 + r) * (unsigned)a.mask_row + 16u * ((lane & 3) ^ pf_mswz(r));
     }
-    // this wave's share of the loads of tile x into ring slot x % SLOTS
+    // this wave's share of the loads of list position x into ring slot x % SLOTS
     auto issue_tile = [&](int x) {
         char *slot = smem + (x % SLOTS) * SLOT_BYTES;
+        const int tx = tile_of(x);
 #pragma unroll
         for (int u = 0; u < DPW; ++u) {
             const int i = i0 + u;
-            const unsigned row0 = (unsigned)(x * PF_BN + i * Lay::ROWS_PER_DMA);
+            const unsigned row0 = (unsigned)(tx * PF_BN + i * Lay::ROWS_PER_DMA);
             dma16_to_lds_buf(rsrc, loff[u % NLO] + row0 * krb,
                              (GQA_LDS char *)(slot + (loads_v ? Lay::TILE_BYTES : 0) + i * 1024));
         }
@@ -219,29 +240,15 @@ void prefill_bf16_kernel(PrefillArgs a) {
                 if (u < mpw)
                     dma16_to_lds_buf(mrsrc,
                                      moff + (unsigned)(128 * u) * (unsigned)a.mask_row +
-                                         (unsigned)(x * PF_BN),
+                                         (unsigned)(tx * PF_BN),
                                      (GQA_LDS char *)(slot + 2 * Lay::TILE_BYTES +
                                                       (wave + 8 * u) * 1024));
         }
     };
 
-    // V rows past the sequence end meet P = 0 and must be finite: zero the V
-    // halves of the ring once, in case an out-of-range load leaves its LDS
-    // bytes untouched.
-    for (int i = threadIdx.x; i < SLOTS * Lay::TILE_BYTES / 16; i += PF_THREADS) {
-        const int sl = i / (Lay::TILE_BYTES / 16), off = i % (Lay::TILE_BYTES / 16);
-        store16_lds(smem + sl * SLOT_BYTES + Lay::TILE_BYTES + 16 * off, u32x4{0u, 0u, 0u, 0u});
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    block_barrier();
-    // Tile 0 streams in while q is read.  A zero-length sequence has no tile;
-    // its buffer range is empty, so these loads read zeros without touching
-    // memory.
-    issue_tile(0);
-
     // Q^T operand: lane holds 8 head-dim values of one query row.
     bf16x8 qf[KSTEPS];
-    {
+    auto load_q = [&]() {
         const int pos = pos0 + (lane & 31);
         if (pos < L) {
             const __bf16 *qrow = static_cast<const __bf16 *>(a.q) +
@@ -290,7 +297,114 @@ void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = bf16x8{};
         }
+    };
+    // The keep-mask form reads q first, so that its latency passes under the
+    // mask scan; the other forms read it while tile 0 streams in.
+    if constexpr (MASK) load_q();
+
+    // Keep-mask form: list the key tiles with a visible key for some row of
+    // the work-group.  Flags first, from the work-group's mask rows, only the
+    // keys each row may see (below L_k, and causally up to its position).  Then
+    // a prefix sum over the flags, 8 tiles a thread, writes the list in tile
+    // order.
+    if constexpr (MASK) {
+        if (ntiles <= Ring::LIST) {
+            use_list = true;
+            unsigned char *flags = reinterpret_cast<unsigned char *>(smem + SLOTS * SLOT_BYTES);
+            uint16_t *list = reinterpret_cast<uint16_t *>(flags + Ring::LIST);
+            int *wsum = reinterpret_cast<int *>(list + Ring::LIST);
+            static_assert(Ring::LIST == 8 * PF_THREADS, "a thread owns 8 tiles of the list");
+            reinterpret_cast<unsigned long long *>(flags)[threadIdx.x] = 0ull;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            block_barrier();
+            const uint8_t *mb = a.mask + (size_t)b * (size_t)a.mask_batch;
+            const int rows = max(0, min(a.BM, L - p0));
+            // items (row r, tile t): the row's 64 mask bytes of the tile, as four
+            // 16-byte pieces, each read only if the row may see its first key
+            // (so every read stays inside the row); four items a step, so that
+            // sixteen reads are in flight before any is tested
+            constexpr int IPS = 4;
+            const int items = rows * ntiles;
+            for (int base = threadIdx.x; base < items; base += IPS * PF_THREADS) {
+                u32x4 m[IPS][4];
+                int lim[IPS], tix[IPS];
+#pragma unroll
+                for (int u = 0; u < IPS; ++u) {
+                    const int it = base + u * PF_THREADS;
+                    const int r = it / ntiles, t = it - r * ntiles;
+                    const int row = p0 + r;
+                    const int seen = min(Lk, CAUSAL ? off + row + 1 : Lk);  // keys row may see
+                    lim[u] = it < items ? seen - PF_BN * t : 0;  // of this tile's 64 bytes
+                    tix[u] = t;
+                    const uint8_t *mp = mb + (size_t)row * (size_t)a.mask_row + PF_BN * t;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        m[u][q] = lim[u] > 16 * q ? *reinterpret_cast<const u32x4 *>(mp + 16 * q)
+                                                  : u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int u = 0; u < IPS; ++u) {
+                    unsigned any = 0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            const int nb = min(max(lim[u] - 16 * q - 4 * w, 0), 4);
+                            any |= m[u][q][w] & (nb == 4 ? 0xffffffffu : (1u << (8 * nb)) - 1u);
+                        }
+                    if (any) flags[tix[u]] = 1;
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            block_barrier();
+            const unsigned long long f8 = reinterpret_cast<const unsigned long long *>(flags)[threadIdx.x];
+            int bits = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bits |= ((f8 >> (8 * e)) & 0xffull) ? (1 << e) : 0;
+            const int cnt = __builtin_popcount(bits);
+            int incl = cnt;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int up = __shfl_up(incl, o);
+                if (lane >= o) incl += up;
+            }
+            if (lane == 63) wsum[wave] = incl;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            block_barrier();
+            int base = 0, total = 0;
+#pragma unroll
+            for (int w = 0; w < PF_WAVES; ++w) {
+                const int ws = wsum[w];
+                base += w < wave ? ws : 0;
+                total += ws;
+            }
+            int at = base + incl - cnt;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (bits & (1 << e)) list[at++] = (uint16_t)(8 * threadIdx.x + e);
+            npos = __builtin_amdgcn_readfirstlane(total);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            block_barrier();
+        }
     }
+
+    // V rows past the sequence end meet P = 0 and must be finite: zero the V
+    // halves of the ring once, in case an out-of-range load leaves its LDS
+    // bytes untouched.
+    for (int i = threadIdx.x; i < SLOTS * Lay::TILE_BYTES / 16; i += PF_THREADS) {
+        const int sl = i / (Lay::TILE_BYTES / 16), off = i % (Lay::TILE_BYTES / 16);
+        store16_lds(smem + sl * SLOT_BYTES + Lay::TILE_BYTES + 16 * off, u32x4{0u, 0u, 0u, 0u});
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    block_barrier();
+    // Tile 0 streams in while q is read.  A zero-length sequence has no tile;
+    // its buffer range is empty, so these loads read zeros without touching
+    // memory.
+    issue_tile(0);
+
+    // q has been read (in the keep-mask form, before the mask scan) or is
+    // read here while tile 0 streams in.
+    if constexpr (!MASK) load_q();
 
     f32x16 acc[DB];
 #pragma unroll
@@ -306,7 +420,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
     bf16x8 pb[2][2];  // P^T of the current tile: [key block][16-key half]
     float m_run = -INFINITY, l_run = 0.f;
     const bool has_rows = pos0 < L;
-    auto active = [&](int j) { return has_rows && (!CAUSAL || j * PF_BN <= off + pos0 + 31); };
+    // whether this wave's rows may see a key of tile t
+    auto active = [&](int t) { return has_rows && (!CAUSAL || t * PF_BN <= off + pos0 + 31); };
 
     // LDS operand reads for step st of the two products (16-byte K chunk;
     // transposed V pair); st runs over (k-step, key block) for QK and over
@@ -382,8 +497,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // The max is raised (and O, l rescaled) only when a row's new max exceeds
     // mu by more than TAU, or when the row sees its first key.
     // full_tile (keep-mask form): every mask byte of the tile is nonzero.
-    auto softmax = [&](int j, bool full_tile) {
-        const int j0 = j * PF_BN;
+    auto softmax = [&](int j, int tile, bool full_tile) {  // list position j, key tile
+        const int j0 = tile * PF_BN;
         if ((MASK && !full_tile) || j0 + PF_BN > Lk || (CAUSAL && j0 + PF_BN - 1 > off + pos0)) {
             pf_keep_branch();  // only diagonal, tail and partly hidden tiles pay for it
             if constexpr (MASK) {
@@ -478,7 +593,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
     pf_settle(qf);
 #pragma unroll
     for (int x = 1; x < DIST; ++x)
-        if (x < ntiles) issue_tile(x);
+        if (x < npos) issue_tile(x);
     // Tile x has landed once at most the loads issued after it are pending:
     // those of tiles x + 1 .. x + DIST - 1 that exist, opw a tile.  Without the
     // mask every wave issues DPW loads a tile and the counts are immediates.
@@ -492,11 +607,12 @@ void prefill_bf16_kernel(PrefillArgs a) {
             else wait_vmcnt<0>();
         }
     };
-    wait_tile(min(ntiles, DIST) - 1);
+    wait_tile(min(npos, DIST) - 1);
     block_barrier();
-    for (int j = 0; j < ntiles; ++j) {
-        if (j + DIST < ntiles) issue_tile(j + DIST);
-        if (active(j)) {
+    for (int j = 0; j < npos; ++j) {
+        if (j + DIST < npos) issue_tile(j + DIST);
+        const int t = tile_of(j);
+        if (active(t)) {
             bool go = true, full = true;
             if constexpr (MASK) {
                 // skip a tile whose mask hides every key from this wave's rows
@@ -516,12 +632,12 @@ void prefill_bf16_kernel(PrefillArgs a) {
                     vload(j);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                softmax(j, full);
+                softmax(j, t, full);
                 pv(j);
             }
         }
         // tile j + 1 must have landed; tiles j + 2 .. j + DIST may be pending
-        wait_tile(max(min(ntiles - 1, j + DIST) - (j + 1), 0));
+        wait_tile(max(min(npos - 1, j + DIST) - (j + 1), 0));
         block_barrier();
     }
 
