@@ -1120,6 +1120,49 @@ def test_prefill_mask_lengths_is_varlen(dev):
         assert torch.equal(a, b)
 
 
+def _scattered_mask(B, Lq, Lk, period, density, hidden_rows, seed):
+    """Keys visible only in key tiles t with t % period == 2 (with the given
+    density inside them), and rows [0, hidden_rows) of every sequence see no
+    key: a work-group's list of visible tiles has gaps, and the work-groups
+    of the hidden rows list none."""
+    m = wl.random_mask((B, Lq, Lk), density, seed)
+    tile = torch.arange(Lk) // 64
+    m = m * (tile % period == 2).to(torch.uint8)[None, None, :]
+    m[:, :hidden_rows] = 0
+    return m
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("d", [128, 64])
+def test_prefill_mask_scattered_tiles(causal, d, dev):
+    """Only every fifth key tile holds visible keys: the list of tiles a
+    work-group walks skips the others, so ring slots follow list positions,
+    not tile indices; rows 0..95 see nothing (whole work-groups with an
+    empty list)."""
+    B, Lq, Lk, h_q, h_kv = 2, 700, 1500, 8, 2
+    q, k, v = wl.prefill_chunk_inputs(B, Lq, Lk, h_q, h_kv, d, 5400 + d)
+    m = _scattered_mask(B, Lq, Lk, 5, 0.5, 96, 5401)
+    say(f"prefill_mask scattered tiles d={d} causal={causal}")
+    out = run_prefill_mask(q, k, v, m, causal, 0.1, dev)
+    ref = oracle.prefill_mask(f64(q), f64(k), f64(v), m.numpy(), causal, 0.1)
+    check(f64(out), ref, "bf16", f"scattered tiles d={d} causal={causal}")
+    assert torch.all(out[:, :96].cpu() == 0), "rows that see no key must be zero"
+
+
+def test_prefill_mask_long_rows_list_every_tile(dev):
+    """Rows of more than 4096 key tiles (262,244 keys): the work-group lists
+    every tile instead of scanning, and the result still matches."""
+    B, Lq, Lk, h_q, h_kv, d = 1, 40, 4096 * 64 + 100, 4, 1, 64
+    q, k, v = wl.prefill_chunk_inputs(B, Lq, Lk, h_q, h_kv, d, 5500)
+    m = wl.random_mask((B, Lq, Lk), 0.002, 5501)
+    m[:, 5] = 0
+    say("prefill_mask with 4098 key tiles per row")
+    out = run_prefill_mask(q, k, v, m, False, 0.125, dev)
+    ref = oracle.prefill_mask(f64(q), f64(k), f64(v), m.numpy(), False, 0.125)
+    check(f64(out), ref, "bf16", "4098 key tiles per row")
+    assert torch.all(out[:, 5].cpu() == 0)
+
+
 def test_workload_document_masked_prefill(dev):
     """The packed-documents workload at full size, every output against the oracle."""
     w = wl.WORKLOADS["document_masked_prefill_bf16"]
