@@ -14,8 +14,11 @@ step runs untimed for --settle-seconds (default 0.5 s) so the GPU reaches its
 working clocks; then K steps are timed back to back between two device
 synchronisations; ``value`` is the algorithmic TFLOP/s of that timed region
 (4 * B * h_q * d * visible (query, key) pairs per step; causal counts
-L(L+1)/2 pairs per head).  K more steps follow, each between two HIP events on
-the launch stream, for the kernel's average duration in ``roofline``.
+L(L+1)/2 pairs per head).  K more steps follow back to back between one pair
+of HIP events on the launch stream, for the kernel's average duration in
+``roofline`` (a kernel trace of the run's last K dispatches covers exactly
+these); K steps timed one by one with events before them give
+``kernel_ms_min``.
 
 The other prefill workloads named by --extra-prefill (default: the pages'
 worked example, the Llama-2-shaped causal layer and the packed-documents
