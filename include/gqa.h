@@ -186,9 +186,10 @@ gqa_status gqa_prefill_rope(const void *q, const void *k, const void *v, const f
  * token's key/value before attending, which the caller has already done).
  *   q, o               : [B, 1, h_q, d]  bf16
  *   k_cache, v_cache   : [B, h_kv, S, d] bf16
- *   seqlens            : [B] int32 on the device, each in [0, S]; not checked on
- *                        the device (a value above S reads past the sequence's
- *                        cache rows).  seqlens[b] == 0 yields a zero output row.
+ *   seqlens            : [B] int32 on the device, each in [0, S].  The kernels
+ *                        clamp a value outside that range into it, so no row
+ *                        outside the sequence's cache is ever read.
+ *                        seqlens[b] == 0 yields a zero output row.
  *                        Cache rows at or beyond seqlens[b] are never read.
  *   scale is fixed to 1/sqrt(d).
  *   num_splits: how many slices the valid cache blocks are cut into (one wave
@@ -259,7 +260,8 @@ gqa_status gqa_decode_token_major(const void *q, const void *k_cache, const void
  *                      page_size) are never read; the others must name blocks
  *                      of the pool (not checked on the device).  Blocks may be
  *                      shared between sequences (a common prefix).
- *   seqlens          : [B] int32 on the device, each in [0, max_blocks * page_size].
+ *   seqlens          : [B] int32 on the device, each in [0, max_blocks * page_size]
+ *                      (clamped into that range on the device, as in gqa_decode).
  *   page_size        : a positive multiple of 32; max_blocks > 0;
  *                      max_blocks * page_size and B * max_blocks below 2^31,
  *                      else GQA_ERR_SIZE.
@@ -284,9 +286,9 @@ gqa_status gqa_decode_paged(const void *q, const void *k_pages, const void *v_pa
  *   seqlens          : [B] int32 on the device, the lengths BEFORE the append,
  *                      each in [0, S - 1]; the token attends over rows
  *                      [0, seqlens[b] + 1).  The caller advances seqlens.
- *                      Not checked on the device: for seqlens[b] >= S nothing is
- *                      written for that sequence (and values above S read past
- *                      its cache rows, as in gqa_decode).
+ *                      A value outside [0, S - 1] is clamped into it for the
+ *                      attention (the clamped length's rows, then the new row)
+ *                      and nothing is written into that sequence's cache.
  *   Other arguments, the workspace and errors as gqa_decode; the workspace size
  *   is gqa_decode_workspace_bytes of the same sizes.  The new rows are read
  *   from k_new / v_new for the attention, so no part of the call depends on

@@ -447,6 +447,43 @@ def test_decode_is_deterministic(dev):
     assert torch.equal(run_decode(seqlens, q, kc, vc, dev), run_decode(seqlens, q, kc, vc, dev))
 
 
+def test_decode_lengths_outside_their_range_are_clamped(dev):
+    """A length outside [0, S] is clamped into it on the device: the result is
+    that of the clamped length, bit for bit, in the head-major, paged and
+    append forms, and the append writes nothing for such a sequence."""
+    B, h_q, h_kv, S, d, P = 6, 32, 8, 320, 128, 64
+    big = 2 ** 31 - 1
+    seqlens, q, kc, vc = wl.decode_inputs(B, h_q, h_kv, S, d, 4200, (1, S))
+    lens = torch.tensor([S + 5, -7, S, big, 0, 150], dtype=torch.int32)
+    clamped = lens.clamp(0, S)
+    say(f"decode lengths {lens.tolist()} against {clamped.tolist()}")
+    out = run_decode(lens, q, kc, vc, dev)
+    assert torch.equal(out, run_decode(clamped, q, kc, vc, dev))
+    # paged: every table entry names a page, so the clamped length may use them all
+    kp, vp, table = wl.to_pages(kc, vc, torch.full((B,), S, dtype=torch.int32), P, 4201)
+    kp, vp, table = kp.to(dev), vp.to(dev), table.to(dev)
+    qd = q.to(dev)
+    o1 = gqa.decode_paged(qd, kp, vp, table, lens.to(dev))
+    o2 = gqa.decode_paged(qd, kp, vp, table, clamped.to(dev))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(o1, out)
+    # append: lengths before the append belong in [0, S - 1]
+    _, q, kn, vn, kc, vc = wl.decode_append_inputs(B, h_q, h_kv, S, d, 4202, (0, S - 1))
+    lens = torch.tensor([S, -3, S - 1, big, 0, 150], dtype=torch.int32)
+    clamped = lens.clamp(0, S - 1)
+    outside = (lens < 0) | (lens > S - 1)
+    say(f"decode_append lengths {lens.tolist()} against {clamped.tolist()}")
+    o1, kc1, vc1 = run_decode_append(lens, q, kn, vn, kc, vc, dev)
+    o2, kc2, vc2 = run_decode_append(clamped, q, kn, vn, kc, vc, dev)
+    assert torch.equal(o1, o2)
+    for b in range(B):
+        if outside[b]:  # nothing written
+            assert torch.equal(kc1[b], kc[b]) and torch.equal(vc1[b], vc[b]), f"sequence {b}"
+        else:
+            assert torch.equal(kc1[b], kc2[b]) and torch.equal(vc1[b], vc2[b]), f"sequence {b}"
+
+
 def test_decode_equals_last_row_of_causal_prefill(dev):
     B, L, h_q, h_kv, d = 2, 777, 32, 8, 128
     q, k, v = wl.prefill_inputs(B, L, h_q, h_kv, d, 43, 1.0, torch.bfloat16)
