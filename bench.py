@@ -226,9 +226,12 @@ def bench_prefill(w, steps, warmup, settle_s=0.0):
     elif w.path == "prefill_mask":
         mask_cpu = wl.workload_inputs(w)[3]
         mask = ins[3]
+        mws = torch.empty(gqa.prefill_mask_workspace_bytes(w.B, w.L, w.Lk or w.L),
+                          dtype=torch.uint8, device=dev)
 
-        def step():
-            gqa.prefill_mask(q, k, v, mask, causal=w.causal, scale=w.scale, out=out)
+        def step():  # two kernels: the mask's summary, then the prefill
+            gqa.prefill_mask(q, k, v, mask, causal=w.causal, scale=w.scale, out=out,
+                             workspace=mws)
     elif w.path == "prefill_rope":  # two kernels: the key rotation, then the prefill
         cos, sin = ins[3:]
         k_rot = torch.empty_like(k)

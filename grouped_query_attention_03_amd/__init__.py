@@ -94,8 +94,11 @@ def lib() -> ctypes.CDLL:
     L.gqa_prefill_varlen.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P]
     L.gqa_prefill_varlen.restype = I
     LL = ctypes.c_longlong
-    L.gqa_prefill_mask.argtypes = [P, P, P, P, LL, LL, P, I, I, I, I, I, I, I, I, F, P]
+    SZ = ctypes.c_size_t
+    L.gqa_prefill_mask.argtypes = [P, P, P, P, LL, LL, P, I, I, I, I, I, I, I, I, F, P, SZ, P]
     L.gqa_prefill_mask.restype = I
+    L.gqa_prefill_mask_workspace_bytes.argtypes = [I, I, I]
+    L.gqa_prefill_mask_workspace_bytes.restype = ctypes.c_size_t
     L.gqa_prefill_rope.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
     L.gqa_prefill_rope.restype = I
     L.gqa_decode_append_rope.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P,
@@ -492,13 +495,19 @@ def mask_layout(mask: torch.Tensor, B: int, Lq: int, Lk: int):
     return m, sr, sb
 
 
-def prefill_mask(q, k, v, mask, *, causal: bool, scale=None, out=None):
+def prefill_mask_workspace_bytes(B: int, L_q: int, L_k: int) -> int:
+    return int(lib().gqa_prefill_mask_workspace_bytes(B, L_q, L_k))
+
+
+def prefill_mask(q, k, v, mask, *, causal: bool, scale=None, out=None, workspace=None):
     """Prefill with a keep-mask.  q [B,L_q,h_q,d], k/v [B,L_k,h_kv,d] (L_q <=
     L_k, causal rows bottom-right aligned as in prefill_chunk), mask
     [B,L_q,L_k] or [L_q,L_k] (shared by the batch), bool or uint8 on the GPU:
     key j is visible to query row i of sequence b only where the mask is
     nonzero.  A row with no visible key is zero.  k and v must be finite
     everywhere (a hidden key has weight exactly 0, and 0 * NaN is NaN).
+    workspace: a GPU tensor of at least prefill_mask_workspace_bytes(B, L_q,
+    L_k) bytes for the mask's summary, or None for a new one.
     -> o [B,L_q,h_q,d]."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, 4)
@@ -523,9 +532,12 @@ def prefill_mask(q, k, v, mask, *, causal: bool, scale=None, out=None):
     if out is None:
         out = torch.empty_like(q)
     _check_out(out, q)
+    need = prefill_mask_workspace_bytes(B, Lq, Lk)
+    workspace = _workspace(workspace, need, q)
     st = lib().gqa_prefill_mask(q.data_ptr(), k.data_ptr(), v.data_ptr(), m.data_ptr(),
                                 int(row_stride), int(batch_stride), out.data_ptr(), B, Lq, Lk,
                                 h_q, h_kv, d, _dtype_code(q), int(bool(causal)), float(scale),
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                 _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_prefill_mask")

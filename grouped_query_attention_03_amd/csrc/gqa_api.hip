@@ -90,6 +90,10 @@ const char *gqa_status_string(gqa_status s) {
 
 namespace {
 
+// Bytes of one row of the keep-mask summary: a byte per 64-key tile, rounded
+// up to a multiple of 8.
+int mask_summary_stride(int Lk) { return ((Lk + 63) / 64 + 7) / 8 * 8; }
+
 // Shared by both prefill entry points: Lq query positions per sequence attend
 // to Lk >= Lq keys, query row i sitting at position Lk - Lq + i.
 // The rotary form passes tables cos, sin [Lk][d/2] and the k_rot output: the
@@ -101,7 +105,8 @@ gqa_status prefill_impl(const void *q, const void *k, const void *v, void *o, in
                         bool rope = false, const int32_t *kv_lens = nullptr,
                         bool varlen = false, const uint8_t *mask = nullptr,
                         long long mask_row = 0, long long mask_batch = 0,
-                        bool masked = false) {
+                        bool masked = false, void *workspace = nullptr,
+                        size_t workspace_bytes = 0) {
     if (!q || !k || !v || !o) return GQA_ERR_NULL_POINTER;
     if (masked) {
         if (!mask) return GQA_ERR_NULL_POINTER;
@@ -165,6 +170,21 @@ gqa_status prefill_impl(const void *q, const void *k, const void *v, void *o, in
         a.fold = frexpf(a.c, &e) == 0.5f ? 1 : 0;
     }
     if ((int64_t)a.n_units * a.n_qtiles > 0x7fffffff) return GQA_ERR_SIZE;
+    a.mcodes = nullptr;
+    a.morder = nullptr;
+    a.mc_stride = 0;
+    if (masked) {
+        const size_t need = gqa_prefill_mask_workspace_bytes(B, Lq, Lk);
+        if (need == 0) return GQA_ERR_SIZE;
+        if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+            return GQA_ERR_WORKSPACE;
+        // laid out for the most query tiles any head count gives (32 rows each)
+        a.mcodes = static_cast<uint8_t *>(workspace);
+        a.mc_stride = mask_summary_stride(Lk);
+        a.morder = reinterpret_cast<int32_t *>(
+            static_cast<char *>(workspace) +
+            round_up_256((size_t)B * ((Lq + 31) / 32) * (size_t)a.mc_stride));
+    }
 
     gqa_status st = check_device();
     if (st != GQA_OK) return st;
@@ -225,10 +245,17 @@ gqa_status gqa_prefill_varlen(const void *q, const void *k, const void *v, void 
 gqa_status gqa_prefill_mask(const void *q, const void *k, const void *v, const uint8_t *mask,
                             long long mask_row_stride, long long mask_batch_stride, void *o,
                             int B, int L_q, int L_k, int h_q, int h_kv, int d, gqa_dtype dt,
-                            int causal, float scale, void *hip_stream) {
+                            int causal, float scale, void *workspace, size_t workspace_bytes,
+                            void *hip_stream) {
     return prefill_impl(q, k, v, o, B, L_q, L_k, h_q, h_kv, d, dt, causal, scale, hip_stream,
                         nullptr, nullptr, nullptr, false, nullptr, false, mask, mask_row_stride,
-                        mask_batch_stride, true);
+                        mask_batch_stride, true, workspace, workspace_bytes);
+}
+
+size_t gqa_prefill_mask_workspace_bytes(int B, int L_q, int L_k) {
+    if (B <= 0 || L_q <= 0 || L_k < L_q) return 0;
+    const size_t tiles = (size_t)B * (size_t)((L_q + 31) / 32);  // at most, 32 rows a tile
+    return round_up_256(tiles * (size_t)mask_summary_stride(L_k)) + round_up_256(tiles * 4);
 }
 
 int gqa_decode_default_splits(void) { return kDefaultSplits; }

@@ -33,6 +33,14 @@ struct PrefillArgs {
     // mask_row a multiple of 16, L * mask_row < 2^32)
     const uint8_t *mask;
     long long mask_row, mask_batch;
+    // keep-mask form, bf16: the mask's summary per (sequence, query tile,
+    // 64-key tile), [B][n_qtiles][mc_stride] bytes (mc_stride = ceil(L_k / 64)
+    // rounded up to a multiple of 8), and the order [B * n_qtiles] in which
+    // the prefill takes the (sequence, query tile) items, both written by
+    // first passes and read by the prefill
+    uint8_t *mcodes;
+    int32_t *morder;
+    int mc_stride;
 };
 
 // Rotary embedding of rows x [rows][d] into out, tables cos, sin [L][d/2].

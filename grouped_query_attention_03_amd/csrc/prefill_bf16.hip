@@ -49,10 +49,18 @@
 //   operand), so S arrives in log2 units already shifted by the running max;
 //   row sums are taken with v_dot2_f32_bf16 on the bf16-rounded P that the PV
 //   product uses.
-//   Keep-mask form: the mask bytes of the work-group's rows for each key tile
-//   are moved into the same ring slot by the same direct loads (a 3-slot ring,
+//   Keep-mask form: a first pass sums the mask up per query tile (the rows of
+//   a work-group) and 64-key tile: none, some or all of the keys the rows may
+//   see are visible.  It runs once per call, not once per key/value head.  A
+//   second, one-work-group pass orders the query tiles by how many key tiles
+//   they see, most first, and the prefill's work-groups take their query
+//   tiles in that order, so the longest lists start first.  A work-group
+//   lists the key tiles some row of it sees, from that summary, and walks
+//   only those.  The
+//   mask bytes of its rows for a listed tile that is not wholly visible are
+//   moved into the tile's ring slot by the same direct loads (a 3-slot ring,
 //   since a slot then also holds up to 256 rows x 64 bytes of mask); a wave
-//   whose 32 rows see no key of a tile skips that tile's products.
+//   whose 32 rows see no key of such a tile skips that tile's products.
 //   Causal: tiles wholly above the diagonal are never loaded or computed; the
 //   diagonal and the sequence tail are masked element-wise.
 //   Work-groups map to XCDs so that a key/value head's tiles share one L2, and
@@ -78,10 +86,11 @@ struct PfRing {
     static constexpr int SLOT_BYTES = 2 * PfLay<D>::TILE_BYTES + MASK_BYTES;
     static constexpr int SLOTS = FORM == kPfMask ? 3 : 4;
     static constexpr int DIST = SLOTS - 1;
-    // keep-mask form: a flag byte and a 16-bit list entry per key tile, up to
+    // keep-mask form: a 16-bit list entry per key tile (the tile, and in bit
+    // 15 whether all its keys are visible to the work-group's rows), up to
     // LIST tiles, and the per-wave counts of the list's prefix sum
     static constexpr int LIST = FORM == kPfMask ? 4096 : 0;
-    static constexpr int LIST_BYTES = FORM == kPfMask ? LIST * 3 + 64 : 0;
+    static constexpr int LIST_BYTES = FORM == kPfMask ? LIST * 2 + 64 : 0;
 };
 
 // Mask tile rows are 64 bytes (4 chunks of 16); logical chunk c of row r sits
@@ -134,8 +143,16 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // units instead, longest first: with a multiple of 8 units each unit still
     // stays on one XCD, and otherwise (one head, say) every XCD still gets an
     // equal mix of long and short tiles.
+    // The keep-mask form takes its (sequence, query tile) from the order the
+    // summary passes wrote, the work-groups of one of them (its key/value
+    // heads and head subgroups) in a row.
     int unit, qt;
-    if (CAUSAL || VARLEN || MASK) {
+    if (MASK) {
+        const int hpi = a.h_kv * a.nsub;  // work-groups per (sequence, query tile)
+        const int item = load_const(a.morder, blockIdx.x / hpi);
+        qt = item % a.n_qtiles;
+        unit = (item / a.n_qtiles) * hpi + blockIdx.x % hpi;
+    } else if (CAUSAL || VARLEN) {
         unit = blockIdx.x % a.n_units;
         qt = blockIdx.x / a.n_units;
     } else {
@@ -143,7 +160,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
         unit = lid / a.n_qtiles;
         qt = lid % a.n_qtiles;
     }
-    if (CAUSAL) qt = a.n_qtiles - 1 - qt;  // longest rows first
+    if (CAUSAL && !MASK) qt = a.n_qtiles - 1 - qt;  // longest rows first
     // The integer divisions above and below run partly on the vector ALU; their
     // wave-uniform results are moved to scalar registers, so they do not hold
     // vector registers for the whole kernel.
@@ -168,17 +185,26 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // = position % SLOTS, keys of tile tile_of(position).  Without a mask the
     // list is every tile, in order.  The keep-mask form lists (below) only the
     // tiles the mask leaves visible to at least one of the work-group's rows,
-    // when it has at most Ring::LIST tiles.
+    // when it has at most Ring::LIST tiles; full_of(position) says that every
+    // key of the tile that a row of the work-group may see is visible to it,
+    // so its mask bytes are neither loaded nor applied.
     int npos = ntiles;
     bool use_list = false;
-    const uint16_t *tlist = reinterpret_cast<const uint16_t *>(smem + SLOTS * SLOT_BYTES +
-                                                               Ring::LIST);
+    const uint16_t *tlist = reinterpret_cast<const uint16_t *>(smem + SLOTS * SLOT_BYTES);
+    auto entry_of = [&](int pos) -> int {
+        return pos < npos ? __builtin_amdgcn_readfirstlane((int)tlist[pos]) : 0;
+    };
     auto tile_of = [&](int pos) -> int {
         if constexpr (MASK) {
-            if (use_list)
-                return pos < npos ? __builtin_amdgcn_readfirstlane((int)tlist[pos]) : 0;
+            if (use_list) return entry_of(pos) & 0x7fff;
         }
         return pos;
+    };
+    auto full_of = [&](int pos) -> bool {
+        if constexpr (MASK) {
+            if (use_list) return (entry_of(pos) >> 15) != 0;
+        }
+        return false;
     };
 
     // ---- direct loads: waves 0-3 stream the K tile and waves 4-7 the V tile;
@@ -235,9 +261,10 @@ void prefill_bf16_kernel(PrefillArgs a) {
         if constexpr (MASK) {
             // piece i = wave + 8 u covers rows 16 i .. 16 i + 15; the swizzle of
             // row r depends on r % 16 only, so one lane offset serves both pieces
+            const int n_mask = full_of(x) ? 0 : mpw;
 #pragma unroll
             for (int u = 0; u < 2; ++u)
-                if (u < mpw)
+                if (u < n_mask)
                     dma16_to_lds_buf(mrsrc,
                                      moff + (unsigned)(128 * u) * (unsigned)a.mask_row +
                                          (unsigned)(tx * PF_BN),
@@ -298,69 +325,38 @@ void prefill_bf16_kernel(PrefillArgs a) {
             for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = bf16x8{};
         }
     };
-    // The keep-mask form reads q first, so that its latency passes under the
-    // mask scan; the other forms read it while tile 0 streams in.
-    if constexpr (MASK) load_q();
+    // The keep-mask form reads its summary row first and q right after, so
+    // that q's latency passes under the list's construction (which waits for
+    // the summary only); the other forms read q while tile 0 streams in.
+    unsigned long long c8 = 0ull;  // keep-mask form: this thread's 8 tiles' summary bytes
+    if constexpr (MASK) {
+        const int t0 = 8 * threadIdx.x;
+        // a summary row is a multiple of 8 bytes long, so 8 tiles are one
+        // aligned load
+        if (ntiles <= Ring::LIST && t0 < ntiles)
+            c8 = *reinterpret_cast<const unsigned long long *>(
+                a.mcodes + ((size_t)b * a.n_qtiles + qt) * a.mc_stride + t0);
+        load_q();
+    }
 
     // Keep-mask form: list the key tiles with a visible key for some row of
-    // the work-group.  Flags first, from the work-group's mask rows, only the
-    // keys each row may see (below L_k, and causally up to its position).  Then
-    // a prefix sum over the flags, 8 tiles a thread, writes the list in tile
-    // order.
+    // the work-group, from the summary of its query tile (bit 0: some key
+    // visible; bit 1: every key its rows may see visible), 8 tiles a thread,
+    // then a prefix sum over the tiles kept writes the list in tile order.
     if constexpr (MASK) {
         if (ntiles <= Ring::LIST) {
             use_list = true;
-            unsigned char *flags = reinterpret_cast<unsigned char *>(smem + SLOTS * SLOT_BYTES);
-            uint16_t *list = reinterpret_cast<uint16_t *>(flags + Ring::LIST);
+            uint16_t *list = reinterpret_cast<uint16_t *>(smem + SLOTS * SLOT_BYTES);
             int *wsum = reinterpret_cast<int *>(list + Ring::LIST);
             static_assert(Ring::LIST == 8 * PF_THREADS, "a thread owns 8 tiles of the list");
-            reinterpret_cast<unsigned long long *>(flags)[threadIdx.x] = 0ull;
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            block_barrier();
-            const uint8_t *mb = a.mask + (size_t)b * (size_t)a.mask_batch;
-            const int rows = max(0, min(a.BM, L - p0));
-            // items (row r, tile t): the row's 64 mask bytes of the tile, as four
-            // 16-byte pieces, each read only if the row may see its first key
-            // (so every read stays inside the row); four items a step, so that
-            // sixteen reads are in flight before any is tested
-            constexpr int IPS = 4;
-            const int items = rows * ntiles;
-            for (int base = threadIdx.x; base < items; base += IPS * PF_THREADS) {
-                u32x4 m[IPS][4];
-                int lim[IPS], tix[IPS];
+            const int t0 = 8 * threadIdx.x;
+            int bits = 0, fbits = 0;
 #pragma unroll
-                for (int u = 0; u < IPS; ++u) {
-                    const int it = base + u * PF_THREADS;
-                    const int r = it / ntiles, t = it - r * ntiles;
-                    const int row = p0 + r;
-                    const int seen = min(Lk, CAUSAL ? off + row + 1 : Lk);  // keys row may see
-                    lim[u] = it < items ? seen - PF_BN * t : 0;  // of this tile's 64 bytes
-                    tix[u] = t;
-                    const uint8_t *mp = mb + (size_t)row * (size_t)a.mask_row + PF_BN * t;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        m[u][q] = lim[u] > 16 * q ? *reinterpret_cast<const u32x4 *>(mp + 16 * q)
-                                                  : u32x4{0u, 0u, 0u, 0u};
-                }
-#pragma unroll
-                for (int u = 0; u < IPS; ++u) {
-                    unsigned any = 0;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-#pragma unroll
-                        for (int w = 0; w < 4; ++w) {
-                            const int nb = min(max(lim[u] - 16 * q - 4 * w, 0), 4);
-                            any |= m[u][q][w] & (nb == 4 ? 0xffffffffu : (1u << (8 * nb)) - 1u);
-                        }
-                    if (any) flags[tix[u]] = 1;
-                }
+            for (int e = 0; e < 8; ++e) {
+                const bool in = t0 + e < ntiles;
+                bits |= (in && ((c8 >> (8 * e)) & 1ull)) ? (1 << e) : 0;
+                fbits |= ((c8 >> (8 * e + 1)) & 1ull) ? (1 << e) : 0;
             }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            block_barrier();
-            const unsigned long long f8 = reinterpret_cast<const unsigned long long *>(flags)[threadIdx.x];
-            int bits = 0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bits |= ((f8 >> (8 * e)) & 0xffull) ? (1 << e) : 0;
             const int cnt = __builtin_popcount(bits);
             int incl = cnt;
 #pragma unroll
@@ -381,7 +377,8 @@ void prefill_bf16_kernel(PrefillArgs a) {
             int at = base + incl - cnt;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                if (bits & (1 << e)) list[at++] = (uint16_t)(8 * threadIdx.x + e);
+                if (bits & (1 << e))
+                    list[at++] = (uint16_t)((t0 + e) | ((fbits >> e) & 1 ? 0x8000 : 0));
             npos = __builtin_amdgcn_readfirstlane(total);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             block_barrier();
@@ -503,9 +500,16 @@ void prefill_bf16_kernel(PrefillArgs a) {
             pf_keep_branch();  // only diagonal, tail and partly hidden tiles pay for it
             if constexpr (MASK) {
                 // read again here rather than kept in registers since the
-                // tile test (the empty asm keeps the two reads apart)
+                // tile test (the empty asm keeps the two reads apart); a tile
+                // whose keys are all visible to the work-group's rows has no
+                // mask bytes in its slot and needs none
                 asm volatile("" ::: "memory");
-                mask_read(j);
+                if (!full_tile) {
+                    mask_read(j);
+                } else {
+#pragma unroll
+                    for (int g = 0; g < 8; ++g) mk[g] = 0xffffffffu;
+                }
             }
             const int pos = pos0 + (lane & 31);
 #pragma unroll
@@ -595,11 +599,17 @@ void prefill_bf16_kernel(PrefillArgs a) {
     for (int x = 1; x < DIST; ++x)
         if (x < npos) issue_tile(x);
     // Tile x has landed once at most the loads issued after it are pending:
-    // those of tiles x + 1 .. x + DIST - 1 that exist, opw a tile.  Without the
-    // mask every wave issues DPW loads a tile and the counts are immediates.
-    auto wait_tile = [&](int pending) {
+    // those of tiles x + 1 .. x + DIST - 1 that exist.  Without the mask every
+    // wave issues DPW loads a tile and the counts are immediates; with it, a
+    // tile issues opw, or DPW when its mask bytes are not loaded.
+    // pending: how many of those exist; x: the tile's list position.
+    auto wait_tile = [&](int pending, int x) {
         if constexpr (MASK) {
-            wait_vmcnt_rt(pending * opw);
+            int n = 0;
+#pragma unroll
+            for (int y = 1; y < DIST; ++y)
+                if (y <= pending) n += full_of(x + y) ? DPW : opw;
+            wait_vmcnt_rt(n);
         } else {
             static_assert(DIST == 3, "the immediate waits assume a prefetch distance of 3");
             if (pending >= 2) wait_vmcnt<2 * DPW>();
@@ -607,14 +617,14 @@ void prefill_bf16_kernel(PrefillArgs a) {
             else wait_vmcnt<0>();
         }
     };
-    wait_tile(min(npos, DIST) - 1);
+    wait_tile(min(npos, DIST) - 1, 0);
     block_barrier();
     for (int j = 0; j < npos; ++j) {
         if (j + DIST < npos) issue_tile(j + DIST);
         const int t = tile_of(j);
         if (active(t)) {
             bool go = true, full = true;
-            if constexpr (MASK) {
+            if (MASK && !full_of(j)) {
                 // skip a tile whose mask hides every key from this wave's rows
                 mask_read(j);
                 unsigned any = 0, zero = 0;
@@ -637,7 +647,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
             }
         }
         // tile j + 1 must have landed; tiles j + 2 .. j + DIST may be pending
-        wait_tile(max(min(npos - 1, j + DIST) - (j + 1), 0));
+        wait_tile(max(min(npos - 1, j + DIST) - (j + 1), 0), j + 1);
         block_barrier();
     }
 
@@ -687,6 +697,101 @@ void prefill_bf16_kernel(PrefillArgs a) {
     }
 }
 
+// Keep-mask summary: one wave per (sequence b, query tile qt of BM rows,
+// 64-key tile t) writes mcodes[(b * n_qtiles + qt) * mc_stride + t]: bit 0
+// set when some row of the query tile (below L) has a visible key among those
+// it may see in the key tile (below L_k, and causally up to its position),
+// bit 1 set when every such key is visible (also when the rows may see none
+// of the tile's keys).  Lane l reads 32 bytes of row 32 p + l / 2 of the
+// query tile in pass p, only where the row may see a key of them, so every
+// read stays inside the row's first L_k bytes rounded up to 16.
+__global__ __launch_bounds__(256) void mask_summary_kernel(PrefillArgs a, bool causal) {
+    const int lane = threadIdx.x & 63;
+    const long long id = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nkt = (a.Lk + PF_BN - 1) / PF_BN;
+    const long long item = id / nkt;  // b * n_qtiles + qt
+    if (item >= (long long)a.B * a.n_qtiles) return;
+    const int t = (int)(id % nkt);
+    const int qt = (int)(item % a.n_qtiles), b = (int)(item / a.n_qtiles);
+    const int k0 = PF_BN * t + 32 * (lane & 1);
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    bool any = false, hole = false;
+    for (int p = 0; p < a.BM / 32; ++p) {
+        const int row = qt * a.BM + 32 * p + (lane >> 1);
+        const int seen = row < a.L ? min(a.Lk, causal ? a.off + row + 1 : a.Lk) : 0;
+        const int lim = min(max(seen - k0, 0), 32);  // bytes of this lane that count
+        const uint8_t *mp = a.mask + (size_t)b * (size_t)a.mask_batch +
+                            (size_t)row * (size_t)a.mask_row + k0;
+        const u32x4 m0 = lim > 0 ? load16(mp) : z;
+        const u32x4 m1 = lim > 16 ? load16(mp + 16) : z;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            const unsigned x = w < 4 ? m0[w] : m1[w - 4];
+            const int nb = min(max(lim - 4 * w, 0), 4);
+            const unsigned keep = nb == 4 ? 0xffffffffu : (1u << (8 * nb)) - 1u;
+            any = any || (x & keep) != 0u;
+            const unsigned y = x | ~keep;  // bytes that do not count read as 0xff
+            hole = hole || ((y - 0x01010101u) & ~y & 0x80808080u) != 0u;  // a zero byte
+        }
+    }
+    const bool any_w = __any(any), hole_w = __any(hole);
+    if (lane == 0)
+        a.mcodes[(size_t)item * a.mc_stride + t] = (uint8_t)((any_w ? 1 : 0) | (hole_w ? 0 : 2));
+}
+
+// Keep-mask order: one work-group ranks the (sequence, query tile) items by
+// the number of key tiles their rows see, most first, ties by item index,
+// and writes morder[rank] = item.  Beyond kOrderItems items it writes the
+// static order instead: query tiles latest first (causally the longest rows),
+// sequences in turn.
+constexpr int kOrderItems = 4096;
+__global__ __launch_bounds__(1024) void mask_order_kernel(PrefillArgs a, bool causal) {
+    __shared__ int cnt[kOrderItems];
+    const int n = a.B * a.n_qtiles, tid = threadIdx.x;
+    if (n > kOrderItems) {
+        for (int r = tid; r < n; r += 1024)
+            a.morder[r] = (r % a.B) * a.n_qtiles + (a.n_qtiles - 1 - r / a.B);
+        return;
+    }
+    for (int i = tid; i < n; i += 1024) cnt[i] = 0;
+    __syncthreads();
+    // one thread per (item, 8 key tiles): the items' summary rows are read in
+    // parallel, eight loads a thread in flight, and summed in LDS
+    const int chunks = a.mc_stride / 8;  // 8-tile pieces of a summary row
+    const long long work = (long long)n * chunks;
+    for (long long w0 = tid; w0 < work; w0 += 8 * 1024) {
+        unsigned long long x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const long long w = w0 + 1024 * u;
+            x[u] = w < work ? *reinterpret_cast<const unsigned long long *>(a.mcodes + 8 * w) : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const long long w = w0 + 1024 * u;
+            if (w >= work) continue;
+            const int i = (int)(w / chunks), t8 = 8 * (int)(w % chunks);
+            const int qt = i % a.n_qtiles;
+            const int kv_end = causal ? min(a.Lk, a.off + (qt + 1) * a.BM) : a.Lk;
+            const int nt = (kv_end + PF_BN - 1) / PF_BN;  // the item's key tiles
+            unsigned long long y = x[u] & 0x0101010101010101ull;  // bit 0 of each byte
+            y = nt - t8 >= 8 ? y : nt - t8 <= 0 ? 0ull : y & ((1ull << (8 * (nt - t8))) - 1ull);
+            const int c = __builtin_popcountll(y);
+            if (c) atomicAdd(&cnt[i], c);
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += 1024) {
+        const int ci = cnt[i];
+        int r = 0;
+        for (int j = 0; j < n; ++j) {
+            const int cj = cnt[j];
+            r += (cj > ci || (cj == ci && j < i)) ? 1 : 0;
+        }
+        a.morder[r] = i;
+    }
+}
+
 template <int D, bool C>
 void launch_form(const PrefillArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
     if (a.rope_cos != nullptr)
@@ -705,6 +810,12 @@ void launch_form(const PrefillArgs &a, dim3 grid, dim3 block, hipStream_t stream
 }  // namespace
 
 int launch_prefill_bf16(const PrefillArgs &a, int d, bool causal, hipStream_t stream) {
+    if (a.mask != nullptr) {
+        const long long waves = (long long)a.B * a.n_qtiles * ((a.Lk + PF_BN - 1) / PF_BN);
+        hipLaunchKernelGGL(mask_summary_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                           stream, a, causal);
+        hipLaunchKernelGGL(mask_order_kernel, dim3(1), dim3(1024), 0, stream, a, causal);
+    }
     dim3 grid(a.n_units * a.n_qtiles), block(PF_THREADS);
     if (d == 128) {
         if (causal) launch_form<128, true>(a, grid, block, stream);

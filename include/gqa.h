@@ -140,17 +140,35 @@ gqa_status gqa_prefill_varlen(const void *q, const void *k, const void *v, void 
  *          [L_q, L_k] mask across the batch.  The caller's buffer must hold
  *          (B - 1) * mask_batch_stride + L_q * mask_row_stride bytes; the
  *          bytes of a row past L_k are read but ignored.
+ *   workspace : device buffer of at least gqa_prefill_mask_workspace_bytes(B,
+ *          L_q, L_k) bytes, 16-byte aligned.  The bf16 path writes into it a
+ *          summary of the mask (per sequence, query tile and 64 keys: whether
+ *          none, some or all of the keys the tile's rows may see are visible)
+ *          and the order in which the query tiles are taken (most visible key
+ *          tiles first), and reads both back in the same call, so its
+ *          contents on entry are ignored; the fp32 path does not touch it.
+ *          Calls that overlap in time must not share one.
  * A row with no visible key is zero.  Masked keys receive weight exactly 0, so
  * every key/value row must be finite (0 times a NaN would still be NaN).
  * With every mask byte nonzero the result equals gqa_prefill_chunk.
  * Other arguments, limits and errors as gqa_prefill_chunk (both dtypes); a
- * NULL mask gives GQA_ERR_NULL_POINTER, a misaligned one GQA_ERR_ALIGNMENT and
- * strides breaking the rules above GQA_ERR_SIZE.
+ * NULL mask gives GQA_ERR_NULL_POINTER, a misaligned one GQA_ERR_ALIGNMENT,
+ * strides breaking the rules above GQA_ERR_SIZE, and a NULL, misaligned or
+ * too small workspace GQA_ERR_WORKSPACE.  In bf16 three kernels run on
+ * `hip_stream`: the mask's summary, the order of the query tiles, then the
+ * prefill.
  */
 gqa_status gqa_prefill_mask(const void *q, const void *k, const void *v, const uint8_t *mask,
                             long long mask_row_stride, long long mask_batch_stride, void *o,
                             int B, int L_q, int L_k, int h_q, int h_kv, int d, gqa_dtype dt,
-                            int causal, float scale, void *hip_stream);
+                            int causal, float scale, void *workspace, size_t workspace_bytes,
+                            void *hip_stream);
+
+/* Bytes of workspace gqa_prefill_mask needs: B * ceil(L_q / 32) rows of
+ * ceil(L_k / 64) bytes rounded up to a multiple of 8, then 4 bytes for each
+ * of those B * ceil(L_q / 32) query tiles, each part rounded up to 256 (0
+ * when B <= 0, L_q <= 0 or L_k < L_q). */
+size_t gqa_prefill_mask_workspace_bytes(int B, int L_q, int L_k);
 
 /*
  * Prefill with rotary position embedding: q and k are rotated, then the

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("gqa_prefill", "gqa_prefill_chunk", "gqa_decode", "gqa_decode_append",
               "gqa_decode_token_major", "gqa_decode_paged", "gqa_prefill_rope",
-              "gqa_prefill_varlen", "gqa_prefill_mask", "gqa_decode_append_rope",
+              "gqa_prefill_varlen", "gqa_prefill_mask", "gqa_prefill_mask_workspace_bytes",
+              "gqa_decode_append_rope",
               "gqa_decode_rope_workspace_bytes",
               "gqa_decode_workspace_bytes",
               "gqa_decode_default_splits", "gqa_status_string"):
@@ -130,9 +131,11 @@ def test_prefill_varlen_without_a_gpu_reports_the_device():
 
 
 def mask_status(q=A, k=A, v=A, m=A, mr=64, mb=0, o=A, B=2, Lq=16, Lk=64, h_q=8, h_kv=2, d=64,
-                dt=1, causal=1, scale=0.125):
+                dt=1, causal=1, scale=0.125, ws=A, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = gqa.prefill_mask_workspace_bytes(B, Lq, Lk)
     return gqa.lib().gqa_prefill_mask(q, k, v, m, mr, mb, o, B, Lq, Lk, h_q, h_kv, d, dt, causal,
-                                      ctypes.c_float(scale), None)
+                                      ctypes.c_float(scale), ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -144,9 +147,29 @@ def mask_status(q=A, k=A, v=A, m=A, mr=64, mb=0, o=A, B=2, Lq=16, Lk=64, h_q=8, 
     (dict(Lq=1 << 16, Lk=1 << 16, mr=1 << 16), SIZE),
     (dict(Lq=65, Lk=64), SIZE), (dict(B=0), SIZE), (dict(h_q=8, h_kv=3), HEADS),
     (dict(d=96), HEADDIM), (dict(dt=3), DTYPE), (dict(scale=-1.0), SIZE),
+    # the mask's summary needs a workspace, for either dtype
+    (dict(ws=None), WORKSPACE), (dict(ws=A + 8), WORKSPACE), (dict(ws_bytes=255), WORKSPACE),
+    (dict(ws=None, dt=0), WORKSPACE),
 ])
 def test_prefill_mask_rejects_bad_arguments(kw, status):
     assert mask_status(**kw) == status
+
+
+@pytest.mark.parametrize("B,Lq,Lk", [(1, 1, 1), (2, 16, 64), (1, 4096, 4096), (3, 33, 1000),
+                                     (1, 100, 32768)])
+def test_prefill_mask_workspace_bytes(B, Lq, Lk):
+    """B * ceil(L_q / 32) summary rows of ceil(L_k / 64) bytes rounded up to
+    8, then a 4-byte order entry per row, each part rounded up to 256."""
+    row = -(-(-(-Lk // 64)) // 8) * 8
+    tiles = B * -(-Lq // 32)
+    up = lambda x: -(-x // 256) * 256
+    assert gqa.prefill_mask_workspace_bytes(B, Lq, Lk) == up(tiles * row) + up(tiles * 4)
+
+
+def test_prefill_mask_workspace_bytes_invalid():
+    assert gqa.prefill_mask_workspace_bytes(0, 16, 64) == 0
+    assert gqa.prefill_mask_workspace_bytes(1, 0, 64) == 0
+    assert gqa.prefill_mask_workspace_bytes(1, 65, 64) == 0
 
 
 def test_prefill_mask_without_a_gpu_reports_the_device():

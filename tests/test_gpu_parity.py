@@ -1157,6 +1157,45 @@ def test_prefill_mask_lengths_is_varlen(dev):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_prefill_mask_lower_triangle_with_padding_bytes(d, dev):
+    """A mask that is exactly the causal pattern, in rows padded with random
+    bytes past L_k: with the causal flag every listed tile has all its keys
+    visible (no mask bytes loaded); without it the diagonal tiles are partly
+    visible.  Both equal the causal chunked prefill bit for bit, and the
+    padding bytes play no part."""
+    B, L, h_q, h_kv = 2, 300, 8, 2
+    q, k, v = wl.prefill_inputs(B, L, h_q, h_kv, d, 5600 + d)
+    g = torch.Generator().manual_seed(5601)
+    big = torch.randint(0, 2, (B, L, L + 52), generator=g, dtype=torch.int64).to(torch.uint8)
+    big[..., :L] = torch.tril(torch.ones(L, L, dtype=torch.uint8))
+    big = big.to(dev)
+    m = big[..., :L]  # row stride 352 bytes, used in place
+    assert gqa.mask_layout(m, B, L, L)[0].data_ptr() == big.data_ptr()
+    want = run_prefill_chunk(q, k, v, True, 0.1, dev)
+    for causal in (True, False):
+        say(f"prefill_mask lower triangle d={d} causal={causal}")
+        assert torch.equal(run_prefill_mask(q, k, v, m, causal, 0.1, dev), want)
+
+
+def test_prefill_mask_more_query_tiles_than_the_ordering_ranks(dev):
+    """4100 (sequence, query tile) items, more than the ranking pass orders
+    (4096): the work-groups take them in the static order instead.  All-ones
+    masks give the chunked prefill bit for bit; a random mask matches the
+    oracle on a sample of sequences (each sequence is independent)."""
+    B, Lq, Lk, h_q, h_kv, d = 4100, 32, 64, 8, 1, 64  # G = 8: 32-row query tiles
+    q, k, v = wl.prefill_chunk_inputs(B, Lq, Lk, h_q, h_kv, d, 5700)
+    say("prefill_mask with 4100 query tiles")
+    ones = torch.ones(B, Lq, Lk, dtype=torch.uint8)
+    assert torch.equal(run_prefill_mask(q, k, v, ones, True, 0.125, dev),
+                       run_prefill_chunk(q, k, v, True, 0.125, dev))
+    m = wl.random_mask((B, Lq, Lk), 0.3, 5701)
+    out = run_prefill_mask(q, k, v, m, True, 0.125, dev).cpu()
+    sel = torch.tensor([0, 1, 2047, 4095, 4096, 4099] + list(range(100, 4100, 137)))
+    ref = oracle.prefill_mask(f64(q[sel]), f64(k[sel]), f64(v[sel]), m[sel].numpy(), True, 0.125)
+    check(f64(out[sel]), ref, "bf16", "4100 query tiles, sampled sequences")
+
+
 def _scattered_mask(B, Lq, Lk, period, density, hidden_rows, seed):
     """Keys visible only in key tiles t with t % period == 2 (with the given
     density inside them), and rows [0, hidden_rows) of every sequence see no
