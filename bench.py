@@ -508,6 +508,10 @@ def prefill_line(w, pf):
             "traffic": recorded_traffic("prefill", w.name),
             "flops_per_launch": pf["flops_per_launch"],
             "kernel_ms_avg": pf["kernel_ms_avg"], "kernel_ms_min": pf["kernel_ms_min"]}
+    if w.path == "prefill_mask":
+        roof["kernels"] = "mask summary + query-tile order + prefill (one call, timed together)"
+    elif w.path == "prefill_rope":
+        roof["kernels"] = "key rotation + prefill (one call, timed together)"
     log(f"prefill {w.name}: {pf['value']:.1f} TFLOP/s wall, kernel avg "
         f"{pf['kernel_ms_avg']:.4f} ms ({achieved:.1f} TFLOP/s, {100 * achieved / peak:.1f}% "
         f"of peak)")
