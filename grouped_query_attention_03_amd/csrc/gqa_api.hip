@@ -172,6 +172,7 @@ gqa_status prefill_impl(const void *q, const void *k, const void *v, void *o, in
     if ((int64_t)a.n_units * a.n_qtiles > 0x7fffffff) return GQA_ERR_SIZE;
     a.mcodes = nullptr;
     a.morder = nullptr;
+    a.mwork = nullptr;
     a.mc_stride = 0;
     if (masked) {
         const size_t need = gqa_prefill_mask_workspace_bytes(B, Lq, Lk);
@@ -181,9 +182,11 @@ gqa_status prefill_impl(const void *q, const void *k, const void *v, void *o, in
         // laid out for the most query tiles any head count gives (32 rows each)
         a.mcodes = static_cast<uint8_t *>(workspace);
         a.mc_stride = mask_summary_stride(Lk);
-        a.morder = reinterpret_cast<int32_t *>(
-            static_cast<char *>(workspace) +
-            round_up_256((size_t)B * ((Lq + 31) / 32) * (size_t)a.mc_stride));
+        const size_t tiles = (size_t)B * ((Lq + 31) / 32);
+        char *ws = static_cast<char *>(workspace);
+        a.morder = reinterpret_cast<int32_t *>(ws + round_up_256(tiles * (size_t)a.mc_stride));
+        a.mwork = reinterpret_cast<int *>(ws + round_up_256(tiles * (size_t)a.mc_stride) +
+                                          round_up_256(tiles * 4));
     }
 
     gqa_status st = check_device();
@@ -255,7 +258,7 @@ gqa_status gqa_prefill_mask(const void *q, const void *k, const void *v, const u
 size_t gqa_prefill_mask_workspace_bytes(int B, int L_q, int L_k) {
     if (B <= 0 || L_q <= 0 || L_k < L_q) return 0;
     const size_t tiles = (size_t)B * (size_t)((L_q + 31) / 32);  // at most, 32 rows a tile
-    return round_up_256(tiles * (size_t)mask_summary_stride(L_k)) + round_up_256(tiles * 4);
+    return round_up_256(tiles * (size_t)mask_summary_stride(L_k)) + round_up_256(tiles * 4) + 256;
 }
 
 int gqa_decode_default_splits(void) { return kDefaultSplits; }

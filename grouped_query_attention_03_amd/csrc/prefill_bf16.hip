@@ -124,46 +124,31 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n) {
 // already); kPfVarlen gives sequence b a.kv_lens[b] visible keys (a padded
 // batch); kPfMask hides key j from query row i unless its mask byte is nonzero.
 // FOLD: scale * log2(e) is an exact power of two and is folded into q.
+// One work item of the prefill: query tile qt of unit (sequence, key/value
+// head, head subgroup) `unit`, from its Q load to its output rows.  smem is the
+// work-group's LDS (the ring, then the keep-mask form's list).
 template <int D, bool CAUSAL, int FORM, bool FOLD>
-__global__ __launch_bounds__(PF_THREADS, D == 64 ? 4 : 2)  // waves per SIMD
-void prefill_bf16_kernel(PrefillArgs a) {
+__device__ __forceinline__ void prefill_item(const PrefillArgs &a, char *smem, int unit, int qt) {
     using Lay = PfLay<D>;
     using Ring = PfRing<D, FORM>;
     constexpr bool ROPE = FORM == kPfRope, VARLEN = FORM == kPfVarlen, MASK = FORM == kPfMask;
     constexpr int KSTEPS = Lay::KSTEPS, DB = Lay::DB;
     constexpr int DPW = 2 * Lay::DMA_PER_TENSOR / PF_WAVES;  // direct loads per wave per tile
     constexpr int SLOTS = Ring::SLOTS, DIST = Ring::DIST, SLOT_BYTES = Ring::SLOT_BYTES;
-    __shared__ __attribute__((aligned(1024))) char smem[SLOTS * SLOT_BYTES + Ring::LIST_BYTES];
 
-    const int lane = threadIdx.x & 63, wave = wave_id();
-    // Work-group -> (unit, query tile).  Dispatch sends work-group i to XCD
-    // i % 8.  Equal-cost tiles are mapped XCD-contiguously, so the tiles of one
-    // key/value head run on one XCD and share its L2.  Causal, variable-length
-    // and masked tiles differ in cost, so they are dealt round-robin over the
-    // units instead, longest first: with a multiple of 8 units each unit still
-    // stays on one XCD, and otherwise (one head, say) every XCD still gets an
-    // equal mix of long and short tiles.
-    // The keep-mask form takes its (sequence, query tile) from the order the
-    // summary passes wrote, the work-groups of one of them (its key/value
-    // heads and head subgroups) in a row.
-    int unit, qt;
-    if (MASK) {
-        const int hpi = a.h_kv * a.nsub;  // work-groups per (sequence, query tile)
-        const int item = load_const(a.morder, blockIdx.x / hpi);
-        qt = item % a.n_qtiles;
-        unit = (item / a.n_qtiles) * hpi + blockIdx.x % hpi;
-    } else if (CAUSAL || VARLEN) {
-        unit = blockIdx.x % a.n_units;
-        qt = blockIdx.x / a.n_units;
-    } else {
-        const int lid = xcd_contiguous_id(blockIdx.x, gridDim.x);
-        unit = lid / a.n_qtiles;
-        qt = lid % a.n_qtiles;
+    int lane_ = threadIdx.x & 63, wave_ = wave_id();
+    if constexpr (MASK) {
+        // in the persistent form the ids pass an empty asm per item, so the
+        // values derived from them are computed per item and not hoisted out
+        // of the item loop, where they would hold registers through it
+        asm volatile("" : "+v"(lane_));
+        wave_ = __builtin_amdgcn_readfirstlane(wave_);
     }
-    if (CAUSAL && !MASK) qt = a.n_qtiles - 1 - qt;  // longest rows first
-    // The integer divisions above and below run partly on the vector ALU; their
-    // wave-uniform results are moved to scalar registers, so they do not hold
-    // vector registers for the whole kernel.
+    const int lane = lane_, wave = wave_;
+    // The integer divisions that produce unit and qt, and those below, run
+    // partly on the vector ALU; their wave-uniform results are moved to
+    // scalar registers, so they do not hold vector registers for the whole
+    // kernel.
     unit = __builtin_amdgcn_readfirstlane(unit);
     qt = __builtin_amdgcn_readfirstlane(qt);
     const int sub = __builtin_amdgcn_readfirstlane(unit % a.nsub);
@@ -182,27 +167,31 @@ void prefill_bf16_kernel(PrefillArgs a) {
     const int kv_end = CAUSAL ? min(Lk, off + p0 + a.BM) : Lk;
     const int ntiles = (kv_end + PF_BN - 1) / PF_BN;
     // The loop walks positions 0 .. npos - 1 of a list of key tiles: ring slot
-    // = position % SLOTS, keys of tile tile_of(position).  Without a mask the
-    // list is every tile, in order.  The keep-mask form lists (below) only the
-    // tiles the mask leaves visible to at least one of the work-group's rows,
-    // when it has at most Ring::LIST tiles; full_of(position) says that every
-    // key of the tile that a row of the work-group may see is visible to it,
-    // so its mask bytes are neither loaded nor applied.
+    // = position % SLOTS, keys of tile tile_e(entry of the position).  Without
+    // a mask the list is every tile, in order (the entry of position p is p).
+    // The keep-mask form lists (below) only the tiles the mask leaves visible
+    // to at least one of the work-group's rows, when it has at most Ring::LIST
+    // tiles; full_e(entry) says that every key of the tile that a row of the
+    // work-group may see is visible to it, so its mask bytes are neither
+    // loaded nor applied.  The loop reads each entry once, a tile ahead.
     int npos = ntiles;
     bool use_list = false;
     const uint16_t *tlist = reinterpret_cast<const uint16_t *>(smem + SLOTS * SLOT_BYTES);
-    auto entry_of = [&](int pos) -> int {
-        return pos < npos ? __builtin_amdgcn_readfirstlane((int)tlist[pos]) : 0;
-    };
-    auto tile_of = [&](int pos) -> int {
+    auto entry_at = [&](int pos) -> int {
         if constexpr (MASK) {
-            if (use_list) return entry_of(pos) & 0x7fff;
+            if (use_list) return pos < npos ? __builtin_amdgcn_readfirstlane((int)tlist[pos]) : 0;
         }
         return pos;
     };
-    auto full_of = [&](int pos) -> bool {
+    auto tile_e = [&](int e) -> int {
         if constexpr (MASK) {
-            if (use_list) return (entry_of(pos) >> 15) != 0;
+            if (use_list) return e & 0x7fff;
+        }
+        return e;
+    };
+    auto full_e = [&](int e) -> bool {
+        if constexpr (MASK) {
+            if (use_list) return (e >> 15) != 0;
         }
         return false;
     };
@@ -247,10 +236,11 @@ void prefill_bf16_kernel(PrefillArgs a) {
         const int r = 16 * wave + (lane >> 2);  // row of this lane's first piece
         moff = (unsigned)(p0 + r) * (unsigned)a.mask_row + 16u * ((lane & 3) ^ pf_mswz(r));
     }
-    // this wave's share of the loads of list position x into ring slot x % SLOTS
-    auto issue_tile = [&](int x) {
+    // this wave's share of the loads of list position x (entry e) into ring
+    // slot x % SLOTS
+    auto issue_tile = [&](int x, int e) {
         char *slot = smem + (x % SLOTS) * SLOT_BYTES;
-        const int tx = tile_of(x);
+        const int tx = tile_e(e);
 #pragma unroll
         for (int u = 0; u < DPW; ++u) {
             const int i = i0 + u;
@@ -261,7 +251,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
         if constexpr (MASK) {
             // piece i = wave + 8 u covers rows 16 i .. 16 i + 15; the swizzle of
             // row r depends on r % 16 only, so one lane offset serves both pieces
-            const int n_mask = full_of(x) ? 0 : mpw;
+            const int n_mask = full_e(e) ? 0 : mpw;
 #pragma unroll
             for (int u = 0; u < 2; ++u)
                 if (u < n_mask)
@@ -397,7 +387,7 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // Tile 0 streams in while q is read.  A zero-length sequence has no tile;
     // its buffer range is empty, so these loads read zeros without touching
     // memory.
-    issue_tile(0);
+    issue_tile(0, entry_at(0));
 
     // q has been read (in the keep-mask form, before the mask scan) or is
     // read here while tile 0 streams in.
@@ -595,60 +585,88 @@ void prefill_bf16_kernel(PrefillArgs a) {
     // it also covers tile 0, and not inside the loop, where it would drain the
     // prefetched tiles every iteration
     pf_settle(qf);
+    if constexpr (MASK) {
+        // list entries of positions j .. j + DIST, read a tile ahead, so that
+        // their LDS latency passes under the ring's wait and the barrier
+        int ent[DIST + 1];
 #pragma unroll
-    for (int x = 1; x < DIST; ++x)
-        if (x < npos) issue_tile(x);
-    // Tile x has landed once at most the loads issued after it are pending:
-    // those of tiles x + 1 .. x + DIST - 1 that exist.  Without the mask every
-    // wave issues DPW loads a tile and the counts are immediates; with it, a
-    // tile issues opw, or DPW when its mask bytes are not loaded.
-    // pending: how many of those exist; x: the tile's list position.
-    auto wait_tile = [&](int pending, int x) {
-        if constexpr (MASK) {
-            int n = 0;
+        for (int i = 0; i <= DIST; ++i) ent[i] = entry_at(i);
 #pragma unroll
-            for (int y = 1; y < DIST; ++y)
-                if (y <= pending) n += full_of(x + y) ? DPW : opw;
-            wait_vmcnt_rt(n);
-        } else {
+        for (int x = 1; x < DIST; ++x)
+            if (x < npos) issue_tile(x, ent[x]);
+        // Tile x has landed once at most the loads issued after it are
+        // pending: those of positions x + 1 .. x + pending (pending < DIST =
+        // 2: at most x + 1, entry e1), opw loads, or DPW when its mask bytes
+        // are not loaded.
+        static_assert(DIST == 2, "one tile pending at most");
+        auto wait_landed = [&](int pending, int e1) {
+            if (pending < 1) wait_vmcnt<0>();
+            else if (full_e(e1)) wait_vmcnt<DPW>();
+            else wait_vmcnt_rt(opw);
+        };
+        wait_landed(min(npos, DIST) - 1, ent[1]);
+        block_barrier();
+        for (int j = 0; j < npos; ++j) {
+            if (j + DIST < npos) issue_tile(j + DIST, ent[DIST]);
+            const int t = tile_e(ent[0]);
+            if (active(t)) {
+                bool go = true, full = true;
+                if (!full_e(ent[0])) {
+                    // skip a tile whose mask hides every key from this wave's rows
+                    mask_read(j);
+                    unsigned any = 0, zero = 0;
+#pragma unroll
+                    for (int g = 0; g < 8; ++g) {
+                        any |= mk[g];
+                        zero |= (mk[g] - 0x01010101u) & ~mk[g] & 0x80808080u;  // a zero byte
+                    }
+                    go = __any(any != 0u);
+                    full = !__any(zero != 0u);
+                }
+                if (go) {
+                    qk(j);
+                    softmax(j, t, full);
+                    pv(j);
+                }
+            }
+            const int nxt = entry_at(j + 1 + DIST);
+            // tile j + 1 must have landed; tiles j + 2 .. j + DIST may be pending
+            wait_landed(max(min(npos - 1, j + DIST) - (j + 1), 0), ent[2]);
+            block_barrier();
+#pragma unroll
+            for (int i = 0; i < DIST; ++i) ent[i] = ent[i + 1];
+            ent[DIST] = nxt;
+        }
+    } else {
+#pragma unroll
+        for (int x = 1; x < DIST; ++x)
+            if (x < npos) issue_tile(x, x);
+        // Tile x has landed once at most the loads issued after it are
+        // pending: those of tiles x + 1 .. x + DIST - 1 that exist, DPW loads
+        // each, so the counts are immediates.
+        auto wait_tile = [&](int pending) {
             static_assert(DIST == 3, "the immediate waits assume a prefetch distance of 3");
             if (pending >= 2) wait_vmcnt<2 * DPW>();
             else if (pending == 1) wait_vmcnt<DPW>();
             else wait_vmcnt<0>();
-        }
-    };
-    wait_tile(min(npos, DIST) - 1, 0);
-    block_barrier();
-    for (int j = 0; j < npos; ++j) {
-        if (j + DIST < npos) issue_tile(j + DIST);
-        const int t = tile_of(j);
-        if (active(t)) {
-            bool go = true, full = true;
-            if (MASK && !full_of(j)) {
-                // skip a tile whose mask hides every key from this wave's rows
-                mask_read(j);
-                unsigned any = 0, zero = 0;
-#pragma unroll
-                for (int g = 0; g < 8; ++g) {
-                    any |= mk[g];
-                    zero |= (mk[g] - 0x01010101u) & ~mk[g] & 0x80808080u;  // a zero byte
-                }
-                go = __any(any != 0u);
-                full = !__any(zero != 0u);
-            }
-            if (go) {
+        };
+        wait_tile(min(npos, DIST) - 1);
+        block_barrier();
+        for (int j = 0; j < npos; ++j) {
+            if (j + DIST < npos) issue_tile(j + DIST, j + DIST);
+            if (active(j)) {
                 qk(j);
                 if (V_EARLY) {
                     vload(j);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                softmax(j, t, full);
+                softmax(j, j, true);
                 pv(j);
             }
+            // tile j + 1 must have landed; tiles j + 2 .. j + DIST may be pending
+            wait_tile(max(min(npos - 1, j + DIST) - (j + 1), 0));
+            block_barrier();
         }
-        // tile j + 1 must have landed; tiles j + 2 .. j + DIST may be pending
-        wait_tile(max(min(npos - 1, j + DIST) - (j + 1), 0), j + 1);
-        block_barrier();
     }
 
     // ---- epilogue: O / l, round to bf16, store.  The ring is free after the
@@ -696,6 +714,56 @@ void prefill_bf16_kernel(PrefillArgs a) {
         }
     }
 }
+
+// The prefill kernel.  Work-group -> (unit, query tile): dispatch sends
+// work-group i to XCD i % 8.  Equal-cost tiles are mapped XCD-contiguously, so
+// the tiles of one key/value head run on one XCD and share its L2.  Causal and
+// variable-length tiles differ in cost, so they are dealt round-robin over the
+// units instead, longest first: with a multiple of 8 units each unit still
+// stays on one XCD, and otherwise (one head, say) every XCD still gets an
+// equal mix of long and short tiles.
+// The keep-mask form is persistent: one work-group per CU takes work items
+// from a counter (zeroed by the ordering pass) in the order that pass wrote,
+// the items of one (sequence, query tile) (its key/value heads and head
+// subgroups) in a row, so a CU that finishes an item starts the next at once.
+template <int D, bool CAUSAL, int FORM, bool FOLD>
+__global__ __launch_bounds__(PF_THREADS, D == 64 ? 4 : 2)  // waves per SIMD
+void prefill_bf16_kernel(PrefillArgs a) {
+    using Ring = PfRing<D, FORM>;
+    constexpr bool VARLEN = FORM == kPfVarlen, MASK = FORM == kPfMask;
+    __shared__ __attribute__((aligned(1024))) char smem[Ring::SLOTS * Ring::SLOT_BYTES +
+                                                        Ring::LIST_BYTES];
+    if constexpr (MASK) {
+        __shared__ int next;
+        const int hpi = a.h_kv * a.nsub;  // items per (sequence, query tile)
+        const int total = a.n_units * a.n_qtiles;
+        for (;;) {
+            // every wave has read the previous value (a barrier lies between)
+            // and finished the previous item's epilogue (the barrier below)
+            if (threadIdx.x == 0) next = atomicAdd(a.mwork, 1);
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            block_barrier();
+            const int r = __builtin_amdgcn_readfirstlane(next);
+            if (r >= total) break;
+            const int item = load_const(a.morder, r / hpi);
+            prefill_item<D, CAUSAL, FORM, FOLD>(a, smem, (item / a.n_qtiles) * hpi + r % hpi,
+                                                item % a.n_qtiles);
+        }
+    } else {
+        int unit, qt;
+        if (CAUSAL || VARLEN) {
+            unit = blockIdx.x % a.n_units;
+            qt = blockIdx.x / a.n_units;
+        } else {
+            const int lid = xcd_contiguous_id(blockIdx.x, gridDim.x);
+            unit = lid / a.n_qtiles;
+            qt = lid % a.n_qtiles;
+        }
+        if (CAUSAL) qt = a.n_qtiles - 1 - qt;  // longest rows first
+        prefill_item<D, CAUSAL, FORM, FOLD>(a, smem, unit, qt);
+    }
+}
+
 
 // Keep-mask summary: one wave per (sequence b, query tile qt of BM rows,
 // 64-key tile t) writes mcodes[(b * n_qtiles + qt) * mc_stride + t]: bit 0
@@ -745,9 +813,11 @@ __global__ __launch_bounds__(256) void mask_summary_kernel(PrefillArgs a, bool c
 // static order instead: query tiles latest first (causally the longest rows),
 // sequences in turn.
 constexpr int kOrderItems = 4096;
+constexpr int kMaskCUs = 256;  // compute units of the part
 __global__ __launch_bounds__(1024) void mask_order_kernel(PrefillArgs a, bool causal) {
     __shared__ int cnt[kOrderItems];
     const int n = a.B * a.n_qtiles, tid = threadIdx.x;
+    if (tid == 0) *a.mwork = 0;  // the prefill's work counter
     if (n > kOrderItems) {
         for (int r = tid; r < n; r += 1024)
             a.morder[r] = (r % a.B) * a.n_qtiles + (a.n_qtiles - 1 - r / a.B);
@@ -816,7 +886,11 @@ int launch_prefill_bf16(const PrefillArgs &a, int d, bool causal, hipStream_t st
                            stream, a, causal);
         hipLaunchKernelGGL(mask_order_kernel, dim3(1), dim3(1024), 0, stream, a, causal);
     }
-    dim3 grid(a.n_units * a.n_qtiles), block(PF_THREADS);
+    // the keep-mask form is persistent: one work-group per CU (its LDS ring
+    // fills the CU), at most one per work item
+    const int items = a.n_units * a.n_qtiles;
+    dim3 grid(a.mask != nullptr ? (items < kMaskCUs ? items : kMaskCUs) : items),
+        block(PF_THREADS);
     if (d == 128) {
         if (causal) launch_form<128, true>(a, grid, block, stream);
         else launch_form<128, false>(a, grid, block, stream);
