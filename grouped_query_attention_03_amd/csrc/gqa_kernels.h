@@ -40,7 +40,7 @@ struct PrefillArgs {
     // first passes and read by the prefill
     uint8_t *mcodes;
     int32_t *morder;
-    int *mwork;  // the persistent prefill's work counter, zeroed by the ordering pass
+    int *mwork;  // the persistent prefill's work counters (one per XCD), zeroed by the ordering pass
     int mc_stride;
 };
 

@@ -76,6 +76,8 @@ namespace {
 
 constexpr int PF_WAVES = 8;
 constexpr int PF_THREADS = 64 * PF_WAVES;
+constexpr int kMaskCUs = 256;  // compute units of the part
+constexpr int kXcds = 8;       // XCDs of the part; work-group i runs on XCD i % 8
 
 // The LDS ring: SLOTS slots, each the K tile, the V tile and (keep-mask form)
 // the mask bytes of up to 256 rows x 64 keys; tile x is issued PF_DIST = SLOTS - 1
@@ -722,10 +724,13 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, char *smem, i
 // units instead, longest first: with a multiple of 8 units each unit still
 // stays on one XCD, and otherwise (one head, say) every XCD still gets an
 // equal mix of long and short tiles.
-// The keep-mask form is persistent: one work-group per CU takes work items
-// from a counter (zeroed by the ordering pass) in the order that pass wrote,
-// the items of one (sequence, query tile) (its key/value heads and head
-// subgroups) in a row, so a CU that finishes an item starts the next at once.
+// The keep-mask form is persistent: one work-group per CU takes work items in
+// the order the ordering pass wrote, the items of one (sequence, query tile)
+// (its key/value heads and head subgroups) in a row, so a CU that finishes an
+// item starts the next at once.  Work-group i runs on XCD x = i % 8 and takes
+// the items r = 8 k + x, k from XCD x's own counter (the eight zeroed by the
+// ordering pass): with a multiple of 8 items per query tile, each key/value
+// head's items stay on one XCD, whose L2 then holds its keys and values.
 template <int D, bool CAUSAL, int FORM, bool FOLD>
 __global__ __launch_bounds__(PF_THREADS, D == 64 ? 4 : 2)  // waves per SIMD
 void prefill_bf16_kernel(PrefillArgs a) {
@@ -737,13 +742,14 @@ void prefill_bf16_kernel(PrefillArgs a) {
         __shared__ int next;
         const int hpi = a.h_kv * a.nsub;  // items per (sequence, query tile)
         const int total = a.n_units * a.n_qtiles;
+        const int xcd = blockIdx.x % kXcds;
         for (;;) {
             // every wave has read the previous value (a barrier lies between)
             // and finished the previous item's epilogue (the barrier below)
-            if (threadIdx.x == 0) next = atomicAdd(a.mwork, 1);
+            if (threadIdx.x == 0) next = atomicAdd(a.mwork + xcd, 1);
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
             block_barrier();
-            const int r = __builtin_amdgcn_readfirstlane(next);
+            const int r = __builtin_amdgcn_readfirstlane(next) * kXcds + xcd;
             if (r >= total) break;
             const int item = load_const(a.morder, r / hpi);
             prefill_item<D, CAUSAL, FORM, FOLD>(a, smem, (item / a.n_qtiles) * hpi + r % hpi,
@@ -813,11 +819,10 @@ __global__ __launch_bounds__(256) void mask_summary_kernel(PrefillArgs a, bool c
 // static order instead: query tiles latest first (causally the longest rows),
 // sequences in turn.
 constexpr int kOrderItems = 4096;
-constexpr int kMaskCUs = 256;  // compute units of the part
 __global__ __launch_bounds__(1024) void mask_order_kernel(PrefillArgs a, bool causal) {
     __shared__ int cnt[kOrderItems];
     const int n = a.B * a.n_qtiles, tid = threadIdx.x;
-    if (tid == 0) *a.mwork = 0;  // the prefill's work counter
+    if (tid < kXcds) a.mwork[tid] = 0;  // the prefill's work counters, one per XCD
     if (n > kOrderItems) {
         for (int r = tid; r < n; r += 1024)
             a.morder[r] = (r % a.B) * a.n_qtiles + (a.n_qtiles - 1 - r / a.B);
