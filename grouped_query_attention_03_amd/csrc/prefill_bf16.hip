@@ -53,14 +53,15 @@
 //   a work-group) and 64-key tile: none, some or all of the keys the rows may
 //   see are visible.  It runs once per call, not once per key/value head.  A
 //   second, one-work-group pass orders the query tiles by how many key tiles
-//   they see, most first, and the prefill's work-groups take their query
-//   tiles in that order, so the longest lists start first.  A work-group
-//   lists the key tiles some row of it sees, from that summary, and walks
-//   only those.  The
-//   mask bytes of its rows for a listed tile that is not wholly visible are
-//   moved into the tile's ring slot by the same direct loads (a 3-slot ring,
-//   since a slot then also holds up to 256 rows x 64 bytes of mask); a wave
-//   whose 32 rows see no key of such a tile skips that tile's products.
+//   they see, most first.  The prefill then runs persistent work-groups, one
+//   per CU, that take their (query tile, head) items in that order from a
+//   counter per XCD, so the longest lists start first and no CU waits on the
+//   dispatcher.  A work-group lists the key tiles some row of the item sees,
+//   from the summary, and walks only those.  The mask bytes of its rows for
+//   a listed tile that is not wholly visible are moved into the tile's ring
+//   slot by the same direct loads (a 3-slot ring, since a slot then also
+//   holds up to 256 rows x 64 bytes of mask); a wave whose 32 rows see no key
+//   of such a tile skips that tile's products.
 //   Causal: tiles wholly above the diagonal are never loaded or computed; the
 //   diagonal and the sequence tail are masked element-wise.
 //   Work-groups map to XCDs so that a key/value head's tiles share one L2, and
@@ -391,7 +392,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs &a, char *smem, i
     // memory.
     issue_tile(0, entry_at(0));
 
-    // q has been read (in the keep-mask form, before the mask scan) or is
+    // q has been read (in the keep-mask form, before the list was built) or is
     // read here while tile 0 streams in.
     if constexpr (!MASK) load_q();
 
