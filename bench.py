@@ -126,11 +126,38 @@ def decode_kv_bytes(w, seqlens) -> float:
     return float(rows) * w.h_kv * w.d * 2 * 2
 
 
+def code_only(text: str) -> str:
+    """C/C++ source with its comments removed and whitespace runs collapsed, so
+    that a digest of it changes with the code only."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        ch = text[i]
+        if ch in "\"'":  # a string or character literal, kept whole
+            j = i + 1
+            while j < n and text[j] != ch:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(ch)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest(files) -> str:
+    """Digest of the kernels' code (comments and layout ignored)."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -166,3 +166,15 @@ def test_committed_traffic_rows_name_known_kernels_and_positive_bytes():
         assert float(cells[3]) > 0 and float(cells[4]) > 0
         n += 1
     assert n >= 8
+
+
+def test_code_only_ignores_comments_and_layout():
+    """The source digest follows the code: comments and whitespace do not
+    change it, any token of code does, and comment markers inside string or
+    character literals are code."""
+    base = 'int f(int x) {\n    return x + 1;  // one more\n}\n'
+    assert bench.code_only(base) == bench.code_only("/* header */\nint f(int x)\n{ return x + 1; }")
+    assert bench.code_only(base) != bench.code_only(base.replace("x + 1", "x + 2"))
+    assert bench.code_only('const char *s = "a // b";') == 'const char *s = "a // b";'
+    assert bench.code_only("char c = '/'; // x") == "char c = '/';"
+    assert bench.code_only('a /* b */ c') == "a c"
