@@ -1196,6 +1196,21 @@ def test_prefill_mask_more_query_tiles_than_the_ordering_ranks(dev):
     check(f64(out[sel]), ref, "bf16", "4100 query tiles, sampled sequences")
 
 
+@pytest.mark.parametrize("B", [1, 5, 7])
+def test_prefill_mask_fewer_items_than_xcds(B, dev):
+    """Fewer (query tile, head) work items than XCDs (one query tile of one
+    key/value head per sequence): the persistent prefill runs B work-groups,
+    each taking the items of its own XCD's counter, and every item is done."""
+    Lq, Lk, h_q, h_kv, d = 30, 100, 4, 1, 128  # G = 4: one 64-row query tile
+    q, k, v = wl.prefill_chunk_inputs(B, Lq, Lk, h_q, h_kv, d, 5800 + B)
+    m = wl.random_mask((B, Lq, Lk), 0.5, 5801 + B)
+    say(f"prefill_mask with {B} work items")
+    for causal in (True, False):
+        out = run_prefill_mask(q, k, v, m, causal, 0.1, dev)
+        ref = oracle.prefill_mask(f64(q), f64(k), f64(v), m.numpy(), causal, 0.1)
+        check(f64(out), ref, "bf16", f"{B} work items, causal={causal}")
+
+
 def _scattered_mask(B, Lq, Lk, period, density, hidden_rows, seed):
     """Keys visible only in key tiles t with t % period == 2 (with the given
     density inside them), and rows [0, hidden_rows) of every sequence see no
