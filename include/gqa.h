@@ -166,8 +166,9 @@ gqa_status gqa_prefill_mask(const void *q, const void *k, const void *v, const u
 
 /* Bytes of workspace gqa_prefill_mask needs: B * ceil(L_q / 32) rows of
  * ceil(L_k / 64) bytes rounded up to a multiple of 8, then 4 bytes for each
- * of those B * ceil(L_q / 32) query tiles, each part rounded up to 256 (0
- * when B <= 0, L_q <= 0 or L_k < L_q). */
+ * of those B * ceil(L_q / 32) query tiles, each part rounded up to 256, then
+ * 256 bytes for the eight per-XCD work counters (0 when B <= 0, L_q <= 0 or
+ * L_k < L_q). */
 size_t gqa_prefill_mask_workspace_bytes(int B, int L_q, int L_k);
 
 /*

@@ -159,11 +159,12 @@ def test_prefill_mask_rejects_bad_arguments(kw, status):
                                      (1, 100, 32768)])
 def test_prefill_mask_workspace_bytes(B, Lq, Lk):
     """B * ceil(L_q / 32) summary rows of ceil(L_k / 64) bytes rounded up to
-    8, then a 4-byte order entry per row, each part rounded up to 256."""
+    8, then a 4-byte order entry per row, each part rounded up to 256, then
+    256 bytes of work counters."""
     row = -(-(-(-Lk // 64)) // 8) * 8
     tiles = B * -(-Lq // 32)
     up = lambda x: -(-x // 256) * 256
-    assert gqa.prefill_mask_workspace_bytes(B, Lq, Lk) == up(tiles * row) + up(tiles * 4)
+    assert gqa.prefill_mask_workspace_bytes(B, Lq, Lk) == up(tiles * row) + up(tiles * 4) + 256
 
 
 def test_prefill_mask_workspace_bytes_invalid():
