@@ -78,7 +78,7 @@ const char *gqa_status_string(gqa_status s) {
         case GQA_ERR_HEADS: return "h_q is not a multiple of h_kv";
         case GQA_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
         case GQA_ERR_DTYPE: return "dtype not supported by this entry point";
-        case GQA_ERR_WORKSPACE: return "decode workspace is NULL or too small";
+        case GQA_ERR_WORKSPACE: return "a workspace is NULL, misaligned or too small";
         case GQA_ERR_LAUNCH: return "the HIP runtime reported a launch error";
         case GQA_ERR_DEVICE: return "the current device is not a gfx950 GPU";
         case GQA_ERR_SCRATCH: return "the call needs more than the fixed decode scratch holds";

@@ -53,7 +53,7 @@ enum {
     GQA_ERR_HEADS = 4,         /* h_q is not a multiple of h_kv */
     GQA_ERR_HEAD_DIM = 5,      /* d is not 64 or 128 */
     GQA_ERR_DTYPE = 6,         /* dtype not supported by this entry point */
-    GQA_ERR_WORKSPACE = 7,     /* workspace NULL or smaller than required */
+    GQA_ERR_WORKSPACE = 7,     /* workspace NULL, misaligned or smaller than required */
     GQA_ERR_LAUNCH = 8,        /* the HIP runtime reported an error at launch */
     GQA_ERR_DEVICE = 9,        /* the current device is not a gfx950 GPU */
     GQA_ERR_SCRATCH = 10       /* gqa_decode_noalloc: the call needs more than its fixed scratch */
