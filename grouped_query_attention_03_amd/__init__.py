@@ -200,8 +200,9 @@ def prefill(q, k, v, *, causal: bool, scale: float | None = None, out=None):
         _check_out(out, q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    st = lib().gqa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, L, h_q,
-                           h_kv, d, _dtype_code(q), int(bool(causal)), float(scale), _stream(q))
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        st = lib().gqa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, L, h_q,
+                               h_kv, d, _dtype_code(q), int(bool(causal)), float(scale), _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_prefill")
     return out
@@ -225,9 +226,10 @@ def prefill_chunk(q, k, v, *, causal: bool, scale: float | None = None, out=None
         _check_out(out, q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    st = lib().gqa_prefill_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Lq,
-                                 Lk, h_q, h_kv, d, _dtype_code(q), int(bool(causal)),
-                                 float(scale), _stream(q))
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        st = lib().gqa_prefill_chunk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Lq,
+                                     Lk, h_q, h_kv, d, _dtype_code(q), int(bool(causal)),
+                                     float(scale), _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_prefill_chunk")
     return out
@@ -262,10 +264,11 @@ def decode(q, k_cache, v_cache, seqlens, *, out=None, workspace=None, num_splits
         _check_out(out, q)
     need = decode_workspace_bytes(B, h_q, h_kv, d, num_splits)
     workspace = _workspace(workspace, need, q)
-    st = lib().gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                          seqlens.data_ptr(), out.data_ptr(), B, h_q, h_kv, S, d, _dtype_code(q),
-                          int(num_splits), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                          _stream(q))
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        st = lib().gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                              seqlens.data_ptr(), out.data_ptr(), B, h_q, h_kv, S, d, _dtype_code(q),
+                              int(num_splits), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                              _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_decode")
     return out
@@ -294,9 +297,10 @@ def decode_noalloc(q, k_cache, v_cache, seqlens, *, out, num_splits: int = 0):
     _same(q, (k_cache, "k_cache"), (v_cache, "v_cache"))
     _on_device(q, (seqlens, "seqlens"))
     _check_out(out, q)
-    st = lib().gqa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                  seqlens.data_ptr(), out.data_ptr(), B, h_q, h_kv, S, d,
-                                  _dtype_code(q), int(num_splits), _stream(q))
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        st = lib().gqa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                      seqlens.data_ptr(), out.data_ptr(), B, h_q, h_kv, S, d,
+                                      _dtype_code(q), int(num_splits), _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_decode_noalloc")
     return out
@@ -332,11 +336,12 @@ def decode_append(q, k_new, v_new, k_cache, v_cache, seqlens, *, out=None, works
         _check_out(out, q)
     need = decode_workspace_bytes(B, h_q, h_kv, d, num_splits)
     workspace = _workspace(workspace, need, q)
-    st = lib().gqa_decode_append(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
-                                 k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
-                                 out.data_ptr(), B, h_q, h_kv, S, d, _dtype_code(q),
-                                 int(num_splits), workspace.data_ptr(),
-                                 workspace.numel() * workspace.element_size(), _stream(q))
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        st = lib().gqa_decode_append(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                     k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
+                                     out.data_ptr(), B, h_q, h_kv, S, d, _dtype_code(q),
+                                     int(num_splits), workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_decode_append")
     return out
@@ -368,10 +373,11 @@ def decode_token_major(q, k_cache, v_cache, seqlens, *, out=None, workspace=None
     _same(q, (k_cache, "k_cache"), (v_cache, "v_cache"))
     _on_device(q, (seqlens, "seqlens"))
     out, workspace = _decode_out_ws(q, out, workspace, B, h_q, h_kv, d, num_splits)
-    st = lib().gqa_decode_token_major(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                      seqlens.data_ptr(), out.data_ptr(), B, h_q, h_kv, S, d,
-                                      _dtype_code(q), int(num_splits), workspace.data_ptr(),
-                                      workspace.numel() * workspace.element_size(), _stream(q))
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        st = lib().gqa_decode_token_major(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                          seqlens.data_ptr(), out.data_ptr(), B, h_q, h_kv, S, d,
+                                          _dtype_code(q), int(num_splits), workspace.data_ptr(),
+                                          workspace.numel() * workspace.element_size(), _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_decode_token_major")
     return out
@@ -397,11 +403,12 @@ def decode_paged(q, k_pages, v_pages, block_table, seqlens, *, out=None, workspa
     _same(q, (k_pages, "k_pages"), (v_pages, "v_pages"))
     _on_device(q, (seqlens, "seqlens"), (block_table, "block_table"))
     out, workspace = _decode_out_ws(q, out, workspace, B, h_q, h_kv, d, num_splits)
-    st = lib().gqa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
-                                block_table.data_ptr(), seqlens.data_ptr(), out.data_ptr(), B,
-                                h_q, h_kv, page_size, block_table.shape[1], d, _dtype_code(q),
-                                int(num_splits), workspace.data_ptr(),
-                                workspace.numel() * workspace.element_size(), _stream(q))
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        st = lib().gqa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                                    block_table.data_ptr(), seqlens.data_ptr(), out.data_ptr(), B,
+                                    h_q, h_kv, page_size, block_table.shape[1], d, _dtype_code(q),
+                                    int(num_splits), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_decode_paged")
     return out
@@ -432,9 +439,10 @@ def prefill_rope(q, k, v, cos, sin, *, causal: bool, scale=None, out=None, k_rot
         k_rot = torch.empty_like(k)
     _check_out(out, q)
     _check_out(k_rot, k, "k_rot")
-    st = lib().gqa_prefill_rope(q.data_ptr(), k.data_ptr(), v.data_ptr(), cos.data_ptr(),
-                                sin.data_ptr(), out.data_ptr(), k_rot.data_ptr(), B, L, h_q, h_kv,
-                                d, _dtype_code(q), int(bool(causal)), float(scale), _stream(q))
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        st = lib().gqa_prefill_rope(q.data_ptr(), k.data_ptr(), v.data_ptr(), cos.data_ptr(),
+                                    sin.data_ptr(), out.data_ptr(), k_rot.data_ptr(), B, L, h_q, h_kv,
+                                    d, _dtype_code(q), int(bool(causal)), float(scale), _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_prefill_rope")
     return out, k_rot
@@ -459,9 +467,10 @@ def prefill_varlen(q, k, v, kv_lens, *, causal: bool, scale=None, out=None):
     if out is None:
         out = torch.empty_like(q)
     _check_out(out, q)
-    st = lib().gqa_prefill_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                  kv_lens.data_ptr(), B, L, h_q, h_kv, d, _dtype_code(q),
-                                  int(bool(causal)), float(scale), _stream(q))
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        st = lib().gqa_prefill_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      kv_lens.data_ptr(), B, L, h_q, h_kv, d, _dtype_code(q),
+                                      int(bool(causal)), float(scale), _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_prefill_varlen")
     return out
@@ -534,11 +543,12 @@ def prefill_mask(q, k, v, mask, *, causal: bool, scale=None, out=None, workspace
     _check_out(out, q)
     need = prefill_mask_workspace_bytes(B, Lq, Lk)
     workspace = _workspace(workspace, need, q)
-    st = lib().gqa_prefill_mask(q.data_ptr(), k.data_ptr(), v.data_ptr(), m.data_ptr(),
-                                int(row_stride), int(batch_stride), out.data_ptr(), B, Lq, Lk,
-                                h_q, h_kv, d, _dtype_code(q), int(bool(causal)), float(scale),
-                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                _stream(q))
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        st = lib().gqa_prefill_mask(q.data_ptr(), k.data_ptr(), v.data_ptr(), m.data_ptr(),
+                                    int(row_stride), int(batch_stride), out.data_ptr(), B, Lq, Lk,
+                                    h_q, h_kv, d, _dtype_code(q), int(bool(causal)), float(scale),
+                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                    _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_prefill_mask")
     return out
@@ -578,11 +588,12 @@ def decode_append_rope(q, k_new, v_new, k_cache, v_cache, seqlens, cos, sin, *, 
     _check_out(out, q)
     need = decode_rope_workspace_bytes(B, h_q, h_kv, d, num_splits)
     workspace = _workspace(workspace, need, q)
-    st = lib().gqa_decode_append_rope(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
-                                      k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
-                                      cos.data_ptr(), sin.data_ptr(), out.data_ptr(), B, h_q, h_kv,
-                                      S, d, _dtype_code(q), int(num_splits), workspace.data_ptr(),
-                                      workspace.numel() * workspace.element_size(), _stream(q))
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        st = lib().gqa_decode_append_rope(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                          k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
+                                          cos.data_ptr(), sin.data_ptr(), out.data_ptr(), B, h_q, h_kv,
+                                          S, d, _dtype_code(q), int(num_splits), workspace.data_ptr(),
+                                          workspace.numel() * workspace.element_size(), _stream(q))
     if st != 0:
         raise GQAError(st, "gqa_decode_append_rope")
     return out
